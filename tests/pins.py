@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle: checks against what the pages and the mathematics fix, each
+written as a function of the oracle module so that ``test_oracle_pins`` runs them on the
+oracle and ``test_oracle_mutants`` runs them on copies of the oracle with a planted mistake
+(every planted mistake must fail at least one pin).
+
+Pages (arXiv 2510.21270, "Sparser Block-Sparse Attention via Token Permutation"):
+  [SS] sciencestack.ai page: Fig. 1 caption (B=1, S=4 segmented permutation; own-segment
+       blocks computed, inter-segment blocks skippable), Fig. 2 caption (coverage), Lemma 3.1
+       (joint key/value permutation invariance).
+  [GS] gist.science summary, Methodik 1-4.
+  [SK] skillmd.com "Sparser Block Attention", Implementation Steps (active-block count rule,
+       inverse permutation).
+"""
+import math
+import os
+
+import numpy as np
+
+import bruteforce as bf
+from pbs_synth import f32_to_bf16_bits, random_bf16
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _tiny(seed, B=1, Hq=4, Hkv=2, N=32, d=8, scale_k=1.0):
+    q = random_bf16((B, Hq, N, d), seed)
+    k = random_bf16((B, Hkv, N, d), seed + 1, scale_k)
+    v = random_bf16((B, Hkv, N, d), seed + 2)
+    return q, k, v
+
+
+def _vis_matrix(N, block, segment, perm_row, counts_row, idx_row, dense=False):
+    sel = None
+    if counts_row is not None:
+        sel = [list(idx_row[i, :counts_row[i]]) for i in range(N // block)]
+    return bf.visibility(N, block, segment, perm=perm_row, sel=sel, dense=dense)
+
+
+# ----------------------------------------------------------------------------- scores
+
+def pin_scores_sum_to_one(O):
+    """Each row's softmax over a segment sums to 1, so each segment's mean-pooled scores
+    sum to 1 ([GS Methodik 3, Proxy-Bewertung]; [SK] normalises importance to sum 1)."""
+    q, k, _ = _tiny(11, N=64, d=16)
+    sc = O.key_scores(q, k, block=8, segment=16, scale=0.25)
+    assert sc.dtype == np.float32 and sc.shape == (1, 2, 64)
+    sums = sc.astype(np.float64).reshape(1, 2, 4, 16).sum(-1)
+    assert np.allclose(sums, 1.0, atol=2e-6), sums
+    assert (sc > 0).all()
+
+
+def pin_scores_identical_keys(O):
+    """Closed form: if every key of a segment is the same vector, each visible key of the
+    segment gets the same probability.  Segments wholly before the last query block give
+    1/S per key; in the last segment row t sees t-s0+1 keys, so
+    score_j = (1/(G*Bs)) * sum over rows (g,t) with t >= j of 1/(t-s0+1)."""
+    B, Hq, Hkv, N, d, Bs, S = 1, 4, 2, 48, 8, 4, 16
+    G = Hq // Hkv
+    q = random_bf16((B, Hq, N, d), 21)
+    base = random_bf16((B, Hkv, N // S, 1, d), 22)
+    k = np.ascontiguousarray(np.broadcast_to(base, (B, Hkv, N // S, S, d)).reshape(B, Hkv, N, d))
+    sc = O.key_scores(q, k, block=Bs, segment=S, scale=0.3535533845424652)
+    s0 = N - S
+    for h in range(Hkv):
+        assert np.allclose(sc[0, h, :s0], 1.0 / S, rtol=1e-6)
+        for j in range(s0, N):
+            exp = sum(1.0 / (t - s0 + 1) for t in range(N - Bs, N) if t >= j) * G / (G * Bs)
+            assert math.isclose(float(sc[0, h, j]), exp, rel_tol=1e-6), (j, sc[0, h, j], exp)
+
+
+def pin_scores_salient_closed_form(O):
+    """Closed form with one salient key: all last-block queries are a*e1, all keys are 0
+    except key j* = b*e1.  Then z(j*) = scale*a*b and z = 0 elsewhere, so in j*'s segment
+    p(j*) = e^z / (e^z + S - 1) for every row; the other segments are uniform."""
+    B, Hq, Hkv, N, d, Bs, S = 1, 2, 1, 32, 16, 4, 8
+    a, b, scale, jstar = 2.0, 3.0, 0.25, 10
+    qf = np.zeros((B, Hq, N, d), np.float32)
+    qf[..., 0] = a
+    kf = np.zeros((B, Hkv, N, d), np.float32)
+    kf[0, 0, jstar, 0] = b
+    sc = O.key_scores(f32_to_bf16_bits(qf), f32_to_bf16_bits(kf), block=Bs, segment=S, scale=scale)
+    ez = math.exp(scale * a * b)
+    assert math.isclose(float(sc[0, 0, jstar]), ez / (ez + S - 1), rel_tol=1e-6)
+    assert math.isclose(float(sc[0, 0, 8]), 1.0 / (ez + S - 1), rel_tol=1e-6)
+    assert math.isclose(float(sc[0, 0, 0]), 1.0 / S, rel_tol=1e-6)
+
+
+def pin_scores_bruteforce(O):
+    """Brute force over every (row, key) pair on a tiny GQA input."""
+    B, Hq, Hkv, N, d, Bs, S = 1, 4, 2, 24, 8, 4, 8
+    q, k, _ = _tiny(31, Hq=Hq, Hkv=Hkv, N=N, d=d, scale_k=1.5)
+    scale = 0.35
+    sc = O.key_scores(q, k, block=Bs, segment=S, scale=scale)
+    G = Hq // Hkv
+    for h in range(Hkv):
+        ref = bf.key_scores([bf.mat(q[0, g]) for g in range(h * G, (h + 1) * G)], bf.mat(k[0, h]),
+                            Bs, S, scale)
+        assert np.allclose(sc[0, h], ref, rtol=2e-6, atol=1e-9), (h, sc[0, h], ref)
+
+
+# ----------------------------------------------------------------------------- permutation
+
+def pin_order_rules(O):
+    """Descending, ties to the lower index, -0 == +0, NaN last (hand-derived)."""
+    v = np.array([0.5, -0.0, 0.0, np.nan, 0.5, 1.0, -1.0], dtype=np.float32)
+    assert list(O.descending_order(v)) == [5, 0, 4, 1, 2, 6, 3]
+
+
+def pin_permutation_fig1(O):
+    """Fig. 1 geometry (B=1, S=4, N=8): keys move only inside their segment, in descending
+    score order ([SS Fig. 1]; [GS Methodik 2, 3 Sortierung]).  Hand-derived."""
+    sc = np.array([[[0.1, 0.4, 0.2, 0.3, 0.05, 0.05, 0.6, 0.3]]], dtype=np.float32)
+    perm = O.segment_permutation(sc, segment=4)
+    assert perm.dtype == np.int32
+    assert perm[0, 0].tolist() == [1, 3, 2, 0, 6, 7, 4, 5]
+
+
+def pin_permutation_properties(O):
+    """Bijection on every segment, non-increasing scores along the permuted order, equal
+    scores in increasing position; the permuted copy is a row gather and the inverse
+    restores the original ([SK Implementation Steps])."""
+    rng = np.random.default_rng(5)
+    B, H, N, S, d = 2, 3, 64, 16, 8
+    sc = rng.choice(np.array([0.0, -0.0, 0.25, 0.5, 1e-8, 3.0], np.float32), size=(B, H, N))
+    perm = O.segment_permutation(sc, segment=S)
+    k = random_bf16((B, H, N, d), 7)
+    kp = O.apply_permutation(k, perm)
+    inv = O.inverse_permutation(perm)
+    for b in range(B):
+        for h in range(H):
+            for s0 in range(0, N, S):
+                seg = perm[b, h, s0:s0 + S]
+                assert sorted(seg.tolist()) == list(range(s0, s0 + S))
+                vals = sc[b, h, seg]
+                for p in range(S - 1):
+                    assert vals[p] >= vals[p + 1]
+                    if vals[p] == vals[p + 1]:
+                        assert seg[p] < seg[p + 1]
+            for p in range(N):
+                assert (kp[b, h, p] == k[b, h, perm[b, h, p]]).all()
+                assert inv[b, h, perm[b, h, p]] == p
+    assert (O.apply_permutation(kp, inv) == k).all()
+
+
+# ----------------------------------------------------------------------------- block scores
+
+def pin_block_probs_closed_form(O):
+    """Closed form: every row of query block i equals c_i*e1 and every row of permuted key
+    block j equals w_j*e1, so the pooled means are c_i*e1 and w_j*e1 and the logit is
+    scale*c_i*w_j.  P is a softmax over the earlier-segment blocks only."""
+    B, Hq, Hkv, N, d, Bs, S = 1, 1, 1, 24, 4, 2, 6
+    nb, bps = N // Bs, S // Bs
+    c = np.linspace(-1.0, 1.0, nb).astype(np.float32)
+    w = np.linspace(2.0, -1.5, nb).astype(np.float32)
+    qf = np.zeros((B, Hq, N, d), np.float32)
+    kf = np.zeros((B, Hkv, N, d), np.float32)
+    for i in range(nb):
+        qf[0, 0, i * Bs:(i + 1) * Bs, 0] = c[i]
+        kf[0, 0, i * Bs:(i + 1) * Bs, 0] = w[i]
+    qb, kb = f32_to_bf16_bits(qf), f32_to_bf16_bits(kf)
+    cq = O.bf16_to_f64(qb[0, 0, ::Bs, 0])
+    wk = O.bf16_to_f64(kb[0, 0, ::Bs, 0])
+    scale = 0.5
+    P = O.block_probabilities(qb, kb, block=Bs, segment=S, scale=scale)
+    for i in range(nb):
+        n = (i // bps) * bps
+        if n == 0:
+            assert (P[0, 0, i] == 0).all()
+            continue
+        e = np.array([math.exp(scale * cq[i] * wk[j]) for j in range(n)])
+        assert np.allclose(P[0, 0, i, :n], e / e.sum(), rtol=1e-6), i
+        assert (P[0, 0, i, n:] == 0).all()
+
+
+def pin_block_probs_bruteforce(O):
+    """Brute force (explicit means and softmax) on a tiny GQA input."""
+    B, Hq, Hkv, N, d, Bs, S = 1, 4, 2, 32, 8, 4, 8
+    q, k, _ = _tiny(41, Hq=Hq, Hkv=Hkv, N=N, d=d)
+    P = O.block_probabilities(q, k, block=Bs, segment=S, scale=0.4)
+    G = Hq // Hkv
+    for g in range(Hq):
+        ref = bf.block_probs(bf.mat(q[0, g]), bf.mat(k[0, g // G]), Bs, S, 0.4)
+        for (i, j), pij in ref.items():
+            assert math.isclose(float(P[0, g, i, j]), pij, rel_tol=2e-6), (g, i, j)
+        assert np.count_nonzero(P[0, g]) == len(ref)
+
+
+# ----------------------------------------------------------------------------- selection
+
+def pin_keep_count_golden(O):
+    """The printed active-block count rule ([SK Implementation Steps]); golden table."""
+    with open(os.path.join(GOLDEN, "keep_count.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    for n, r, want in rows:
+        assert O.keep_count(int(n), float(r)) == int(want), (n, r, want)
+
+
+def _select_case(O, rows, mode, param):
+    """rows: list of 5-value P rows for query blocks 5..9 of a block=1, segment=5, N=10
+    layout (5 candidates each)."""
+    P = np.zeros((1, 1, 10, 10), np.float32)
+    for r, vals in enumerate(rows):
+        P[0, 0, 5 + r, :5] = np.array(vals, np.float32)
+    counts, idx = O.select_blocks(P, block=1, segment=5, mode=mode, param=param)
+    assert counts.dtype == np.int32 and idx.dtype == np.int32 and idx.shape == (1, 1, 10, 5)
+    assert (counts[0, 0, :5] == 0).all()
+    return [idx[0, 0, 5 + r, :counts[0, 0, 5 + r]].tolist() for r in range(len(rows))]
+
+
+def pin_select_handworked(O):
+    """Hand-worked selections (values exact in binary): ranking by P descending with ties
+    to the lower block, output in ascending block order; coverage stops at the first
+    prefix whose float32 sum reaches tau (>=), and keeps every block if it never does."""
+    rows = [[0.125, 0.25, 0.25, 0.0625, 0.125],
+            [0.2, 0.2, 0.2, 0.2, 0.2],
+            [0.0, 0.0, 0.0, 0.0, 1.0],
+            [-0.0, 0.0, 0.5, 0.25, 0.25],
+            [0.25, 0.5, 0.125, 0.125, 0.0]]
+    assert _select_case(O, rows, O.KEEP, 0.5) == [[1, 2], [0, 1], [0, 4], [2, 3], [0, 1]]
+    assert _select_case(O, rows, O.KEEP, 0.1) == [[1], [0], [4], [2], [1]]
+    assert _select_case(O, rows, O.COVERAGE, 0.75) == [[0, 1, 2, 4], [0, 1, 2, 3], [4], [2, 3], [0, 1]]
+    assert _select_case(O, rows, O.COVERAGE, 1.0)[4] == [0, 1, 2, 3]
+    assert _select_case(O, [[0.125] * 5], O.COVERAGE, 0.9) == [[0, 1, 2, 3, 4]]
+
+
+def pin_select_sequential_fp32(O):
+    """Coverage sums in sequential float32: 0.75 + 2^-25 rounds back to 0.75 (tie to even),
+    so with tau = 0.75 + 2^-24 the float32 running sum never reaches tau and every block is
+    kept, while an exact or pairwise sum would stop after three blocks."""
+    tiny = 2.0 ** -25
+    tau = 0.75 + 2.0 ** -24
+    got = _select_case(O, [[0.75, tiny, tiny, tiny, 0.0]], O.COVERAGE, tau)
+    assert got == [[0, 1, 2, 3, 4]]
+
+
+def pin_select_laws(O):
+    """Laws on random rows: the count law (keep), dominance (every kept block outranks
+    every dropped one), and coverage minimality (kept mass reaches tau; without the last
+    kept block it does not)."""
+    rng = np.random.default_rng(9)
+    nb, bps = 24, 4
+    P = np.zeros((1, 2, nb, nb), np.float32)
+    for g in range(2):
+        for i in range(bps, nb):
+            n = (i // bps) * bps
+            x = rng.normal(size=n) * 0.5
+            x[rng.integers(0, n)] = x.max()            # a planted tie
+            e = np.exp(x - x.max())
+            P[0, g, i, :n] = (e / e.sum()).astype(np.float32)
+    for mode, param in ((O.KEEP, 0.3), (O.KEEP, 1.0), (O.COVERAGE, 0.6), (O.COVERAGE, 0.95)):
+        counts, idx = O.select_blocks(P, block=1, segment=bps, mode=mode, param=param)
+        for g in range(2):
+            for i in range(nb):
+                n = (i // bps) * bps
+                kk = int(counts[0, g, i])
+                sel = idx[0, g, i, :kk].tolist()
+                assert sel == sorted(set(sel)) and all(0 <= j < n for j in sel)
+                if n == 0:
+                    assert kk == 0
+                    continue
+                if mode == O.KEEP:
+                    assert kk == max(1, int(param * n))
+                row = P[0, g, i, :n]
+                rest = [j for j in range(n) if j not in sel]
+                for a in sel:
+                    for b in rest:
+                        assert row[a] > row[b] or (row[a] == row[b] and a < b)
+                if mode == O.COVERAGE:
+                    ranked = sorted(sel, key=lambda j: (-row[j], j))
+                    c = np.float32(0)
+                    partial = []
+                    for j in ranked:
+                        c = np.float32(c + row[j])
+                        partial.append(float(c))
+                    if kk < n:
+                        assert partial[-1] >= param
+                    if kk > 1:
+                        assert partial[-2] < param
+
+
+# ----------------------------------------------------------------------------- geometry
+
+def pin_fig1_geometry(O):
+    """Golden region map of Fig. 1 (B=1, S=4, N=8): own-segment keys visible up to t,
+    earlier segments are exactly the block-selection candidates, later segments never
+    appear.  Holds for the natural order and for a permuted one."""
+    with open(os.path.join(GOLDEN, "fig1_b1_s4_n8.txt")) as f:
+        grid = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    N, S = 8, 4
+    q, k, _ = _tiny(3, Hq=1, Hkv=1, N=N, d=4)
+    for perm in (None, np.array([2, 0, 3, 1, 7, 4, 6, 5], np.int32)):
+        kp = k if perm is None else O.apply_permutation(k, perm[None, None])
+        P = O.block_probabilities(q, kp, block=1, segment=S, scale=0.5)
+        for t in range(N):
+            vis = set(O.visible_keys(t, block=1, segment=S, perm_row=perm, sel_blocks=[],
+                                     dense=False).tolist())
+            for j in range(N):
+                want = grid[t][j]
+                assert (want == "D") == (j in vis), (t, j)
+                # candidate slots are permuted block indices; with B=1 and a permutation
+                # inside segments, slot j lies in the same segment as key j
+                assert (want == "Y") == (P[0, 0, t, j] > 0), (t, j)
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _tiny_pbs(O, seed, mode="keep", param=0.5, N=32, Bs=4, S=8, Hq=4, Hkv=2, d=8):
+    q, k, v = _tiny(seed, Hq=Hq, Hkv=Hkv, N=N, d=d, scale_k=1.7)
+    out = O.prefill(q, k, v, block=Bs, segment=S, scale=0.4, mode=mode, param=param)
+    return q, k, v, out
+
+
+def pin_attention_bruteforce(O):
+    """PBS and dense outputs (and log-normalisers) against an explicit N x N visibility
+    matrix built from the definitions ([SS Fig. 1]: own segment under the causal mask,
+    selected earlier-segment blocks in full)."""
+    N, Bs, S, Hq, Hkv = 32, 4, 8, 4, 2
+    q, k, v, out = _tiny_pbs(O, 51, param=0.34)
+    G = Hq // Hkv
+    od, lsed = O.dense_causal(q, k, v, block=Bs, scale=0.4)
+    for g in range(Hq):
+        h = g // G
+        Q, K, V = bf.mat(q[0, g]), bf.mat(k[0, h]), bf.mat(v[0, h])
+        vis = _vis_matrix(N, Bs, S, out["perm"][0, h], out["counts"][0, g], out["idx"][0, g])
+        ref = bf.attention(Q, K, V, vis, 0.4)
+        assert np.allclose(out["o"][0, g], ref, atol=1e-12), g
+        visd = bf.visibility(N, Bs, S, dense=True)
+        assert np.allclose(od[0, g], bf.attention(Q, K, V, visd, 0.4), atol=1e-12)
+        for t in (0, 5, N - 1):
+            lse = math.log(math.fsum(math.exp(0.4 * bf.dot(Q[t], K[j])) for j in range(N) if vis[t][j]))
+            assert math.isclose(out["lse"][0, g, t], lse, rel_tol=1e-12)
+
+
+def pin_lemma_3_1(O):
+    """[SS Lemma 3.1]: attention over the permuted copies, with the causal mask mapped
+    through the stored original positions, equals the oracle's result computed from the
+    original K and V (the permutation is not an involution, so its direction matters)."""
+    N, Bs, S, Hq, Hkv = 32, 4, 8, 4, 2
+    q, k, v, out = _tiny_pbs(O, 61, param=0.5)
+    G = Hq // Hkv
+    for g in range(Hq):
+        h = g // G
+        perm = out["perm"][0, h]
+        assert any(perm[perm[p]] != p for p in range(N))
+        vis = _vis_matrix(N, Bs, S, perm, out["counts"][0, g], out["idx"][0, g])
+        vis_perm = [[vis[t][int(perm[p])] for p in range(N)] for t in range(N)]
+        ref = bf.attention(bf.mat(q[0, g]), bf.mat(out["k_perm"][0, h]), bf.mat(out["v_perm"][0, h]),
+                           vis_perm, 0.4)
+        assert np.allclose(out["o"][0, g], ref, atol=1e-12), g
+
+
+def pin_keep_one_is_dense(O):
+    """Keep ratio 1 keeps every earlier-segment block, so PBS equals dense causal."""
+    q, k, v, out = _tiny_pbs(O, 71, param=1.0)
+    od, lsed = O.dense_causal(q, k, v, block=4, scale=0.4)
+    assert np.abs(out["o"] - od).max() < 1e-12
+    assert np.abs(out["lse"] - lsed).max() < 1e-12
+
+
+def pin_one_segment_is_dense(O):
+    """With S = N there is no earlier segment, so PBS equals dense causal for any ratio."""
+    q, k, v = _tiny(81, N=32)
+    out = O.prefill(q, k, v, block=4, segment=32, scale=0.4, mode=O.KEEP, param=0.1)
+    od, _ = O.dense_causal(q, k, v, block=4, scale=0.4)
+    assert (out["counts"] == 0).all()
+    assert np.abs(out["o"] - od).max() < 1e-12
+
+
+def pin_segment0_rows_are_dense(O):
+    """Rows of the first segment have no candidate block and equal dense causal; later
+    rows at a low keep ratio do not."""
+    q, k, v, out = _tiny_pbs(O, 91, param=0.1)
+    od, _ = O.dense_causal(q, k, v, block=4, scale=0.4)
+    assert np.abs(out["o"][:, :, :8] - od[:, :, :8]).max() < 1e-12
+    assert np.abs(out["o"][:, :, 8:] - od[:, :, 8:]).max() > 1e-3
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -1,0 +1,59 @@
+"""Plant one plausible mistake at a time in a copy of the oracle (on the CPU) and check that
+at least one pin catches it: the pins are strong enough that such a mistake cannot pass."""
+import os
+import types
+
+import pytest
+
+import pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "pbs_oracle.py")
+
+MUTANTS = {
+    "scores_no_scale": ("Z = scale * (Qr @", "Z = (Qr @"),
+    "scores_no_causal_mask": ("Z = np.where(visible, Z, -np.inf)", "Z = Z"),
+    "scores_sum_not_mean": ("(acc / (G * block))", "(acc / block)"),
+    "scores_first_block_rows": ("rows = np.arange(N - block, N)", "rows = np.arange(0, block)"),
+    "order_ascending": ("neg = np.where(nan, np.float32(0), -v)", "neg = np.where(nan, np.float32(0), v)"),
+    "order_ties_high_index": ("(pos, neg, nan)", "(-pos, neg, nan)"),
+    "order_nan_first": ("(pos, neg, nan)", "(pos, neg, ~nan)"),
+    "permute_inverse_gather": ("out[b, h] = x[b, h, perm[b, h]]", "out[b, h] = x[b, h, np.argsort(perm[b, h])]"),
+    "visible_inverse_perm": ("perm_row[slots].astype(np.int64)", "np.argsort(perm_row)[slots].astype(np.int64)"),
+    "visible_own_excludes_t": ("own = np.arange(s0, t + 1)", "own = np.arange(s0, t)"),
+    "pool_sum_not_mean": ("qbar = bf16_to_f64(q[b, g]).reshape(nb, block, d).mean(axis=1)",
+                          "qbar = bf16_to_f64(q[b, g]).reshape(nb, block, d).sum(axis=1)"),
+    "candidates_include_own_segment": ("n = (i // bps) * bps\n                logits",
+                                       "n = min((i // bps + 1) * bps, nb)\n                logits"),
+    "block_logits_no_scale": ("logits = scale * (kbar[b, h, :n] @ qbar[i])", "logits = (kbar[b, h, :n] @ qbar[i])"),
+    "keep_min_zero": ("return max(1, int(math.floor(", "return max(0, int(math.floor("),
+    "keep_round_up": ("int(math.floor(float(ratio) * n))", "int(math.ceil(float(ratio) * n))"),
+    "coverage_strict": (">= tau          # compared in double", "> tau          # compared in double"),
+    "coverage_double_sum": ("axis=-1, dtype=np.float32)   # sequential", "axis=-1, dtype=np.float64)   # sequential"),
+    "attn_mask_strict": ("Z = np.where(keys[None, :] <= t[:, None], Z, -np.inf)",
+                         "Z = np.where(keys[None, :] < t[:, None], Z, -np.inf)"),
+    "attn_no_scale": ("Z = scale * (Qb @ Kf[keys].T)", "Z = (Qb @ Kf[keys].T)"),
+    "attn_values_are_keys": ("ob = (E @ Vf[keys]) / l", "ob = (E @ Kf[keys]) / l"),
+    "attn_gqa_modulo": ("    for n_out, (b, g, i) in enumerate(todo):\n        h = g // G",
+                        "    for n_out, (b, g, i) in enumerate(todo):\n        h = g % Hkv"),
+    "attn_lse_log2": ("lb = (m + np.log(l))[:, 0]", "lb = (m + np.log2(l))[:, 0]"),
+}
+
+
+def _mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _mutant(*MUTANTS[name])
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"

@@ -1,0 +1,169 @@
+// C-ABI entry points of libpbs: argument validation, workspace carving and kernel launches on
+// the caller's stream.  Every check happens before the first launch; nothing here allocates,
+// frees or synchronises.
+#include "../../include/pbs.h"
+#include "pbs_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+using pbs::Dims;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Fills `d` and returns PBS_OK, or the status describing why the shape is unsupported.
+int check_shape(const pbs_shape* s, Dims* d) {
+  if (!s) return PBS_E_ARG;
+  if (s->batch < 0 || s->seq_len < 0) return PBS_E_SHAPE;
+  if (s->heads_q <= 0 || s->heads_kv <= 0 || s->heads_q % s->heads_kv) return PBS_E_SHAPE;
+  if (s->head_dim != 64 && s->head_dim != 128) return PBS_E_SHAPE;
+  if (s->block != 64 && s->block != 128) return PBS_E_SHAPE;
+  if (s->segment <= 0 || s->segment % s->block || s->segment > 16384) return PBS_E_SHAPE;
+  if (s->seq_len % s->segment) return PBS_E_SHAPE;
+  if (s->seq_len / s->block > 8192) return PBS_E_SHAPE;
+  d->B = s->batch;
+  d->Hq = s->heads_q;
+  d->Hkv = s->heads_kv;
+  d->N = s->seq_len;
+  d->d = s->head_dim;
+  d->Bs = s->block;
+  d->S = s->segment;
+  d->G = s->heads_q / s->heads_kv;
+  d->nb = s->seq_len / s->block;
+  d->bps = s->segment / s->block;
+  d->nseg = s->seq_len / s->segment;
+  d->max_off = d->nseg > 0 ? (d->nseg - 1) * d->bps : 0;
+  return PBS_OK;
+}
+
+bool empty(const Dims& d) { return d.B == 0 || d.N == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? PBS_OK : PBS_E_LAUNCH; }
+
+// All of `ptrs` present (non-null) and 16-byte aligned.
+template <int K>
+int check_required(const void* const (&ptrs)[K]) {
+  for (int i = 0; i < K; ++i)
+    if (!ptrs[i]) return PBS_E_ARG;
+  for (int i = 0; i < K; ++i)
+    if (!aligned16(ptrs[i])) return PBS_E_ALIGN;
+  return PBS_OK;
+}
+
+int check_optional(const void* p) { return (p && !aligned16(p)) ? PBS_E_ALIGN : PBS_OK; }
+
+bool finite_positive(float x) { return x > 0.f && x < 3.0e38f; }
+
+}  // namespace
+
+extern "C" {
+
+size_t pbs_workspace_bytes(const pbs_shape* shape) {
+  Dims d;
+  if (check_shape(shape, &d) != PBS_OK) return 0;
+  const size_t a = pbs::score_workspace_bytes(d);
+  const size_t b = pbs::select_workspace_bytes(d);
+  return a > b ? a : b;
+}
+
+int32_t pbs_max_offdiag(const pbs_shape* shape) {
+  Dims d;
+  if (check_shape(shape, &d) != PBS_OK) return -1;
+  return d.max_off;
+}
+
+const char* pbs_strerror(int status) {
+  switch (status) {
+    case PBS_OK: return "ok";
+    case PBS_E_ARG: return "invalid argument (null pointer, mode, flag or parameter)";
+    case PBS_E_SHAPE: return "unsupported shape";
+    case PBS_E_ALIGN: return "pointer not 16-byte aligned";
+    case PBS_E_WORKSPACE: return "workspace too small";
+    case PBS_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pbs_score(const pbs_shape* shape, const uint16_t* q, const uint16_t* k, float scale,
+              float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int st = check_shape(shape, &d);
+  if (st != PBS_OK) return st;
+  if (!finite_positive(scale)) return PBS_E_ARG;
+  if (empty(d)) return PBS_OK;
+  const void* const req[] = {q, k, scores, workspace};
+  if ((st = check_required(req)) != PBS_OK) return st;
+  if (workspace_bytes < pbs::score_workspace_bytes(d)) return PBS_E_WORKSPACE;
+  return status_of(pbs::launch_score(d, q, k, scale, scores, workspace,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int pbs_permute(const pbs_shape* shape, const float* scores, const uint16_t* k,
+                const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
+                float* k_pool, int32_t* blk_minpos, void* stream) {
+  Dims d;
+  int st = check_shape(shape, &d);
+  if (st != PBS_OK) return st;
+  if (empty(d)) return PBS_OK;
+  const void* const req[] = {scores, k, v, perm, k_perm, v_perm};
+  if ((st = check_required(req)) != PBS_OK) return st;
+  if ((st = check_optional(k_pool)) != PBS_OK) return st;
+  if ((st = check_optional(blk_minpos)) != PBS_OK) return st;
+  return status_of(pbs::launch_permute(d, scores, k, v, perm, k_perm, v_perm, k_pool, blk_minpos,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int pbs_block_select(const pbs_shape* shape, const uint16_t* q, const uint16_t* k_perm,
+                     const float* k_pool, float scale, int mode, double param,
+                     float* blk_scores, int flags, int32_t* counts, int32_t* idx,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int st = check_shape(shape, &d);
+  if (st != PBS_OK) return st;
+  if (mode != PBS_SELECT_KEEP_RATIO && mode != PBS_SELECT_COVERAGE) return PBS_E_ARG;
+  if (!(param > 0.0 && param <= 1.0)) return PBS_E_ARG;
+  if (flags & ~PBS_FLAG_SCORES_IN) return PBS_E_ARG;
+  const bool scores_in = (flags & PBS_FLAG_SCORES_IN) != 0;
+  if (!scores_in && !finite_positive(scale)) return PBS_E_ARG;
+  if (empty(d)) return PBS_OK;
+  const void* const req[] = {counts, idx, workspace};
+  if ((st = check_required(req)) != PBS_OK) return st;
+  if (scores_in) {
+    if (!blk_scores) return PBS_E_ARG;
+  } else {
+    if (!q || (!k_perm && !k_pool)) return PBS_E_ARG;
+  }
+  if ((st = check_optional(q)) != PBS_OK) return st;
+  if ((st = check_optional(k_perm)) != PBS_OK) return st;
+  if ((st = check_optional(k_pool)) != PBS_OK) return st;
+  if ((st = check_optional(blk_scores)) != PBS_OK) return st;
+  if (workspace_bytes < pbs::select_workspace_bytes(d)) return PBS_E_WORKSPACE;
+  return status_of(pbs::launch_block_select(d, q, k_perm, k_pool, scale, mode, param, blk_scores,
+                                            scores_in, counts, idx, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int pbs_attn_fwd(const pbs_shape* shape, const uint16_t* q, const uint16_t* k,
+                 const uint16_t* v, const int32_t* perm, const int32_t* blk_minpos,
+                 const int32_t* counts, const int32_t* idx, float scale, uint16_t* o,
+                 float* lse, void* stream) {
+  Dims d;
+  int st = check_shape(shape, &d);
+  if (st != PBS_OK) return st;
+  if (!finite_positive(scale)) return PBS_E_ARG;
+  if ((counts == nullptr) != (idx == nullptr)) return PBS_E_ARG;
+  if (!counts && (perm || blk_minpos)) return PBS_E_ARG;  // dense mode takes no permutation
+  if (empty(d)) return PBS_OK;
+  const void* const req[] = {q, k, v, o};
+  if ((st = check_required(req)) != PBS_OK) return st;
+  const void* const opt[] = {perm, blk_minpos, counts, idx, lse};
+  for (const void* p : opt)
+    if ((st = check_optional(p)) != PBS_OK) return st;
+  const int mode = !counts ? 0 : (perm ? 1 : 2);
+  return status_of(pbs::launch_attn(d, q, k, v, perm, blk_minpos, counts, idx, mode, scale, o, lse,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI layer (pbs_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pbs {
+
+// Validated problem dimensions.
+struct Dims {
+  int B, Hq, Hkv, N, d, Bs, S;
+  int G;        // Hq / Hkv
+  int nb;       // N / Bs
+  int bps;      // S / Bs
+  int nseg;     // N / S
+  int max_off;  // (nseg - 1) * bps
+};
+
+// Kernel launch through hipLaunchKernel so that the status of this very launch is returned
+// (every kernel takes one argument struct).
+template <typename Args>
+inline hipError_t launch(void (*kernel)(Args), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, const Args& args) {
+  Args copy = args;
+  void* argv[] = {&copy};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, shmem, stream);
+}
+
+// Workspace of pbs_score: per (batch, KV head, segment, scoring row) softmax max and sum.
+size_t score_workspace_bytes(const Dims& d);
+hipError_t launch_score(const Dims& d, const uint16_t* q, const uint16_t* k, float scale,
+                        float* scores, void* ws, hipStream_t stream);
+
+hipError_t launch_permute(const Dims& d, const float* scores, const uint16_t* k,
+                          const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
+                          float* k_pool, int32_t* blk_minpos, hipStream_t stream);
+
+// Workspace of pbs_block_select: pooled queries (and pooled keys when not supplied).
+size_t select_workspace_bytes(const Dims& d);
+hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t* k_perm,
+                               const float* k_pool, float scale, int mode, double param,
+                               float* blk_scores, bool scores_in, int32_t* counts, int32_t* idx,
+                               void* ws, hipStream_t stream);
+
+// mode: 0 dense causal, 1 PBS with a permutation, 2 PBS in the identity order.
+hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const int32_t* perm, const int32_t* blk_minpos, const int32_t* counts,
+                       const int32_t* idx, int mode, float scale, uint16_t* o, float* lse,
+                       hipStream_t stream);
+
+}  // namespace pbs

@@ -1,0 +1,137 @@
+// pbs_permute: segmented argsort of the key scores and gather of the permuted K / V (gfx950).
+//
+// What it computes (arXiv 2510.21270; gist.science summary, Methodik 2: permutation only inside
+// contiguous, non-overlapping segments of size S; Methodik 3 "Sortierung": keys in descending
+// order of importance inside each segment; sciencestack.ai page, Lemma 3.1: keys and values
+// move together): perm[p] = original position of the key at slot p; k_perm / v_perm are bit
+// copies of the rows in that order.
+//
+// Kernels:
+//  * seg_sort: one workgroup per (batch, KV head, segment).  The segment's scores become 64-bit
+//    keys (order-preserving float bits, inverted for descending order, with the in-segment
+//    position in the low word so equal scores keep their original order) and are sorted by a
+//    bitonic network in LDS (S <= 16384 keys = 128 KiB).
+//  * gather: one workgroup per (batch, KV head, block of Bs slots).  16-byte lanes read whole
+//    source rows (a row of K is contiguous, so every group of D/8 lanes issues one coalesced
+//    row read) and write the permuted rows contiguously; the same pass produces the float32
+//    mean of the block's keys (reduced through LDS) and the block's smallest original position.
+#include "pbs_device.h"
+#include "pbs_internal.h"
+
+namespace pbs {
+namespace {
+
+struct SortArgs {
+  const float* scores;
+  int32_t* perm;
+  int N, S, n2;
+};
+
+__global__ __launch_bounds__(1024) void seg_sort_kernel(SortArgs a) {
+  extern __shared__ uint64_t keys[];
+  const int sigma = blockIdx.x;
+  const size_t base = static_cast<size_t>(blockIdx.y) * a.N + static_cast<size_t>(sigma) * a.S;
+  for (int p = threadIdx.x; p < a.n2; p += blockDim.x)
+    keys[p] = (p < a.S) ? desc_sort_key(a.scores[base + p], static_cast<uint32_t>(p)) : ~0ull;
+  bitonic_sort_lds(keys, a.n2);
+  const int s0 = sigma * a.S;
+  for (int p = threadIdx.x; p < a.S; p += blockDim.x)
+    a.perm[base + p] = s0 + static_cast<int32_t>(keys[p] & 0xffffffffull);
+}
+
+struct GatherArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* perm;
+  uint16_t* k_perm;
+  uint16_t* v_perm;
+  float* k_pool;
+  int32_t* minpos;
+  int N, nb;
+};
+
+template <int D, int BS>
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+  constexpr int CH = D / 8;        // 16-byte chunks per row
+  constexpr int RP = 256 / CH;     // rows per pass
+  __shared__ float red[RP * D];
+  __shared__ int32_t mins[256];
+  const int tid = threadIdx.x;
+  const int c = tid % CH, rg = tid / CH;
+  const int j = blockIdx.x;
+  const int bh = blockIdx.y;
+  const size_t head = static_cast<size_t>(bh) * a.N;
+  float sum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sum[e] = 0.f;
+  int mn = 0x7fffffff;
+#pragma unroll 4
+  for (int r = rg; r < BS; r += RP) {
+    const size_t p = head + static_cast<size_t>(j) * BS + r;
+    const int src = a.perm[p];
+    mn = min(mn, src);
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(a.k + (head + src) * D + c * 8);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v + (head + src) * D + c * 8);
+    *reinterpret_cast<u32x4*>(a.k_perm + p * D + c * 8) = kv;
+    *reinterpret_cast<u32x4*>(a.v_perm + p * D + c * 8) = vv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sum[2 * e] += __uint_as_float(kv[e] << 16);
+      sum[2 * e + 1] += __uint_as_float(kv[e] & 0xffff0000u);
+    }
+  }
+  if (a.k_pool) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rg * D + c * 8 + e] = sum[e];
+  }
+  mins[tid] = mn;
+  __syncthreads();
+  if (a.k_pool) {
+    for (int dd = tid; dd < D; dd += 256) {
+      float tot = 0.f;
+      for (int q = 0; q < RP; ++q) tot += red[q * D + dd];
+      a.k_pool[(static_cast<size_t>(bh) * a.nb + j) * D + dd] = tot / static_cast<float>(BS);
+    }
+  }
+  if (a.minpos) {
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s) mins[tid] = min(mins[tid], mins[tid + s]);
+      __syncthreads();
+    }
+    if (tid == 0) a.minpos[static_cast<size_t>(bh) * a.nb + j] = mins[0];
+  }
+}
+
+template <int D, int BS>
+hipError_t launch_gather_t(const Dims& d, const GatherArgs& a, hipStream_t stream) {
+  return launch(gather_kernel<D, BS>, dim3(d.nb, d.B * d.Hkv), dim3(256), 0, stream, a);
+}
+
+}  // namespace
+
+hipError_t launch_permute(const Dims& d, const float* scores, const uint16_t* k,
+                          const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
+                          float* k_pool, int32_t* blk_minpos, hipStream_t stream) {
+  SortArgs sa;
+  sa.scores = scores; sa.perm = perm; sa.N = d.N; sa.S = d.S;
+  int n2 = 1;
+  while (n2 < d.S) n2 <<= 1;
+  sa.n2 = n2;
+  const size_t shmem = static_cast<size_t>(n2) * sizeof(uint64_t);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(seg_sort_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(shmem));
+  if (e != hipSuccess) return e;
+  const int threads = n2 >= 1024 ? 1024 : (n2 >= 64 ? n2 : 64);
+  e = launch(seg_sort_kernel, dim3(d.nseg, d.B * d.Hkv), dim3(threads), shmem, stream, sa);
+  if (e != hipSuccess) return e;
+  GatherArgs ga;
+  ga.k = k; ga.v = v; ga.perm = perm; ga.k_perm = k_perm; ga.v_perm = v_perm;
+  ga.k_pool = k_pool; ga.minpos = blk_minpos; ga.N = d.N; ga.nb = d.nb;
+  if (d.d == 128 && d.Bs == 128) return launch_gather_t<128, 128>(d, ga, stream);
+  if (d.d == 128 && d.Bs == 64) return launch_gather_t<128, 64>(d, ga, stream);
+  if (d.d == 64 && d.Bs == 128) return launch_gather_t<64, 128>(d, ga, stream);
+  return launch_gather_t<64, 64>(d, ga, stream);
+}
+
+}  // namespace pbs

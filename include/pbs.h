@@ -1,0 +1,185 @@
+/*
+ * pbs.h -- C ABI of libpbs, Permuted Block-Sparse Attention (PBS-Attn) prefill on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (arXiv 2510.21270, "Sparser Block-Sparse Attention via Token Permutation";
+ * sciencestack.ai page: Abstract, Fig. 1 caption, Lemma 3.1; gist.science summary: Methodik
+ * 2-4) computes causal prefill attention in four steps, one entry point each:
+ *   pbs_score         importance of every key, from the last block of queries
+ *   pbs_permute       segment-local descending sort of the keys; permuted copies of K and V
+ *   pbs_block_select  per query block, which earlier-segment key blocks to compute
+ *   pbs_attn_fwd      block-sparse flash attention over those blocks plus the whole own
+ *                     segment (token-level causal mask through the stored positions)
+ *
+ * Conventions shared by every call
+ *  - Tensors are DEVICE pointers owned by the caller, contiguous, batch-major "BHND":
+ *    Q/O [B, Hq, N, d], K/V [B, Hkv, N, d]; bf16 is passed as uint16_t bit patterns.
+ *    Every pointer must be 16-byte aligned (PBS_E_ALIGN otherwise).
+ *  - Query head g reads KV head g / (Hq / Hkv) (grouped-query attention).
+ *  - Block size Bs (the pages' B) and segment size S (the pages' S) come in pbs_shape.
+ *    Required: Hq % Hkv == 0, d in {64, 128}, Bs in {64, 128}, S % Bs == 0, N % S == 0,
+ *    S <= 16384, N / Bs <= 8192 (PBS_E_SHAPE otherwise).  batch == 0 or seq_len == 0 is an
+ *    empty problem: once the shape and the scalar arguments are valid the call returns PBS_OK
+ *    without launching anything or inspecting the pointers.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).  The
+ *    library never allocates or frees device memory, never synchronises, and keeps no
+ *    mutable global state; calls on different streams with disjoint outputs may overlap.
+ *  - Return value: PBS_OK (0) or a negative pbs_status.  All arguments are checked before
+ *    any launch, so an error return means nothing was enqueued, except PBS_E_LAUNCH (a
+ *    launch was rejected by the runtime; earlier kernels of the same call may have run).
+ *    Outputs are only valid once the stream has reached the call.
+ */
+#ifndef PBS_H
+#define PBS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pbs_shape {
+  int32_t batch;     /* B                                                */
+  int32_t heads_q;   /* Hq, query heads                                  */
+  int32_t heads_kv;  /* Hkv, key/value heads (Hq % Hkv == 0)             */
+  int32_t seq_len;   /* N                                                */
+  int32_t head_dim;  /* d, 64 or 128                                     */
+  int32_t block;     /* Bs, attention block size, 64 or 128              */
+  int32_t segment;   /* S, permutation segment size, multiple of Bs      */
+} pbs_shape;
+
+typedef enum pbs_status {
+  PBS_OK = 0,
+  PBS_E_ARG = -1,       /* NULL where a pointer is required, bad mode / flag / parameter */
+  PBS_E_SHAPE = -2,     /* shape outside the supported set above                          */
+  PBS_E_ALIGN = -3,     /* a pointer not 16-byte aligned                                  */
+  PBS_E_WORKSPACE = -4, /* workspace smaller than pbs_workspace_bytes()                   */
+  PBS_E_LAUNCH = -5     /* the HIP runtime rejected a kernel launch                       */
+} pbs_status;
+
+typedef enum pbs_select_mode {
+  PBS_SELECT_KEEP_RATIO = 0, /* keep max(1, floor(r * n)) of the n candidate blocks, 0 < r <= 1   */
+  PBS_SELECT_COVERAGE = 1    /* keep the fewest top blocks whose probability reaches tau, 0 < tau <= 1 */
+} pbs_select_mode;
+
+/* pbs_block_select flag: read the block probabilities from `blk_scores` instead of
+   computing them (selection only). */
+#define PBS_FLAG_SCORES_IN 1
+
+/* Bytes of device workspace that pbs_score and pbs_block_select need for `shape`
+   (the larger of the two).  0 for an invalid shape. */
+size_t pbs_workspace_bytes(const pbs_shape* shape);
+
+/* Row stride of the `idx` lists: (N/S - 1) * (S/Bs), the number of key blocks in earlier
+   segments for the last segment.  -1 for an invalid shape. */
+int32_t pbs_max_offdiag(const pbs_shape* shape);
+
+/* Static description of a status code. */
+const char* pbs_strerror(int status);
+
+/*
+ * pbs_score -- query-aware key importance from the last query block.
+ * Passage: gist.science summary, Methodik 3 ("Proxy-Bewertung"): the global importance of
+ * the keys is estimated from the last block of queries by mean pooling of their attention
+ * scores; Methodik 2: no attention crosses into a later segment.
+ *
+ * For every KV head h and key j in segment s:
+ *   scores[b,h,j] = 1/(G*Bs) * sum over q-heads g of h and rows t in [N-Bs, N) of
+ *                   softmax over keys j' of segment s with j' <= t of (scale * <q[b,g,t], k[b,h,j']>), at j
+ * (0 where j > t).  Each segment's scores sum to 1.
+ *   q        [B,Hq,N,d] bf16 (only the last Bs rows of each head are read)
+ *   k        [B,Hkv,N,d] bf16
+ *   scale    softmax scale, normally 1/sqrt(d)
+ *   scores   [B,Hkv,N] float32, written
+ *   workspace / workspace_bytes   device scratch of at least pbs_workspace_bytes(shape)
+ */
+int pbs_score(const pbs_shape* shape, const uint16_t* q, const uint16_t* k, float scale,
+              float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pbs_permute -- segmented permutation of keys and values.
+ * Passage: gist.science summary, Methodik 2 (permutation only inside contiguous segments of
+ * size S) and Methodik 3 ("Sortierung": keys sorted by descending importance in each
+ * segment); sciencestack.ai page, Lemma 3.1 (keys and values move together).
+ *
+ * Within each segment, slots are ordered by score descending, ties by lower original
+ * position (-0 equals +0; NaN after every number):
+ *   perm[b,h,p]      original position of the key at slot p (int32, stays in p's segment)
+ *   k_perm[b,h,p,:]  = k[b,h,perm[b,h,p],:]   (bit copy), same for v_perm
+ *   k_pool[b,h,j,:]  float32 mean of k_perm rows of block j (optional, may be NULL;
+ *                    pbs_block_select can reuse it)
+ *   blk_minpos[b,h,j] smallest original position held by block j (optional, may be NULL;
+ *                    lets pbs_attn_fwd skip own-segment blocks no query of a block can see)
+ *   scores [B,Hkv,N] float32, k/v [B,Hkv,N,d] bf16 -> perm [B,Hkv,N], k_perm/v_perm
+ *   [B,Hkv,N,d], k_pool [B,Hkv,N/Bs,d], blk_minpos [B,Hkv,N/Bs].
+ */
+int pbs_permute(const pbs_shape* shape, const float* scores, const uint16_t* k,
+                const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
+                float* k_pool, int32_t* blk_minpos, void* stream);
+
+/*
+ * pbs_block_select -- which earlier-segment key blocks each query block computes.
+ * Passage: gist.science summary, Methodik 4 ("Block-Auswahl": block importance from mean
+ * pooling on the permuted keys); sciencestack.ai page, Fig. 1 caption (blocks of the own,
+ * on-diagonal segment are always computed; inter-segment blocks may be skipped) and Fig. 2
+ * caption (coverage = attention mass of the selected blocks); skillmd.com page, Implementation
+ * Steps (active-block count max(1, int(num_blocks * keep))).
+ *
+ * For query block i of segment s = i / (S/Bs), the candidates are key blocks j < s*(S/Bs):
+ *   P[i,j] = softmax over candidates of scale * <mean of q rows of block i,
+ *                                              mean of k_perm rows of block j>
+ * ranked by P descending, ties to the lower j; kept:
+ *   PBS_SELECT_KEEP_RATIO (param = r):   the first max(1, floor(r*n)) (in double), n = #candidates
+ *   PBS_SELECT_COVERAGE   (param = tau): the shortest prefix whose sequential float32 sum of
+ *                                        P (compared in double) is >= tau; all n if none.
+ *   q          [B,Hq,N,d] bf16
+ *   k_perm     [B,Hkv,N,d] bf16 (permuted keys; the natural K gives plain block-sparse
+ *              selection). May be NULL if k_pool is given.
+ *   k_pool     [B,Hkv,N/Bs,d] float32 block means of k_perm, or NULL (then computed here)
+ *   blk_scores [B,Hq,N/Bs,N/Bs] float32 or NULL.  Output of P (0 off the candidates) unless
+ *              flags has PBS_FLAG_SCORES_IN; then P is read from it (candidates only).
+ *   counts     [B,Hq,N/Bs] int32, written: number kept (0 for the first segment)
+ *   idx        [B,Hq,N/Bs,pbs_max_offdiag] int32, written: kept block indices ascending in
+ *              the first counts entries of each row; the rest of a row is left untouched
+ *   workspace  at least pbs_workspace_bytes(shape) bytes
+ */
+int pbs_block_select(const pbs_shape* shape, const uint16_t* q, const uint16_t* k_perm,
+                     const float* k_pool, float scale, int mode, double param,
+                     float* blk_scores, int flags, int32_t* counts, int32_t* idx,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pbs_attn_fwd -- block-sparse flash-attention forward with permuted keys.
+ * Passage: sciencestack.ai page, Fig. 1 caption (own-segment blocks computed under the causal
+ * mask, inter-segment blocks skippable) and Lemma 3.1 (a joint key/value permutation leaves
+ * attention unchanged); gist.science summary, Methodik 3 ("Handling von Queries": queries keep
+ * their natural order, so the output is already in original token order) and Methodik 4
+ * ("Kernel").
+ *
+ * PBS mode (counts and idx given): query row t of block i in segment s attends to
+ *   - every key of the kept blocks idx[b,g,i,0..counts) (whole blocks, no mask), and
+ *   - every key of segment s with original position <= t: the own segment's blocks are
+ *     walked in the order of `k`, and slot p is visible to row t iff perm[b,h,p] <= t
+ *     (perm NULL: identity order, plain block-sparse attention).
+ * Dense mode (perm, counts, idx all NULL): plain causal attention over keys 0..t.
+ *   q      [B,Hq,N,d] bf16 (natural order)
+ *   k, v   [B,Hkv,N,d] bf16: k_perm/v_perm from pbs_permute in PBS mode, natural K/V in
+ *          dense mode or with perm == NULL
+ *   perm   [B,Hkv,N] int32 or NULL;  blk_minpos [B,Hkv,N/Bs] int32 or NULL (skip hint)
+ *   counts [B,Hq,N/Bs], idx [B,Hq,N/Bs,pbs_max_offdiag] int32 from pbs_block_select, or NULL
+ *   o      [B,Hq,N,d] bf16, written, original token order
+ *   lse    [B,Hq,N] float32 natural-log softmax normaliser of every row, or NULL
+ * counts and idx are trusted to come from pbs_block_select; an out-of-range count or index is
+ * clamped into range (memory-safe, result unspecified).
+ */
+int pbs_attn_fwd(const pbs_shape* shape, const uint16_t* q, const uint16_t* k,
+                 const uint16_t* v, const int32_t* perm, const int32_t* blk_minpos,
+                 const int32_t* counts, const int32_t* idx, float scale, uint16_t* o,
+                 float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PBS_H */

@@ -1,0 +1,94 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header declares, and
+rejects bad arguments before touching the GPU (no compute call here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_pbs_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "pbs.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pbs_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(P.ENTRY_POINTS)
+    L = P.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_shape_rules():
+    good = P.make_shape(1, 32, 8, 131072, 128, 128, 8192)
+    assert P.pbs_max_offdiag(good) == 15 * 64
+    assert P.pbs_workspace_bytes(good) > 0
+    bad = [P.make_shape(1, 32, 8, 1000, 128, 128, 256),   # N % S
+           P.make_shape(1, 32, 8, 1024, 128, 128, 192),   # S % Bs
+           P.make_shape(1, 30, 8, 1024, 128, 128, 256),   # Hq % Hkv
+           P.make_shape(1, 32, 8, 1024, 96, 128, 256),    # d
+           P.make_shape(1, 32, 8, 1024, 128, 32, 256),    # Bs
+           P.make_shape(1, 32, 8, 65536, 128, 128, 32768),  # S too large
+           P.make_shape(1, 32, 8, 8192 * 64 * 2, 128, 64, 64)]  # too many blocks
+    for s in bad:
+        assert P.pbs_max_offdiag(s) == -1
+        assert P.pbs_workspace_bytes(s) == 0
+
+
+def _call(fn, *args):
+    return getattr(P.lib(), fn)(*args)
+
+
+def test_errors_before_any_launch():
+    s = P.make_shape(1, 4, 2, 1024, 128, 128, 256)
+    S = ctypes.byref(s)
+    fake = 0x10000  # an aligned, never dereferenced address: every call below fails validation
+    assert _call("pbs_score", ctypes.byref(P.make_shape(1, 4, 2, 1000, 128, 128, 256)), fake, fake,
+                 0.1, fake, fake, 1 << 30, None) == P.PBS_E_SHAPE
+    assert _call("pbs_score", S, None, fake, 0.1, fake, fake, 1 << 30, None) == P.PBS_E_ARG
+    assert _call("pbs_score", S, fake + 4, fake, 0.1, fake, fake, 1 << 30, None) == P.PBS_E_ALIGN
+    assert _call("pbs_score", S, fake, fake, 0.1, fake, fake, 16, None) == P.PBS_E_WORKSPACE
+    assert _call("pbs_score", S, fake, fake, -1.0, fake, fake, 1 << 30, None) == P.PBS_E_ARG
+    assert _call("pbs_permute", S, fake, None, fake, fake, fake, fake, None, None, None) == P.PBS_E_ARG
+    assert _call("pbs_permute", S, fake, fake, fake, fake, fake, fake, fake + 8, None, None) == P.PBS_E_ALIGN
+    sel = lambda mode, param, flags, ws=1 << 30, bs=None: _call(
+        "pbs_block_select", S, fake, fake, None, 0.1, mode, param, bs, flags, fake, fake, fake, ws, None)
+    assert sel(2, 0.5, 0) == P.PBS_E_ARG
+    assert sel(0, 0.0, 0) == P.PBS_E_ARG
+    assert sel(1, 1.5, 0) == P.PBS_E_ARG
+    assert sel(0, 0.5, 4) == P.PBS_E_ARG
+    assert sel(0, 0.5, P.PBS_FLAG_SCORES_IN) == P.PBS_E_ARG   # probabilities in, but none given
+    assert sel(0, 0.5, 0, ws=16) == P.PBS_E_WORKSPACE
+    attn = lambda perm, minpos, counts, idx: _call(
+        "pbs_attn_fwd", S, fake, fake, fake, perm, minpos, counts, idx, 0.1, fake, None, None)
+    assert attn(None, None, fake, None) == P.PBS_E_ARG          # counts without idx
+    assert attn(fake, None, None, None) == P.PBS_E_ARG          # permutation in dense mode
+    assert attn(fake, fake + 4, fake, fake) == P.PBS_E_ALIGN
+
+
+def test_empty_problem_is_ok_without_pointers():
+    s = P.make_shape(0, 4, 2, 1024, 128, 128, 256)
+    assert _call("pbs_attn_fwd", ctypes.byref(s), None, None, None, None, None, None, None, 0.1,
+                 None, None, None) == P.PBS_OK
+    s = P.make_shape(2, 4, 2, 0, 128, 128, 256)
+    assert _call("pbs_permute", ctypes.byref(s), None, None, None, None, None, None, None, None,
+                 None) == P.PBS_OK
+
+
+def test_strerror():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert P.pbs_strerror(code)
+    assert P.pbs_strerror(-99) == "unknown status"
+
+
+def test_binding_raises_pbs_error():
+    s = P.make_shape(1, 4, 2, 1000, 128, 128, 256)
+    with pytest.raises(P.PbsError) as e:
+        P.pbs_attn_fwd(s, 0x10000, 0x10000, 0x10000, None, None, None, None, 0.1, 0x10000, None, stream=0)
+    assert e.value.code == P.PBS_E_SHAPE

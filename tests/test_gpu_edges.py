@@ -1,0 +1,166 @@
+"""GPU edge cases: degenerate shapes of the method, sort specials, extreme sizes, determinism."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_pbs_amd as P
+import oracle
+import pbs_synth
+from gpu_helpers import (check_attn, dev, dev_bf16, lists_equal, run_attn, run_permute, run_select,
+                         say, shape)
+
+pytestmark = pytest.mark.gpu
+
+
+def _planted(Hq, Hkv, N, d, Bs, S, seed):
+    w = pbs_synth.WORKLOADS["gqa_8k"].scaled(heads_q=Hq, heads_kv=Hkv, seq_len=N, head_dim=d,
+                                             block=Bs, segment=S, seed=seed)
+    return w, pbs_synth.make_inputs(w)
+
+
+def test_keep_one_equals_dense():
+    """Keep ratio 1 keeps every earlier-segment block: PBS equals dense causal attention."""
+    say("keep=1 vs dense")
+    w, inp = _planted(8, 2, 2048, 128, 128, 512, 11)
+    scale = oracle.default_scale(128)
+    od, _ = oracle.dense_causal(inp["q"], inp["k"], inp["v"], block=128, scale=scale)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    bufs = P.prefill(q, k, v, block=128, segment=512, keep=1.0, scale=scale)
+    dense = P.dense_causal(q, k, v, block=128, scale=scale)
+    torch.cuda.synchronize()
+    nb = 2048 // 128
+    want = np.array([(i // 4) * 4 for i in range(nb)])
+    assert (bufs.counts.cpu().numpy() == want[None, None, :]).all()
+    check_attn(bufs.o.float().cpu().numpy(), od, "keep=1 PBS vs oracle dense")
+    check_attn(dense.float().cpu().numpy(), od, "GPU dense vs oracle dense")
+
+
+def test_single_segment_is_dense():
+    """S = N: no earlier segment, no candidate, PBS equals dense causal for any ratio."""
+    say("S = N")
+    w, inp = _planted(4, 2, 1024, 128, 128, 1024, 12)
+    scale = oracle.default_scale(128)
+    od, _ = oracle.dense_causal(inp["q"], inp["k"], inp["v"], block=128, scale=scale)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    bufs = P.prefill(q, k, v, block=128, segment=1024, keep=0.1, scale=scale)
+    torch.cuda.synchronize()
+    assert (bufs.counts.cpu().numpy() == 0).all()
+    check_attn(bufs.o.float().cpu().numpy(), od, "S=N PBS vs oracle dense")
+
+
+def test_tiny_keep_ratio_keeps_one_block():
+    say("tiny keep ratio")
+    w, inp = _planted(2, 1, 1024, 64, 64, 128, 13)
+    scale = oracle.default_scale(64)
+    ref = oracle.prefill(inp["q"], inp["k"], inp["v"], block=64, segment=128, scale=scale,
+                         mode=oracle.KEEP, param=1e-6)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    bufs = P.prefill(q, k, v, block=64, segment=128, keep=1e-6, scale=scale)
+    torch.cuda.synchronize()
+    c = bufs.counts.cpu().numpy()
+    assert ((c == 1) | (np.arange(16)[None, None, :] < 2)).all()
+    check_attn(bufs.o.float().cpu().numpy(), ref["o"], "keep=1e-6 end-to-end")
+
+
+def test_sort_specials_bitexact():
+    """Ties, signed zeros and NaN in the scores: the GPU permutation equals the oracle's."""
+    say("sort specials")
+    rng = np.random.default_rng(3)
+    B, H, N, d, Bs, S = 1, 2, 2048, 64, 64, 1024
+    vals = np.array([0.0, -0.0, 1e-30, 0.25, 0.25, np.nan, -1.0, np.inf, 3.0], np.float32)
+    sc = rng.choice(vals, size=(B, H, N)).astype(np.float32)
+    k = pbs_synth.random_bf16((B, H, N, d), 5)
+    v = pbs_synth.random_bf16((B, H, N, d), 6)
+    sh = shape(B, H, H, N, d, Bs, S)
+    perm, kp, vp, _, _ = run_permute(sh, dev(sc), dev_bf16(k), dev_bf16(v), pool=False, minpos=False)
+    assert np.array_equal(perm.cpu().numpy(), oracle.segment_permutation(sc, segment=S))
+
+
+def test_select_handworked_rows_on_gpu():
+    """Hand-made probability rows (exact in binary): the GPU selection matches the oracle,
+    including the >= boundary of coverage and the sequential float32 sum."""
+    say("select handworked")
+    B, Hq, N, d, Bs, S = 1, 1, 640, 64, 64, 320   # 10 blocks, 2 segments of 5 blocks
+    Pm = np.zeros((B, Hq, 10, 10), np.float32)
+    rows = [[0.125, 0.25, 0.25, 0.0625, 0.125], [0.2] * 5, [0.0, 0.0, 0.0, 0.0, 1.0],
+            [0.75, 2.0 ** -25, 2.0 ** -25, 2.0 ** -25, 0.0], [0.25, 0.5, 0.125, 0.125, 0.0]]
+    for r, vals in enumerate(rows):
+        Pm[0, 0, 5 + r, :5] = vals
+    sh = shape(B, Hq, 1, N, d, Bs, S)
+    for mode, cmode, param in ((oracle.KEEP, P.PBS_SELECT_KEEP_RATIO, 0.5),
+                               (oracle.COVERAGE, P.PBS_SELECT_COVERAGE, 0.75),
+                               (oracle.COVERAGE, P.PBS_SELECT_COVERAGE, 0.75 + 2.0 ** -24),
+                               (oracle.COVERAGE, P.PBS_SELECT_COVERAGE, 1.0)):
+        rc, ri = oracle.select_blocks(Pm, block=Bs, segment=S, mode=mode, param=param)
+        counts, idx = run_select(sh, None, None, None, 0.125, cmode, param, blk_scores=dev(Pm),
+                                 flags=P.PBS_FLAG_SCORES_IN)
+        assert lists_equal(counts.cpu().numpy(), idx.cpu().numpy(), rc, ri), (mode, param)
+
+
+def test_select_widest_rows():
+    """The widest supported candidate set (8191 blocks, an 8192-entry sort per row)."""
+    say("select widest rows")
+    B, Hq, N, d, Bs, S = 1, 1, 8192 * 64, 64, 64, 64
+    nb = N // Bs
+    rng = np.random.default_rng(8)
+    rows = [nb - 1, nb - 2, 4097, 100, 1]
+    Pm = np.zeros((B, Hq, nb, nb), np.float32)
+    for i in rows:
+        x = rng.normal(size=i)
+        e = np.exp(x - x.max())
+        Pm[0, 0, i, :i] = (e / e.sum()).astype(np.float32)
+    sh = shape(B, Hq, 1, N, d, Bs, S)
+    assert P.pbs_max_offdiag(sh) == 8191
+    for mode, cmode, param in ((oracle.KEEP, P.PBS_SELECT_KEEP_RATIO, 0.1),
+                               (oracle.COVERAGE, P.PBS_SELECT_COVERAGE, 0.9)):
+        counts, idx = run_select(sh, None, None, None, 0.125, cmode, param, blk_scores=dev(Pm),
+                                 flags=P.PBS_FLAG_SCORES_IN)
+        c, ix = counts.cpu().numpy(), idx.cpu().numpy()
+        for i in rows:
+            sub = Pm[:, :, i:i + 1, :]
+            # the oracle's selection of one row, laid out as a single-candidate-row problem
+            order = oracle.descending_order(sub[0, 0, 0, :i])
+            if mode == oracle.KEEP:
+                kk = oracle.keep_count(i, param)
+            else:
+                cs = np.add.accumulate(sub[0, 0, 0, :i][order], dtype=np.float32).astype(np.float64)
+                hit = np.nonzero(cs >= param)[0]
+                kk = int(hit[0]) + 1 if hit.size else i
+            assert c[0, 0, i] == kk
+            assert np.array_equal(ix[0, 0, i, :kk], np.sort(order[:kk]))
+
+
+def test_permute_largest_segment():
+    """The largest supported segment (16384 keys sorted in one workgroup)."""
+    say("permute S=16384")
+    B, H, N, d, Bs, S = 1, 1, 32768, 128, 128, 16384
+    rng = np.random.default_rng(9)
+    sc = (rng.random((B, H, N)) * 1e-3).astype(np.float32)
+    sc[0, 0, ::7] = sc[0, 0, 3]                 # many ties
+    k = pbs_synth.random_bf16((B, H, N, d), 10)
+    v = pbs_synth.random_bf16((B, H, N, d), 11)
+    sh = shape(B, H, H, N, d, Bs, S)
+    perm, kp, vp, _, mpos = run_permute(sh, dev(sc), dev_bf16(k), dev_bf16(v), pool=False)
+    ref = oracle.segment_permutation(sc, segment=S)
+    assert np.array_equal(perm.cpu().numpy(), ref)
+    assert np.array_equal(mpos.cpu().numpy(), ref.reshape(B, H, N // Bs, Bs).min(-1))
+
+
+def test_deterministic():
+    """Two runs of the whole pipeline give bitwise-identical results."""
+    say("determinism")
+    w, inp = _planted(8, 2, 2048, 128, 128, 512, 14)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    a = P.prefill(q, k, v, block=128, segment=512, coverage=0.9)
+    b = P.prefill(q, k, v, block=128, segment=512, coverage=0.9)
+    torch.cuda.synchronize()
+    for name in ("scores", "perm", "k_perm", "v_perm", "k_pool", "counts", "o", "lse"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    assert lists_equal(a.counts.cpu().numpy(), a.idx.cpu().numpy(), b.counts.cpu().numpy(),
+                       b.idx.cpu().numpy())
+
+
+def test_empty_problem_launches_nothing():
+    sh = shape(0, 4, 2, 1024, 128, 128, 256)
+    P.pbs_attn_fwd(sh, 0, 0, 0, None, None, None, None, 0.1, 0)
+    P.pbs_score(sh, 0, 0, 0.1, 0, 0, 0)

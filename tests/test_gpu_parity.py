@@ -1,0 +1,170 @@
+"""GPU parity of every stage of the PBS-Attn path against the CPU oracle, through the C ABI.
+
+Bars: permutations and block lists bit-exact when both sides start from the same float32
+values (the oracle's scores / block probabilities); scores and block probabilities within a
+relative 1e-4; attention within max-abs 2e-2 and mean-abs 2e-3 of the float64 oracle.
+
+Cases are small enough for the oracle to finish in seconds and still span several blocks and
+segments, ragged segment counts (S = 3 Bs), both head dims and block sizes, GQA groups of 4 and 7,
+and both selection rules."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_pbs_amd as P
+import oracle
+import pbs_synth
+from gpu_helpers import (check_attn, dev, dev_bf16, host_bits, lists_equal, run_attn, run_permute,
+                         run_score, run_select, say, shape)
+
+pytestmark = pytest.mark.gpu
+
+SCORE_RTOL = 1e-4
+
+# name -> (Hq, Hkv, N, d, Bs, S, mode, param)
+CASES = {
+    "toy_1k": (1, 1, 1024, 64, 64, 256, "keep", 0.5),
+    "gqa4_2k_keep": (8, 2, 2048, 128, 128, 512, "keep", 0.3),
+    "gqa7_1536_ragged": (14, 2, 1536, 128, 128, 384, "keep", 0.25),
+    "d64_bs128_cov": (4, 2, 1024, 64, 128, 256, "coverage", 0.9),
+    "d128_bs64_cov": (4, 1, 1152, 128, 64, 192, "coverage", 0.8),
+}
+
+
+def _inputs(name):
+    Hq, Hkv, N, d, Bs, S, mode, param = CASES[name]
+    w = pbs_synth.WORKLOADS["gqa_8k"].scaled(name=name, heads_q=Hq, heads_kv=Hkv, seq_len=N,
+                                             head_dim=d, block=Bs, segment=S, mode=mode,
+                                             params=(param,), seed=zlib.crc32(name.encode()) % 100000)
+    return w, pbs_synth.make_inputs(w)
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def case(request):
+    name = request.param
+    w, inp = _inputs(name)
+    scale = oracle.default_scale(w.head_dim)
+    mode = oracle.KEEP if w.mode == "keep" else oracle.COVERAGE
+    ref = oracle.prefill(inp["q"], inp["k"], inp["v"], block=w.block, segment=w.segment,
+                         scale=scale, mode=mode, param=w.params[0])
+    ref["dense_o"], ref["dense_lse"] = oracle.dense_causal(inp["q"], inp["k"], inp["v"],
+                                                           block=w.block, scale=scale)
+    sh = shape(w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment)
+    g = dict(q=dev_bf16(inp["q"]), k=dev_bf16(inp["k"]), v=dev_bf16(inp["v"]))
+    say(f"case {name}: shape {CASES[name]}")
+    return dict(name=name, w=w, inp=inp, ref=ref, scale=scale, sh=sh, g=g,
+                cmode=P.PBS_SELECT_KEEP_RATIO if w.mode == "keep" else P.PBS_SELECT_COVERAGE)
+
+
+def test_scores(case):
+    say(case["name"], "pbs_score")
+    s = run_score(case["sh"], case["g"]["q"], case["g"]["k"], case["scale"]).cpu().numpy()
+    ref = case["ref"]["scores"].astype(np.float64)
+    rel = np.abs(s - ref) / np.abs(ref)
+    say(f"scores max rel err {rel.max():.2e}")
+    assert rel.max() <= SCORE_RTOL
+    S = case["w"].segment
+    sums = s.astype(np.float64).reshape(s.shape[0], s.shape[1], -1, S).sum(-1)
+    assert np.allclose(sums, 1.0, atol=1e-4)
+
+
+def test_permute_bitexact_given_oracle_scores(case):
+    say(case["name"], "pbs_permute")
+    sh, ref = case["sh"], case["ref"]
+    perm, kp, vp, kpool, mpos = run_permute(sh, dev(ref["scores"]), case["g"]["k"], case["g"]["v"])
+    assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+    assert np.array_equal(host_bits(kp), ref["k_perm"])
+    assert np.array_equal(host_bits(vp), ref["v_perm"])
+    B, H, N = ref["perm"].shape
+    Bs = sh.block
+    assert np.array_equal(mpos.cpu().numpy(), ref["perm"].reshape(B, H, N // Bs, Bs).min(-1))
+    kbar = oracle.pooled_blocks(ref["k_perm"], Bs)
+    assert np.allclose(kpool.cpu().numpy(), kbar, rtol=1e-5, atol=1e-6)
+
+
+def test_select_bitexact_given_oracle_probabilities(case):
+    say(case["name"], "pbs_block_select (probabilities in)")
+    ref = case["ref"]
+    w = case["w"]
+    counts, idx = run_select(case["sh"], None, None, None, case["scale"], case["cmode"],
+                             w.params[0], blk_scores=dev(ref["P"]), flags=P.PBS_FLAG_SCORES_IN)
+    assert lists_equal(counts.cpu().numpy(), idx.cpu().numpy(), ref["counts"], ref["idx"])
+
+
+def test_block_probabilities(case):
+    say(case["name"], "pbs_block_select (probabilities computed)")
+    ref, sh, w = case["ref"], case["sh"], case["w"]
+    kp = dev_bf16(ref["k_perm"])
+    nb = w.seq_len // w.block
+    Pg = torch.zeros((w.batch, w.heads_q, nb, nb), dtype=torch.float32, device="cuda")
+    for k_perm, k_pool in ((kp, None), (None, dev(oracle.pooled_blocks(ref["k_perm"], w.block).astype(np.float32)))):
+        counts, idx = run_select(sh, case["g"]["q"], k_perm, k_pool, case["scale"], case["cmode"],
+                                 w.params[0], blk_scores=Pg)
+        got = Pg.cpu().numpy().astype(np.float64)
+        want = ref["P"].astype(np.float64)
+        cand = want > 0
+        assert np.array_equal(got > 0, cand)
+        rel = np.abs(got - want)[cand] / want[cand]
+        say(f"P max rel err {rel.max() if rel.size else 0:.2e}")
+        assert rel.size == 0 or rel.max() <= SCORE_RTOL
+        agree = np.mean(counts.cpu().numpy() == ref["counts"])
+        say(f"count agreement {agree:.4f}")
+
+
+def test_attention_given_oracle_lists(case):
+    say(case["name"], "pbs_attn_fwd (oracle permutation and lists)")
+    ref, sh = case["ref"], case["sh"]
+    B, H, N = ref["perm"].shape
+    Bs = sh.block
+    minpos = ref["perm"].reshape(B, H, N // Bs, Bs).min(-1).astype(np.int32)
+    o, lse = run_attn(sh, case["g"]["q"], dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
+                      dev(ref["perm"]), dev(minpos), dev(ref["counts"]), dev(ref["idx"]),
+                      case["scale"])
+    check_attn(o.float().cpu().numpy(), ref["o"], f"{case['name']} attention")
+    assert np.abs(lse.cpu().numpy() - ref["lse"]).max() < 1e-3
+    # the block-skip hint is only an optimisation: without it the result is the same
+    o2, _ = run_attn(sh, case["g"]["q"], dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
+                     dev(ref["perm"]), None, dev(ref["counts"]), dev(ref["idx"]), case["scale"])
+    assert torch.equal(o, o2)
+
+
+def test_dense_causal(case):
+    say(case["name"], "pbs_attn_fwd dense")
+    ref, sh = case["ref"], case["sh"]
+    o, lse = run_attn(sh, case["g"]["q"], case["g"]["k"], case["g"]["v"], None, None, None, None,
+                      case["scale"])
+    check_attn(o.float().cpu().numpy(), ref["dense_o"], f"{case['name']} dense")
+    assert np.abs(lse.cpu().numpy() - ref["dense_lse"]).max() < 1e-3
+
+
+def test_identity_order_block_sparse(case):
+    """perm = NULL: plain block-sparse attention over the natural key order."""
+    say(case["name"], "pbs_attn_fwd identity order")
+    inp, sh, w = case["inp"], case["sh"], case["w"]
+    mode = oracle.KEEP if w.mode == "keep" else oracle.COVERAGE
+    Pn = oracle.block_probabilities(inp["q"], inp["k"], block=w.block, segment=w.segment,
+                                    scale=case["scale"])
+    cn, ixn = oracle.select_blocks(Pn, block=w.block, segment=w.segment, mode=mode, param=w.params[0])
+    on, _ = oracle.attention(inp["q"], inp["k"], inp["v"], block=w.block, segment=w.segment,
+                             scale=case["scale"], perm=None, counts=cn, idx=ixn)
+    o, _ = run_attn(sh, case["g"]["q"], case["g"]["k"], case["g"]["v"], None, None, dev(cn),
+                    dev(ixn), case["scale"])
+    check_attn(o.float().cpu().numpy(), on, f"{case['name']} identity-order")
+
+
+def test_end_to_end(case):
+    """Whole GPU pipeline against the whole oracle pipeline.  Near-equal float32 scores may be
+    ordered differently by the two sides (rounding), so the permutation and the lists are
+    compared by agreement rate; the output must still meet the attention bar."""
+    say(case["name"], "end-to-end prefill")
+    ref, w, g = case["ref"], case["w"], case["g"]
+    kw = {"keep": w.params[0]} if w.mode == "keep" else {"coverage": w.params[0]}
+    bufs = P.prefill(g["q"], g["k"], g["v"], block=w.block, segment=w.segment, scale=case["scale"], **kw)
+    torch.cuda.synchronize()
+    perm_agree = float(np.mean(bufs.perm.cpu().numpy() == ref["perm"]))
+    cnt_agree = float(np.mean(bufs.counts.cpu().numpy() == ref["counts"]))
+    say(f"perm agreement {perm_agree:.4f}, count agreement {cnt_agree:.4f}")
+    check_attn(bufs.o.float().cpu().numpy(), ref["o"], f"{case['name']} end-to-end")
+    assert perm_agree > 0.5

@@ -4,20 +4,31 @@
 // gist.science summary, Methodik 3 "Handling von Queries" and Methodik 4 "Kernel"): every query
 // row t of query block i, segment s, attends to the keys of the kept earlier-segment blocks of
 // its row (whole blocks) and to every key of its own segment whose ORIGINAL position is <= t.
-// The own segment is walked in the order of the given key tensor (permuted copies), the causal
-// test going through the stored original positions.  Queries are never permuted, so the output
-// is written in original token order.
+// The own segment is walked in the order of the given key tensor (the permuted copies), the
+// causal test going through the stored original positions.  Queries are never permuted, so
+// the output is written in original token order.
 //
-// Design (CDNA4, wave64):
-//  * one workgroup per (query block, query head); BS/32 waves, 32 query rows per wave;
+// Design (CDNA4, wave64, one workgroup of 2*Bs/32 waves per (query block, query head)):
+//  * wave w owns 32 query rows (row group w % (Bs/32)) and, of every key block, one half of the
+//    keys (w / (Bs/32)): two waves per SIMD, so one wave's softmax (VALU) and LDS reads can run
+//    under the other wave's MFMAs.  The two key halves keep separate online-softmax states and
+//    are merged through LDS at the end;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 (A = K rows from
-//    LDS, B = the wave's Q rows kept in registers), so each lane owns ONE query row: the online
-//    softmax max / sum stay in the lane, with a single cross-half exchange per key block;
-//  * the output is accumulated transposed, O^T += V^T P^T: P leaves the score accumulators as
-//    the bf16 B operand without touching LDS (the key order inside a 16-key step is a
-//    relabelling shared by both operands), and V^T is read from the row-major V tile with the
-//    gfx950 transposing LDS load ds_read_b64_tr_b16;
-//  * exp2 with scale*log2(e) folded into one multiply; fp32 accumulators; bf16 output (RNE).
+//    LDS, B = the wave's Q rows held in registers), so each lane owns one query row: the softmax
+//    max / sum need one cross-half exchange per block and fragment;
+//  * the output is accumulated transposed, O^T += V^T P^T: P leaves the score accumulators as the
+//    bf16 B operand without touching LDS (the key order inside a 16-key step is a relabelling
+//    shared by both operands); V^T comes from the row-major V tile through the transposing LDS
+//    load ds_read_b64_tr_b16;
+//  * K/V tiles are double-buffered in LDS and filled by asynchronous direct global->LDS loads
+//    (global_load_lds_dwordx4) one block ahead of the compute; rows are padded by one 16-byte
+//    chunk, which spreads both the K reads (one chunk of 32 rows) and the transposing V reads
+//    (4 rows x 32 bytes) over the banks and keeps every LDS address a base plus an immediate;
+//  * exp2 with scale*log2(e) folded into one FMA per element; the running max is only moved (and
+//    the accumulator rescaled) when it grows by more than 2^8, which keeps every exponent <= 8;
+//  * work order: heaviest query blocks first, and consecutive workgroups of one XCD (the
+//    hardware deals workgroups round-robin over the 8 XCDs) walk one KV head, so the K/V tiles a
+//    head's query blocks share stay in that XCD's L2.
 #include "pbs_device.h"
 #include "pbs_internal.h"
 
@@ -34,209 +45,376 @@ struct AttnArgs {
   const int32_t* idx;
   uint16_t* o;
   float* lse;
-  int Hq, Hkv, G, N, nb, bps, max_off;
+  int B, Hq, Hkv, G, N, nb, bps, max_off;
   int mode;      // 0 dense causal, 1 permuted PBS, 2 identity-order PBS
+  int xcd_map;   // 1: total work items divisible by 8, use the XCD-grouped order
   float c;       // scale * log2(e)
+  // Element offsets of the K/V stage tiles in LDS.  Passed at run time on purpose: the
+  // compiler then keeps one (tile base + lane) address per tile and folds every in-tile offset
+  // (< 64 KiB) into the DS instruction, instead of materialising one register per offset.
+  int tile_off[4];
 };
 
 template <int D, int BS>
-struct AttnCfg {
-  static constexpr int NW = BS / 32;     // waves per workgroup, 32 query rows each
-  static constexpr int NT = NW * kWave;
-  static constexpr int STR = D + 8;      // LDS row stride of the K / V tiles (bf16 elements)
-  static constexpr int NKT = BS / 32;    // 32-key sub-tiles per key block
-  static constexpr int NKS = D / 16;     // 16-wide k-steps over the head dim
-  static constexpr int NMT = D / 32;     // 32-row tiles of O^T over the head dim
+struct Cfg {
+  static constexpr int RG = BS / 32;       // 32-row groups of a query block
+  static constexpr int NW = 2 * RG;        // waves: every row group x two key halves
+  static constexpr int NT = NW * 64;
+  static constexpr int RW = 32;            // query rows per wave
+  static constexpr int KW = BS / 2;        // keys per wave and block
+  static constexpr int NRF = 1;            // 32-row fragments per wave
+  static constexpr int NKT = KW / 32;      // 32-key sub-tiles per wave and block
+  static constexpr int NKS = D / 16;       // 16-wide k-steps over the head dim
+  static constexpr int NMT = D / 32;       // 32-row tiles of O^T over the head dim
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int STR = D + 8;        // LDS row stride (bf16 elements)
+  static constexpr int TILE = BS * STR;    // bf16 elements of one K (or V) tile in LDS
+  static constexpr int NLD = BS * (CPR + 1) / 64;  // 1 KiB direct loads per tile
 };
 
-__device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* lds_ptr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(lds_ptr));
+// LDS tile layout: each row of D bf16 is followed by one spare 16-byte chunk (row stride D + 8
+// elements), which spreads the 32 rows of a K fragment read, and the 4 rows of a transposing
+// V read, over distinct banks.  Every LDS address is a per-lane base plus a compile-time offset.
+template <int D>
+__device__ __forceinline__ constexpr int toff(int r, int e) {
+  return r * (D + 8) + e;
 }
 
+__device__ __forceinline__ void load_lds16(const uint16_t* g, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const int32_t* g, int32_t* lds) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* lds_ptr) {
+  // Whole-vector cast only: extracting single elements of this builtin's result is lowered to
+  // a broadcast of element 0 by this compiler.
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) i16x4*)(lds_ptr)));
+}
+
+// The key blocks one query block visits, in order; uniform across the workgroup.
+struct BlockIter {
+  int n, n_total, n_off, seg_first, i, last_row, mode;
+  const int32_t* list;
+  const int32_t* minpos;
+  __device__ __forceinline__ bool next(int& j, bool& masked) {
+    while (n < n_total) {
+      const int m = n++;
+      if (mode == 0) {
+        j = m;
+        masked = (j == i);
+        return true;
+      }
+      if (m < n_off) {
+        j = min(max(list[m], 0), seg_first - 1);
+        masked = false;
+        return true;
+      }
+      j = seg_first + (m - n_off);
+      if (mode == 2) {
+        if (j > i) {  // identity order: blocks past the diagonal hold only future keys
+          n = n_total;
+          return false;
+        }
+        masked = (j == i);
+        return true;
+      }
+      if (minpos && minpos[j] > last_row) continue;  // no key of this block is visible
+      masked = true;
+      return true;
+    }
+    return false;
+  }
+};
+
 template <int D, int BS>
-__global__ __launch_bounds__(BS / 32 * 64) void attn_fwd_kernel(AttnArgs a) {
-  using C = AttnCfg<D, BS>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BS * C::STR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BS * C::STR];
-  __shared__ int32_t Pos[BS];
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, size_t kv_head, int j, bool masked,
+                                           uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
+                                           int lane) {
+  using C = Cfg<D, BS>;
+  const uint16_t* kb = a.k + (kv_head + static_cast<size_t>(j) * BS) * D;
+  const uint16_t* vb = a.v + (kv_head + static_cast<size_t>(j) * BS) * D;
+#pragma unroll
+  for (int n = w; n < C::NLD; n += C::NW) {
+    // lane -> 16-byte chunk P of the padded tile; the spare chunk of a row re-reads chunk 0
+    const int P = n * 64 + lane;
+    const int r = P / (C::CPR + 1), pc = P - r * (C::CPR + 1);
+    const int off = r * D + (pc < C::CPR ? pc : 0) * 8;
+    load_lds16(kb + off, Kst + n * 512);
+    load_lds16(vb + off, Vst + n * 512);
+  }
+  if (masked && a.mode == 1 && w < BS / 64)
+    load_lds4(a.perm + kv_head + static_cast<size_t>(j) * BS + w * 64 + lane, Pst + w * 64);
+}
+
+// One key block for one wave: 32-key steps of S^T = K Q^T, masking, online softmax and
+// O^T += V^T P^T.  Ks / Vs / Ps are the block's LDS stage.
+template <int D, int BS, int MODE, bool MASKED>
+__device__ __forceinline__ void attn_block(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vs,
+                                           const int32_t* Ps, int j, int lane, int kh, int row0,
+                                           const bf16x8 (&qf)[Cfg<D, BS>::NRF][Cfg<D, BS>::NKS],
+                                           f32x16 (&oacc)[Cfg<D, BS>::NRF][Cfg<D, BS>::NMT],
+                                           float (&mref)[Cfg<D, BS>::NRF],
+                                           float (&lsum)[Cfg<D, BS>::NRF]) {
+  using C = Cfg<D, BS>;
+  constexpr bool masked = MASKED;
+  const int hl = lane >> 5;
+  const int c32 = lane & 31;
+    const int gp = lane >> 4, li = lane & 15;
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt) {
+    // ---- S^T for 32 keys x this wave's rows
+    f32x16 s[C::NRF];
+#pragma unroll
+    for (int f = 0; f < C::NRF; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[f][r] = 0.f;
+    const int kr = kh * C::KW + kt * 32 + c32;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[toff<D>(kr, ks * 16 + hl * 8)]);
+#pragma unroll
+      for (int f = 0; f < C::NRF; ++f)
+        s[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[f][ks], s[f], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- mask, online softmax.  Lane value r is key kh*KW + kt*32 + (r/4)*8 + hl*4 + r%4.
+    bf16x8 pb[C::NRF][2];
+#pragma unroll
+    for (int f = 0; f < C::NRF; ++f) {
+      const int t = row0 + f * 32 + c32;
+      if constexpr (masked) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const int key = kh * C::KW + kt * 32 + rb * 8 + hl * 4;
+          int4 pos;
+          if constexpr (MODE == 1) {
+            pos = *reinterpret_cast<const int4*>(&Ps[key]);
+          } else {
+            pos = make_int4(j * BS + key, j * BS + key + 1, j * BS + key + 2, j * BS + key + 3);
+          }
+          if (pos.x > t) s[f][rb * 4 + 0] = -INFINITY;
+          if (pos.y > t) s[f][rb * 4 + 1] = -INFINITY;
+          if (pos.z > t) s[f][rb * 4 + 2] = -INFINITY;
+          if (pos.w > t) s[f][rb * 4 + 3] = -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[f][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c;
+      // move the reference only when the max grows by more than 2^8 (a wave-uniform branch,
+      // rarely taken once the first blocks have been seen)
+      const bool grow = mx > mref[f] + 8.f;
+      const float alpha = grow ? fast_exp2(mref[f] - mx) : 1.f;
+      mref[f] = grow ? mx : mref[f];
+      if (__any(grow)) {
+        lsum[f] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < C::NMT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[f][mt][r] *= alpha;
+      }
+      const float nm = (mref[f] == -INFINITY) ? 0.f : -mref[f];
+      float rs = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(fmaf(s[f][8 * s2 + e], a.c, nm));
+          rs += p;
+          pb[f][s2][e] = static_cast<__bf16>(p);   // v_cvt_pk_bf16_f32, round to nearest even
+        }
+      }
+      lsum[f] += rs;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T P^T over these 32 keys
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int key0 = kh * C::KW + kt * 32 + 16 * s2 + 4 * (gp >> 1) + (li >> 2);
+#pragma unroll
+      for (int mt = 0; mt < C::NMT; ++mt) {
+        const int dv = mt * 32 + (gp & 1) * 16 + 4 * (li & 3);
+        const u32x2 lo = ds_read_tr(&Vs[toff<D>(key0, dv)]);
+        const u32x2 hi = ds_read_tr(&Vs[toff<D>(key0 + 8, dv)]);
+        const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
+        const bf16x8 va = __builtin_bit_cast(bf16x8, w4);
+#pragma unroll
+        for (int f = 0; f < C::NRF; ++f)
+          oacc[f][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[f][s2], oacc[f][mt], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int D, int BS, int MODE>
+__global__ __launch_bounds__(BS * 4) void attn_fwd_kernel(AttnArgs a) {
+  using C = Cfg<D, BS>;
+  // One LDS array laid out [K stage 0][K stage 1][V stage 0][V stage 1] so that the distance
+  // between the two stages of a tile fits the 16-bit offset field of the DS instructions.
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * C::TILE];
+  __shared__ __attribute__((aligned(16))) int32_t Ps0[BS];
+  __shared__ __attribute__((aligned(16))) int32_t Ps1[BS];
+  uint16_t* const Ks0 = smem + a.tile_off[0];
+  uint16_t* const Ks1 = smem + a.tile_off[1];
+  uint16_t* const Vs0 = smem + a.tile_off[2];
+  uint16_t* const Vs1 = smem + a.tile_off[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int hl = lane >> 5;      // which half of the wave
-  const int c32 = lane & 31;     // query row inside the wave
-  const int i = gridDim.x - 1 - blockIdx.x;  // later query blocks carry more work: start them first
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  const int hl = lane >> 5;
+  const int c32 = lane & 31;
+  const int rg = w % C::RG;  // 32-row group of the query block
+  const int kh = w / C::RG;  // key half of every key block
+
+  // work item -> (b, g, i): heaviest query blocks first, one KV head per XCD run
+  int b, g, i;
+  {
+    const int total = gridDim.x;
+    const int L = blockIdx.x;
+    const int item = a.xcd_map ? (L & 7) * (total >> 3) + (L >> 3) : L;
+    const int per_head = a.G * a.nb;
+    const int hb = item / per_head;            // b * Hkv + h
+    const int rem = item - hb * per_head;
+    i = a.nb - 1 - rem / a.G;
+    b = hb / a.Hkv;
+    g = (hb - b * a.Hkv) * a.G + rem % a.G;
+  }
   const int h = g / a.G;
   const size_t q_head = (static_cast<size_t>(b) * a.Hq + g) * a.N;
   const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;
-  const int t = i * BS + w * 32 + c32;
+  const int row0 = i * BS + rg * C::RW;        // first query row of this wave
 
-  bf16x8 qf[C::NKS];
-  {
-    const uint16_t* qrow = a.q + (q_head + t) * D + hl * 8;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
-  }
-  f32x16 oacc[C::NMT];
-#pragma unroll
-  for (int mt = 0; mt < C::NMT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
-  float m_i = -INFINITY;
-  float l_i = 0.f;
-
-  const int seg = i / a.bps;
-  const int seg_first = seg * a.bps;
-  int n_off = 0;
-  const int32_t* list = nullptr;
-  if (a.mode != 0) {
+  BlockIter it;
+  it.n = 0;
+  it.i = i;
+  it.mode = MODE;
+  it.seg_first = (i / a.bps) * a.bps;
+  it.last_row = i * BS + BS - 1;
+  it.minpos = a.minpos ? a.minpos + kv_head / BS : nullptr;
+  it.n_off = 0;
+  it.list = nullptr;
+  if (MODE != 0) {
     const size_t row = (static_cast<size_t>(b) * a.Hq + g) * a.nb + i;
-    n_off = min(max(a.counts[row], 0), seg_first);
-    list = a.idx + row * a.max_off;
+    it.n_off = min(max(a.counts[row], 0), it.seg_first);
+    it.list = a.idx + row * a.max_off;
   }
-  const int n_total = (a.mode == 0) ? (i + 1) : (n_off + a.bps);
-  const int last_row = i * BS + BS - 1;
-  const int32_t* minpos = a.minpos ? a.minpos + kv_head / BS : nullptr;
+  it.n_total = (MODE == 0) ? (i + 1) : (it.n_off + a.bps);
 
-  for (int n = 0; n < n_total; ++n) {
-    int j;
-    bool masked;
-    if (a.mode == 0) {
-      j = n;
-      masked = (j == i);
-    } else if (n < n_off) {
-      j = min(max(list[n], 0), seg_first - 1);
-      masked = false;
-    } else {
-      j = seg_first + (n - n_off);
-      if (a.mode == 2) {
-        if (j > i) break;  // identity order: blocks past the diagonal hold only future keys
-        masked = (j == i);
-      } else {
-        if (minpos && minpos[j] > last_row) continue;  // no key of this block is visible
-        masked = true;
-      }
-    }
-
-    __syncthreads();  // the previous tile is no longer read
-    {
-      const uint16_t* kb = a.k + (kv_head + static_cast<size_t>(j) * BS) * D;
-      const uint16_t* vb = a.v + (kv_head + static_cast<size_t>(j) * BS) * D;
-      constexpr int CH = D / 8;
+  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][ks*16 + hl*8 .. +8]
+  bf16x8 qf[C::NRF][C::NKS];
 #pragma unroll
-      for (int c = tid; c < BS * CH; c += C::NT) {
-        const int r = c / CH, col = (c % CH) * 8;
-        *reinterpret_cast<u32x4*>(&Ks[r * C::STR + col]) =
-            *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(r) * D + col);
-        *reinterpret_cast<u32x4*>(&Vs[r * C::STR + col]) =
-            *reinterpret_cast<const u32x4*>(vb + static_cast<size_t>(r) * D + col);
-      }
-      if (masked) {
-        for (int r = tid; r < BS; r += C::NT)
-          Pos[r] = (a.mode == 1) ? a.perm[kv_head + static_cast<size_t>(j) * BS + r] : j * BS + r;
-      }
-    }
-    __syncthreads();
-
-    // S^T (keys x query rows) for the whole key block.
-    f32x16 s[C::NKT];
+  for (int f = 0; f < C::NRF; ++f) {
+    const uint16_t* qrow = a.q + (q_head + row0 + f * 32 + c32) * D + hl * 8;
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
+    for (int ks = 0; ks < C::NKS; ++ks) qf[f][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+  }
+  f32x16 oacc[C::NRF][C::NMT];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-      const uint16_t* krow = &Ks[(kt * 32 + c32) * C::STR + hl * 8];
-#pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + ks * 16);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
-      }
-    }
-
-    // Online softmax: lane value r of sub-tile kt is key kt*32 + (r/4)*8 + hl*4 + r%4.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float z = s[kt][r] * a.c;
-        if (masked) {
-          const int key = kt * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          if (Pos[key] > t) z = -INFINITY;
-        }
-        s[kt][r] = z;
-        mx = fmaxf(mx, z);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_i, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_i - m_use);
-    float rs = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[kt][r] - m_use);
-        s[kt][r] = p;
-        rs += p;
-      }
-    }
-    rs += __shfl_xor(rs, 32);
-    l_i = l_i * alpha + rs;
-    m_i = m_new;
+  for (int f = 0; f < C::NRF; ++f)
 #pragma unroll
     for (int mt = 0; mt < C::NMT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[mt][r] *= alpha;
+      for (int r = 0; r < 16; ++r) oacc[f][mt][r] = 0.f;
+  float mref[C::NRF], lsum[C::NRF];
+#pragma unroll
+  for (int f = 0; f < C::NRF; ++f) {
+    mref[f] = -INFINITY;   // running reference max, log2 units
+    lsum[f] = 0.f;         // this lane's half of the row sum
+  }
 
-    // O^T += V^T P^T, 16 keys per MFMA.
-    const int gp = lane >> 4, li = lane & 15;
+  int j_cur = 0, j_next = 0;
+  bool m_cur = false, m_next = false;
+  bool have = it.next(j_cur, m_cur);
+  if (have) issue_tile<D, BS>(a, kv_head, j_cur, m_cur, Ks0, Vs0, Ps0, w, lane);
+
+  // Two stages, unrolled so that each stage's LDS offsets are compile-time constants.
+  while (have) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // stage 0 landed; stage 1 no longer read
+    const bool more = it.next(j_next, m_next);
+    if (more) issue_tile<D, BS>(a, kv_head, j_next, m_next, Ks1, Vs1, Ps1, w, lane);
+    if (m_cur)
+      attn_block<D, BS, MODE, true>(a, Ks0, Vs0, Ps0, j_cur, lane, kh, row0, qf, oacc, mref, lsum);
+    else
+      attn_block<D, BS, MODE, false>(a, Ks0, Vs0, Ps0, j_cur, lane, kh, row0, qf, oacc, mref, lsum);
+    if (!more) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // stage 1 landed; stage 0 no longer read
+    have = it.next(j_cur, m_cur);
+    if (have) issue_tile<D, BS>(a, kv_head, j_cur, m_cur, Ks0, Vs0, Ps0, w, lane);
+    if (m_next)
+      attn_block<D, BS, MODE, true>(a, Ks1, Vs1, Ps1, j_next, lane, kh, row0, qf, oacc, mref, lsum);
+    else
+      attn_block<D, BS, MODE, false>(a, Ks1, Vs1, Ps1, j_next, lane, kh, row0, qf, oacc, mref, lsum);
+  }
+
+  // ---- merge the two key halves (kh = 1 hands its state to kh = 0) through LDS
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(smem);                // [rg][f][mt][r][lane] partial O
+  float* xm = reinterpret_cast<float*>(smem + 3 * C::TILE);  // [rg][f][2][lane] max and row sum
+  static_assert(2 * C::NRF * C::NMT * 16 * 64 * 4 <= 3 * C::TILE * 2,
+                "merge buffer must fit in the K/V stages");
+  if (kh == 1) {
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
+    for (int f = 0; f < C::NRF; ++f) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 pb;
+      for (int mt = 0; mt < C::NMT; ++mt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[kt][8 * s2 + e]);
-        const int key0 = kt * 32 + 16 * s2 + 4 * (gp >> 1) + (li >> 2);
+        for (int r = 0; r < 16; ++r)
+          xo[(((rg * C::NRF + f) * C::NMT + mt) * 16 + r) * 64 + lane] = oacc[f][mt][r];
+      xm[((rg * C::NRF + f) * 2 + 0) * 64 + lane] = mref[f];
+      xm[((rg * C::NRF + f) * 2 + 1) * 64 + lane] = lsum[f];
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
 #pragma unroll
-        for (int mt = 0; mt < C::NMT; ++mt) {
-          const int dv = mt * 32 + (gp & 1) * 16 + 4 * (li & 3);
-          // Whole-vector casts only: extracting single elements of the transposing load's
-          // result is lowered to a broadcast of element 0 by this compiler.
-          const u32x2 lo = __builtin_bit_cast(u32x2, ds_read_tr(&Vs[key0 * C::STR + dv]));
-          const u32x2 hi = __builtin_bit_cast(u32x2, ds_read_tr(&Vs[(key0 + 8) * C::STR + dv]));
-          const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
-          const bf16x8 va = __builtin_bit_cast(bf16x8, w4);
-          oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[mt], 0, 0, 0);
+  for (int f = 0; f < C::NRF; ++f) {
+    const float mb = xm[((rg * C::NRF + f) * 2 + 0) * 64 + lane];
+    const float lb = xm[((rg * C::NRF + f) * 2 + 1) * 64 + lane];
+    const float m = fmaxf(mref[f], mb);
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    const float sa = fast_exp2(mref[f] - mu), sb = fast_exp2(mb - mu);
+    float la = lsum[f] * sa + lb * sb;
+    la += __shfl_xor(la, 32);                  // the two halves of the row
+    const float inv_l = (la > 0.f) ? 1.f / la : 0.f;
+    const int t = row0 + f * 32 + c32;
+    uint16_t* orow = a.o + (q_head + t) * D;
+#pragma unroll
+    for (int mt = 0; mt < C::NMT; ++mt) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        float v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rb * 4 + e;
+          const float ob = xo[(((rg * C::NRF + f) * C::NMT + mt) * 16 + r) * 64 + lane];
+          v4[e] = (oacc[f][mt][r] * sa + ob * sb) * inv_l;
         }
+        bf16x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = static_cast<__bf16>(v4[e]);
+        // O^T lane value r of tile mt is head-dim index mt*32 + (r/4)*8 + hl*4 + r%4 of row t
+        *reinterpret_cast<bf16x4*>(orow + mt * 32 + rb * 8 + hl * 4) = pk;
       }
     }
+    if (a.lse && hl == 0) a.lse[q_head + t] = (m + __log2f(la)) * kLn2;
   }
-
-  // O^T lane value r of tile mt is head-dim index mt*32 + (r/4)*8 + hl*4 + r%4 of row t.
-  const float inv_l = (l_i > 0.f) ? 1.f / l_i : 0.f;
-  uint16_t* orow = a.o + (q_head + t) * D;
-#pragma unroll
-  for (int mt = 0; mt < C::NMT; ++mt) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      u32x2 pk;
-      pk[0] = pack_bf16x2(oacc[mt][rb * 4 + 0] * inv_l, oacc[mt][rb * 4 + 1] * inv_l);
-      pk[1] = pack_bf16x2(oacc[mt][rb * 4 + 2] * inv_l, oacc[mt][rb * 4 + 3] * inv_l);
-      *reinterpret_cast<u32x2*>(orow + mt * 32 + rb * 8 + hl * 4) = pk;
-    }
-  }
-  if (a.lse && hl == 0) a.lse[q_head + t] = (m_i + __log2f(l_i)) * kLn2;
 }
 
 template <int D, int BS>
 hipError_t launch_attn_t(const Dims& d, const AttnArgs& a, hipStream_t stream) {
-  dim3 grid(d.nb, d.Hq, d.B);
-  return launch(attn_fwd_kernel<D, BS>, grid, dim3(AttnCfg<D, BS>::NT), 0, stream, a);
+  const int total = d.B * d.Hq * d.nb;
+  if (a.mode == 1) return launch(attn_fwd_kernel<D, BS, 1>, dim3(total), dim3(Cfg<D, BS>::NT), 0, stream, a);
+  if (a.mode == 2) return launch(attn_fwd_kernel<D, BS, 2>, dim3(total), dim3(Cfg<D, BS>::NT), 0, stream, a);
+  return launch(attn_fwd_kernel<D, BS, 0>, dim3(total), dim3(Cfg<D, BS>::NT), 0, stream, a);
 }
 
 }  // namespace
@@ -249,10 +427,14 @@ hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, cons
   a.q = q; a.k = k; a.v = v;
   a.perm = perm; a.minpos = blk_minpos; a.counts = counts; a.idx = idx;
   a.o = o; a.lse = lse;
-  a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.N = d.N; a.nb = d.nb; a.bps = d.bps;
+  a.B = d.B; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.N = d.N; a.nb = d.nb; a.bps = d.bps;
   a.max_off = d.max_off > 0 ? d.max_off : 1;
   a.mode = mode;
+  const long long total = static_cast<long long>(d.B) * d.Hq * d.nb;
+  a.xcd_map = (total % 8 == 0) ? 1 : 0;
   a.c = scale * kLog2e;
+  const int tile = d.Bs * (d.d + 8);
+  for (int t = 0; t < 4; ++t) a.tile_off[t] = t * tile;
   if (d.d == 128 && d.Bs == 128) return launch_attn_t<128, 128>(d, a, stream);
   if (d.d == 128 && d.Bs == 64) return launch_attn_t<128, 64>(d, a, stream);
   if (d.d == 64 && d.Bs == 128) return launch_attn_t<64, 128>(d, a, stream);

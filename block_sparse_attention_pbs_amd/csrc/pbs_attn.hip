@@ -21,9 +21,9 @@
 //    shared by both operands); V^T comes from the row-major V tile through the transposing LDS
 //    load ds_read_b64_tr_b16;
 //  * K/V tiles are double-buffered in LDS and filled by asynchronous direct global->LDS loads
-//    (global_load_lds_dwordx4) one block ahead of the compute; rows are padded by one 16-byte
-//    chunk, which spreads both the K reads (one chunk of 32 rows) and the transposing V reads
-//    (4 rows x 32 bytes) over the banks and keeps every LDS address a base plus an immediate;
+//    (buffer_load_dwordx4 ... lds, bounds-checked) one block ahead of the compute; K and V rows are padded (by 16
+//    and 64 bytes) so that the K fragment reads and the transposing V reads are free of bank
+//    conflicts, and every LDS address is a base plus an immediate;
 //  * exp2 with scale*log2(e) folded into one FMA per element; the running max is only moved (and
 //    the accumulator rescaled) when it grows by more than 2^8, which keeps every exponent <= 8;
 //  * work order: heaviest query blocks first, and consecutive workgroups of one XCD (the
@@ -67,26 +67,44 @@ struct Cfg {
   static constexpr int NKS = D / 16;       // 16-wide k-steps over the head dim
   static constexpr int NMT = D / 32;       // 32-row tiles of O^T over the head dim
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
-  static constexpr int STR = D + 8;        // LDS row stride (bf16 elements)
-  static constexpr int TILE = BS * STR;    // bf16 elements of one K (or V) tile in LDS
-  static constexpr int NLD = BS * (CPR + 1) / 64;  // 1 KiB direct loads per tile
+  static constexpr int KPAD = 1;           // spare 16-byte chunks per K row
+  static constexpr int VPAD = 4;           // spare 16-byte chunks per V row
+  static constexpr int KTILE = BS * (D + 8 * KPAD);   // bf16 elements of a K tile in LDS
+  static constexpr int VTILE = BS * (D + 8 * VPAD);   // bf16 elements of a V tile in LDS
+  static constexpr int NLDK = BS * (CPR + KPAD) / 64; // 1 KiB direct loads per K tile
+  static constexpr int NLDV = BS * (CPR + VPAD) / 64; // 1 KiB direct loads per V tile
 };
 
-// LDS tile layout: each row of D bf16 is followed by one spare 16-byte chunk (row stride D + 8
-// elements), which spreads the 32 rows of a K fragment read, and the 4 rows of a transposing
-// V read, over distinct banks.  Every LDS address is a per-lane base plus a compile-time offset.
+// LDS tile layouts.  K rows are padded by one 16-byte chunk (row stride = 16 B mod 256 B), so
+// the 16 lanes of a K fragment read (16 rows, one chunk each) hit 16 distinct bank groups.  V
+// rows are padded by four chunks (row stride = 64 B mod 256 B), so the 4 rows x 64 B that 32
+// lanes of a transposing V read touch fill the 64 banks exactly once.  Every LDS address is a
+// per-lane base plus a compile-time offset.
 template <int D>
-__device__ __forceinline__ constexpr int toff(int r, int e) {
+__device__ __forceinline__ constexpr int koff(int r, int e) {
   return r * (D + 8) + e;
 }
-
-__device__ __forceinline__ void load_lds16(const uint16_t* g, uint16_t* lds) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)lds, 16, 0, 0);
+template <int D>
+__device__ __forceinline__ constexpr int voff(int r, int e) {
+  return r * (D + 32) + e;
 }
-__device__ __forceinline__ void load_lds4(const int32_t* g, int32_t* lds) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)lds, 4, 0, 0);
+
+// Buffer resource over `bytes` bytes from `base` (gfx9 descriptor word 3).  Loads through it are
+// bounds-checked by the hardware and take a 32-bit per-lane offset plus a scalar offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+// Direct buffer->LDS loads: lane l's 16 (or 4) bytes land at lds + l*16 (l*4).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                           uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                          uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* lds_ptr) {
@@ -110,7 +128,8 @@ struct BlockIter {
         return true;
       }
       if (m < n_off) {
-        j = min(max(list[m], 0), seg_first - 1);
+        // the list entry is the same for the whole workgroup: keep it scalar
+        j = __builtin_amdgcn_readfirstlane(min(max(list[m], 0), seg_first - 1));
         masked = false;
         return true;
       }
@@ -123,7 +142,8 @@ struct BlockIter {
         masked = (j == i);
         return true;
       }
-      if (minpos && minpos[j] > last_row) continue;  // no key of this block is visible
+      if (minpos && __builtin_amdgcn_readfirstlane(minpos[j]) > last_row)
+        continue;  // no key of this block is visible
       masked = true;
       return true;
     }
@@ -131,37 +151,45 @@ struct BlockIter {
   }
 };
 
+// Start the asynchronous loads of key block j (K, V and, for masked permuted blocks, the
+// original positions) into one LDS stage.  K/V rows are padded in LDS; a spare chunk re-reads
+// chunk 0 of its row.
 template <int D, int BS>
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, size_t kv_head, int j, bool masked,
-                                           uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
-                                           int lane) {
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, __amdgpu_buffer_rsrc_t rk,
+                                           __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rp,
+                                           int j, bool masked, uint16_t* Kst, uint16_t* Vst,
+                                           int32_t* Pst, int w, int lane) {
   using C = Cfg<D, BS>;
-  const uint16_t* kb = a.k + (kv_head + static_cast<size_t>(j) * BS) * D;
-  const uint16_t* vb = a.v + (kv_head + static_cast<size_t>(j) * BS) * D;
+  const uint32_t tile = static_cast<uint32_t>(j) * BS * D * 2;
 #pragma unroll
-  for (int n = w; n < C::NLD; n += C::NW) {
-    // lane -> 16-byte chunk P of the padded tile; the spare chunk of a row re-reads chunk 0
+  for (int n = w; n < C::NLDK; n += C::NW) {
     const int P = n * 64 + lane;
-    const int r = P / (C::CPR + 1), pc = P - r * (C::CPR + 1);
-    const int off = r * D + (pc < C::CPR ? pc : 0) * 8;
-    load_lds16(kb + off, Kst + n * 512);
-    load_lds16(vb + off, Vst + n * 512);
+    const int r = P / (C::CPR + C::KPAD), pc = P - r * (C::CPR + C::KPAD);
+    load_lds16(rk, Kst + n * 512, static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2), tile);
+  }
+#pragma unroll
+  for (int n = w; n < C::NLDV; n += C::NW) {
+    const int P = n * 64 + lane;
+    const int r = P / (C::CPR + C::VPAD), pc = P - r * (C::CPR + C::VPAD);
+    load_lds16(rv, Vst + n * 512, static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2), tile);
   }
   if (masked && a.mode == 1 && w < BS / 64)
-    load_lds4(a.perm + kv_head + static_cast<size_t>(j) * BS + w * 64 + lane, Pst + w * 64);
+    load_lds4(rp, Pst + w * 64, static_cast<uint32_t>((w * 64 + lane) * 4),
+                static_cast<uint32_t>(j) * BS * 4);
 }
 
 // One key block for one wave: 32-key steps of S^T = K Q^T, masking, online softmax and
 // O^T += V^T P^T.  Ks / Vs / Ps are the block's LDS stage.
-template <int D, int BS, int MODE, bool MASKED>
+template <int D, int BS, int MODE>
 __device__ __forceinline__ void attn_block(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vs,
-                                           const int32_t* Ps, int j, int lane, int kh, int row0,
+                                           const int32_t* Ps, int j, bool masked, int lane, int kh,
+                                           int row0,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NRF][Cfg<D, BS>::NKS],
                                            f32x16 (&oacc)[Cfg<D, BS>::NRF][Cfg<D, BS>::NMT],
                                            float (&mref)[Cfg<D, BS>::NRF],
-                                           float (&lsum)[Cfg<D, BS>::NRF]) {
+                                           float (&lsum)[Cfg<D, BS>::NRF],
+                                           float (&mseen)[Cfg<D, BS>::NRF], bool& bad) {
   using C = Cfg<D, BS>;
-  constexpr bool masked = MASKED;
   const int hl = lane >> 5;
   const int c32 = lane & 31;
     const int gp = lane >> 4, li = lane & 15;
@@ -169,17 +197,14 @@ __device__ __forceinline__ void attn_block(const AttnArgs& a, const uint16_t* Ks
   for (int kt = 0; kt < C::NKT; ++kt) {
     // ---- S^T for 32 keys x this wave's rows
     f32x16 s[C::NRF];
-#pragma unroll
-    for (int f = 0; f < C::NRF; ++f)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[f][r] = 0.f;
     const int kr = kh * C::KW + kt * 32 + c32;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[toff<D>(kr, ks * 16 + hl * 8)]);
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kr, ks * 16 + hl * 8)]);
 #pragma unroll
       for (int f = 0; f < C::NRF; ++f)
-        s[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[f][ks], s[f], 0, 0, 0);
+        s[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[f][ks], ks == 0 ? f32x16{} : s[f],
+                                                        0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- mask, online softmax.  Lane value r is key kh*KW + kt*32 + (r/4)*8 + hl*4 + r%4.
@@ -187,7 +212,8 @@ __device__ __forceinline__ void attn_block(const AttnArgs& a, const uint16_t* Ks
 #pragma unroll
     for (int f = 0; f < C::NRF; ++f) {
       const int t = row0 + f * 32 + c32;
-      if constexpr (masked) {
+      // (one uniform branch that only touches the score registers)
+      if (masked) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
           const int key = kh * C::KW + kt * 32 + rb * 8 + hl * 4;
@@ -207,18 +233,12 @@ __device__ __forceinline__ void attn_block(const AttnArgs& a, const uint16_t* Ks
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[f][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c;
-      // move the reference only when the max grows by more than 2^8 (a wave-uniform branch,
-      // rarely taken once the first blocks have been seen)
-      const bool grow = mx > mref[f] + 8.f;
-      const float alpha = grow ? fast_exp2(mref[f] - mx) : 1.f;
-      mref[f] = grow ? mx : mref[f];
-      if (__any(grow)) {
-        lsum[f] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < C::NMT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[f][mt][r] *= alpha;
-      }
+      // Fixed reference: the first finite block max of the row (the accumulators are still
+      // zero when it is set, so nothing is rescaled).  A later max more than 2^64 above it is
+      // only recorded; the workgroup then recomputes with the exact row max (see the kernel).
+      mseen[f] = fmaxf(mseen[f], mx);
+      mref[f] = (mref[f] == -INFINITY) ? mx : mref[f];
+      bad |= mx > mref[f] + 64.f;
       const float nm = (mref[f] == -INFINITY) ? 0.f : -mref[f];
       float rs = 0.f;
 #pragma unroll
@@ -240,8 +260,8 @@ __device__ __forceinline__ void attn_block(const AttnArgs& a, const uint16_t* Ks
 #pragma unroll
       for (int mt = 0; mt < C::NMT; ++mt) {
         const int dv = mt * 32 + (gp & 1) * 16 + 4 * (li & 3);
-        const u32x2 lo = ds_read_tr(&Vs[toff<D>(key0, dv)]);
-        const u32x2 hi = ds_read_tr(&Vs[toff<D>(key0 + 8, dv)]);
+        const u32x2 lo = ds_read_tr(&Vs[voff<D>(key0, dv)]);
+        const u32x2 hi = ds_read_tr(&Vs[voff<D>(key0 + 8, dv)]);
         const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
         const bf16x8 va = __builtin_bit_cast(bf16x8, w4);
 #pragma unroll
@@ -255,9 +275,8 @@ __device__ __forceinline__ void attn_block(const AttnArgs& a, const uint16_t* Ks
 template <int D, int BS, int MODE>
 __global__ __launch_bounds__(BS * 4) void attn_fwd_kernel(AttnArgs a) {
   using C = Cfg<D, BS>;
-  // One LDS array laid out [K stage 0][K stage 1][V stage 0][V stage 1] so that the distance
-  // between the two stages of a tile fits the 16-bit offset field of the DS instructions.
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * C::TILE];
+  // One LDS array laid out [K stage 0][K stage 1][V stage 0][V stage 1].
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::KTILE + 2 * C::VTILE];
   __shared__ __attribute__((aligned(16))) int32_t Ps0[BS];
   __shared__ __attribute__((aligned(16))) int32_t Ps1[BS];
   uint16_t* const Ks0 = smem + a.tile_off[0];
@@ -267,7 +286,8 @@ __global__ __launch_bounds__(BS * 4) void attn_fwd_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  // wave index as a scalar: keeps LDS destinations and row/key offsets wave-uniform
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;
   const int c32 = lane & 31;
   const int rg = w % C::RG;  // 32-row group of the query block
@@ -290,6 +310,11 @@ __global__ __launch_bounds__(BS * 4) void attn_fwd_kernel(AttnArgs a) {
   const size_t q_head = (static_cast<size_t>(b) * a.Hq + g) * a.N;
   const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;
   const int row0 = i * BS + rg * C::RW;        // first query row of this wave
+  const uint32_t head_bytes = static_cast<uint32_t>(a.N) * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t rp =
+      make_rsrc(a.perm ? a.perm + kv_head : nullptr, a.perm ? static_cast<uint32_t>(a.N) * 4 : 0u);
 
   BlockIter it;
   it.n = 0;
@@ -316,50 +341,52 @@ __global__ __launch_bounds__(BS * 4) void attn_fwd_kernel(AttnArgs a) {
     for (int ks = 0; ks < C::NKS; ++ks) qf[f][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
   }
   f32x16 oacc[C::NRF][C::NMT];
+  float mref[C::NRF], lsum[C::NRF], mseen[C::NRF];
 #pragma unroll
-  for (int f = 0; f < C::NRF; ++f)
-#pragma unroll
-    for (int mt = 0; mt < C::NMT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[f][mt][r] = 0.f;
-  float mref[C::NRF], lsum[C::NRF];
-#pragma unroll
-  for (int f = 0; f < C::NRF; ++f) {
-    mref[f] = -INFINITY;   // running reference max, log2 units
-    lsum[f] = 0.f;         // this lane's half of the row sum
-  }
+  for (int f = 0; f < C::NRF; ++f) mseen[f] = -INFINITY;   // largest row max seen, log2 units
 
-  int j_cur = 0, j_next = 0;
-  bool m_cur = false, m_next = false;
-  bool have = it.next(j_cur, m_cur);
-  if (have) issue_tile<D, BS>(a, kv_head, j_cur, m_cur, Ks0, Vs0, Ps0, w, lane);
-
-  // Two stages, unrolled so that each stage's LDS offsets are compile-time constants.
-  while (have) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // stage 0 landed; stage 1 no longer read
-    const bool more = it.next(j_next, m_next);
-    if (more) issue_tile<D, BS>(a, kv_head, j_next, m_next, Ks1, Vs1, Ps1, w, lane);
-    if (m_cur)
-      attn_block<D, BS, MODE, true>(a, Ks0, Vs0, Ps0, j_cur, lane, kh, row0, qf, oacc, mref, lsum);
-    else
-      attn_block<D, BS, MODE, false>(a, Ks0, Vs0, Ps0, j_cur, lane, kh, row0, qf, oacc, mref, lsum);
-    if (!more) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // stage 1 landed; stage 0 no longer read
-    have = it.next(j_cur, m_cur);
-    if (have) issue_tile<D, BS>(a, kv_head, j_cur, m_cur, Ks0, Vs0, Ps0, w, lane);
-    if (m_next)
-      attn_block<D, BS, MODE, true>(a, Ks1, Vs1, Ps1, j_next, lane, kh, row0, qf, oacc, mref, lsum);
-    else
-      attn_block<D, BS, MODE, false>(a, Ks1, Vs1, Ps1, j_next, lane, kh, row0, qf, oacc, mref, lsum);
+  // Pass 0 runs with the first-block reference; pass 1 (rare) reruns with the exact row max.
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int f = 0; f < C::NRF; ++f) {
+#pragma unroll
+      for (int mt = 0; mt < C::NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[f][mt][r] = 0.f;
+      mref[f] = pass == 0 ? -INFINITY : mseen[f];   // reference max, log2 units
+      lsum[f] = 0.f;                                // this lane's half of the row sum
+    }
+    bool bad = false;
+    it.n = 0;
+    int j_cur = 0, j_next = 0;
+    bool m_cur = false, m_next = false;
+    bool have = it.next(j_cur, m_cur);
+    if (have) issue_tile<D, BS>(a, rk, rv, rp, j_cur, m_cur, Ks0, Vs0, Ps0, w, lane);
+    // Two stages, unrolled so that each stage's LDS offsets are compile-time constants.
+    while (have) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // stage 0 landed; stage 1 no longer read
+      const bool more = it.next(j_next, m_next);
+      if (more) issue_tile<D, BS>(a, rk, rv, rp, j_next, m_next, Ks1, Vs1, Ps1, w, lane);
+      attn_block<D, BS, MODE>(a, Ks0, Vs0, Ps0, j_cur, m_cur, lane, kh, row0, qf, oacc, mref,
+                              lsum, mseen, bad);
+      if (!more) break;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // stage 1 landed; stage 0 no longer read
+      have = it.next(j_cur, m_cur);
+      if (have) issue_tile<D, BS>(a, rk, rv, rp, j_cur, m_cur, Ks0, Vs0, Ps0, w, lane);
+      attn_block<D, BS, MODE>(a, Ks1, Vs1, Ps1, j_next, m_next, lane, kh, row0, qf, oacc, mref,
+                              lsum, mseen, bad);
+    }
+    // Every wave has finished reading the stages before a second pass or the merge reuses them.
+    if (!__syncthreads_or(bad ? 1 : 0)) break;
   }
 
   // ---- merge the two key halves (kh = 1 hands its state to kh = 0) through LDS
   __syncthreads();
   float* xo = reinterpret_cast<float*>(smem);                // [rg][f][mt][r][lane] partial O
-  float* xm = reinterpret_cast<float*>(smem + 3 * C::TILE);  // [rg][f][2][lane] max and row sum
-  static_assert(2 * C::NRF * C::NMT * 16 * 64 * 4 <= 3 * C::TILE * 2,
+  float* xm = reinterpret_cast<float*>(smem + 2 * C::KTILE + C::VTILE);  // [rg][f][2][lane]
+  static_assert(C::RG * C::NRF * C::NMT * 16 * 64 * 4 <= (2 * C::KTILE + C::VTILE) * 2,
                 "merge buffer must fit in the K/V stages");
   if (kh == 1) {
 #pragma unroll
@@ -433,8 +460,11 @@ hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, cons
   const long long total = static_cast<long long>(d.B) * d.Hq * d.nb;
   a.xcd_map = (total % 8 == 0) ? 1 : 0;
   a.c = scale * kLog2e;
-  const int tile = d.Bs * (d.d + 8);
-  for (int t = 0; t < 4; ++t) a.tile_off[t] = t * tile;
+  const int ktile = d.Bs * (d.d + 8), vtile = d.Bs * (d.d + 32);
+  a.tile_off[0] = 0;
+  a.tile_off[1] = ktile;
+  a.tile_off[2] = 2 * ktile;
+  a.tile_off[3] = 2 * ktile + vtile;
   if (d.d == 128 && d.Bs == 128) return launch_attn_t<128, 128>(d, a, stream);
   if (d.d == 128 && d.Bs == 64) return launch_attn_t<128, 64>(d, a, stream);
   if (d.d == 64 && d.Bs == 128) return launch_attn_t<64, 128>(d, a, stream);

@@ -209,8 +209,7 @@ def prefill(q, k, v, *, block: int, segment: int, keep: Optional[float] = None,
 def dense_causal(q, k, v, *, block: int = 128, scale: Optional[float] = None, o=None, lse=None,
                  stream=None):
     """Plain causal attention with the same kernel (dense mode of pbs_attn_fwd)."""
-    N = q.shape[2]
-    shape = shape_of(q, k, block, N)
+    shape = shape_of(q, k, block, block)   # dense mode does not use segments
     if scale is None:
         scale = default_scale(q.shape[-1])
     if o is None:

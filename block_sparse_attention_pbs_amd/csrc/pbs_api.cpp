@@ -1,7 +1,7 @@
 // C-ABI entry points of libpbs: argument validation, workspace carving and kernel launches on
 // the caller's stream.  Every check happens before the first launch; nothing here allocates,
 // frees or synchronises.
-#include "../../include/pbs.h"
+#include "pbs.h"
 #include "pbs_internal.h"
 
 #include <hip/hip_runtime.h>

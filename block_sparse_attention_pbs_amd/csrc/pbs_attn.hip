@@ -8,24 +8,28 @@
 // causal test going through the stored original positions.  Queries are never permuted, so
 // the output is written in original token order.
 //
-// Design (CDNA4, wave64, one workgroup of 2*Bs/32 waves per (query block, query head)):
-//  * wave w owns 32 query rows (row group w % (Bs/32)) and, of every key block, one half of the
-//    keys (w / (Bs/32)): two waves per SIMD, so one wave's softmax (VALU) and LDS reads can run
-//    under the other wave's MFMAs.  The two key halves keep separate online-softmax states and
-//    are merged through LDS at the end;
+// Design (CDNA4, wave64):
+//  * one workgroup of Bs/32 waves per (query block, query head); wave w owns 32 query rows and
+//    sees every key of every visited block, so no cross-wave reduction is needed;
+//  * keys stream through LDS in stages of 64 keys (half a 128-key block), double-buffered and
+//    filled by asynchronous direct buffer->LDS loads (buffer_load_dwordx4 ... lds, bounds-
+//    checked) one stage ahead of the compute.  A workgroup needs ~75 KiB of LDS, so two
+//    workgroups share a CU: while one waits for its next stage the other computes;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 (A = K rows from
-//    LDS, B = the wave's Q rows held in registers), so each lane owns one query row: the softmax
-//    max / sum need one cross-half exchange per block and fragment;
+//    LDS, B = the wave's Q rows held in registers), so each lane owns one query row and the
+//    softmax statistics need one cross-half exchange per 32 keys;
 //  * the output is accumulated transposed, O^T += V^T P^T: P leaves the score accumulators as the
 //    bf16 B operand without touching LDS (the key order inside a 16-key step is a relabelling
 //    shared by both operands); V^T comes from the row-major V tile through the transposing LDS
 //    load ds_read_b64_tr_b16;
-//  * K/V tiles are double-buffered in LDS and filled by asynchronous direct global->LDS loads
-//    (buffer_load_dwordx4 ... lds, bounds-checked) one block ahead of the compute; K and V rows are padded (by 16
-//    and 64 bytes) so that the K fragment reads and the transposing V reads are free of bank
-//    conflicts, and every LDS address is a base plus an immediate;
-//  * exp2 with scale*log2(e) folded into one FMA per element; the running max is only moved (and
-//    the accumulator rescaled) when it grows by more than 2^8, which keeps every exponent <= 8;
+//  * K rows are padded by 16 bytes and V rows by 64 bytes in LDS, which makes both the K fragment
+//    reads (16 rows x 16 B) and the transposing V reads (4 rows x 64 B) free of bank conflicts and
+//    keeps every LDS address a per-lane base plus an immediate;
+//  * exp2 with scale*log2(e) folded into one FMA per element, and a fixed per-row reference max
+//    (the first finite block max of the row): the accumulator is never rescaled inside the loop.
+//    A later max more than 2^64 above the reference only sets a flag, and the workgroup then
+//    recomputes with the exact row max (never seen on realistic inputs, but it keeps every value
+//    in range on any input);
 //  * work order: heaviest query blocks first, and consecutive workgroups of one XCD (the
 //    hardware deals workgroups round-robin over the 8 XCDs) walk one KV head, so the K/V tiles a
 //    head's query blocks share stay in that XCD's L2.
@@ -49,37 +53,35 @@ struct AttnArgs {
   int mode;      // 0 dense causal, 1 permuted PBS, 2 identity-order PBS
   int xcd_map;   // 1: total work items divisible by 8, use the XCD-grouped order
   float c;       // scale * log2(e)
-  // Element offsets of the K/V stage tiles in LDS.  Passed at run time on purpose: the
-  // compiler then keeps one (tile base + lane) address per tile and folds every in-tile offset
-  // (< 64 KiB) into the DS instruction, instead of materialising one register per offset.
+  // Element offsets of the K/V stage tiles in LDS.  Passed at run time on purpose: the compiler
+  // then keeps one (tile base + lane) address per tile and folds every in-tile offset into the
+  // DS instruction, instead of materialising one register per (stage, offset) pair.
   int tile_off[4];
 };
 
+constexpr int kStageKeys = 64;  // keys per LDS stage
+
 template <int D, int BS>
 struct Cfg {
-  static constexpr int RG = BS / 32;       // 32-row groups of a query block
-  static constexpr int NW = 2 * RG;        // waves: every row group x two key halves
+  static constexpr int NW = BS / 32;       // waves: 32 query rows each
   static constexpr int NT = NW * 64;
-  static constexpr int RW = 32;            // query rows per wave
-  static constexpr int KW = BS / 2;        // keys per wave and block
-  static constexpr int NRF = 1;            // 32-row fragments per wave
-  static constexpr int NKT = KW / 32;      // 32-key sub-tiles per wave and block
+  static constexpr int SK = kStageKeys;    // keys per stage
+  static constexpr int HALVES = BS / SK;   // stages per key block
+  static constexpr int NKT = SK / 32;      // 32-key sub-tiles per stage
   static constexpr int NKS = D / 16;       // 16-wide k-steps over the head dim
   static constexpr int NMT = D / 32;       // 32-row tiles of O^T over the head dim
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int KPAD = 1;           // spare 16-byte chunks per K row
   static constexpr int VPAD = 4;           // spare 16-byte chunks per V row
-  static constexpr int KTILE = BS * (D + 8 * KPAD);   // bf16 elements of a K tile in LDS
-  static constexpr int VTILE = BS * (D + 8 * VPAD);   // bf16 elements of a V tile in LDS
-  static constexpr int NLDK = BS * (CPR + KPAD) / 64; // 1 KiB direct loads per K tile
-  static constexpr int NLDV = BS * (CPR + VPAD) / 64; // 1 KiB direct loads per V tile
+  static constexpr int KTILE = SK * (D + 8 * KPAD);   // bf16 elements of a K stage in LDS
+  static constexpr int VTILE = SK * (D + 8 * VPAD);   // bf16 elements of a V stage in LDS
+  static constexpr int NLDK = SK * (CPR + KPAD) / 64; // 1 KiB direct loads per K stage
+  static constexpr int NLDV = SK * (CPR + VPAD) / 64; // 1 KiB direct loads per V stage
 };
 
-// LDS tile layouts.  K rows are padded by one 16-byte chunk (row stride = 16 B mod 256 B), so
-// the 16 lanes of a K fragment read (16 rows, one chunk each) hit 16 distinct bank groups.  V
-// rows are padded by four chunks (row stride = 64 B mod 256 B), so the 4 rows x 64 B that 32
-// lanes of a transposing V read touch fill the 64 banks exactly once.  Every LDS address is a
-// per-lane base plus a compile-time offset.
+// LDS row layouts.  K rows: stride = 16 B mod 256 B, so the 16 lanes of a K fragment read
+// (16 rows, one 16-byte chunk each) hit 16 distinct bank groups.  V rows: stride = 64 B mod
+// 256 B, so the 4 rows x 64 B touched by 32 lanes of a transposing V read cover the 64 banks once.
 template <int D>
 __device__ __forceinline__ constexpr int koff(int r, int e) {
   return r * (D + 8) + e;
@@ -114,12 +116,16 @@ __device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* lds_ptr) {
                                        (__attribute__((address_space(3))) i16x4*)(lds_ptr)));
 }
 
-// The key blocks one query block visits, in order; uniform across the workgroup.
-struct BlockIter {
-  int n, n_total, n_off, seg_first, i, last_row, mode;
+// The key blocks one query block visits, in order, each split into stages of 64 keys; uniform
+// across the workgroup (every value it returns is scalar).
+struct StageIter {
+  int n, n_total, n_off, seg_first, i, last_row, mode, halves;
+  int j, half;
+  bool masked;
   const int32_t* list;
   const int32_t* minpos;
-  __device__ __forceinline__ bool next(int& j, bool& masked) {
+
+  __device__ __forceinline__ bool next_block() {
     while (n < n_total) {
       const int m = n++;
       if (mode == 0) {
@@ -128,7 +134,6 @@ struct BlockIter {
         return true;
       }
       if (m < n_off) {
-        // the list entry is the same for the whole workgroup: keep it scalar
         j = __builtin_amdgcn_readfirstlane(min(max(list[m], 0), seg_first - 1));
         masked = false;
         return true;
@@ -149,136 +154,135 @@ struct BlockIter {
     }
     return false;
   }
+  // Advance to the next stage; false when the list is exhausted.
+  __device__ __forceinline__ bool next() {
+    if (half >= 0 && half + 1 < halves) {
+      ++half;
+      return true;
+    }
+    half = 0;
+    return next_block();
+  }
 };
 
-// Start the asynchronous loads of key block j (K, V and, for masked permuted blocks, the
-// original positions) into one LDS stage.  K/V rows are padded in LDS; a spare chunk re-reads
-// chunk 0 of its row.
+struct Stage {
+  int key0;     // first key of the stage in the head's key order (block * Bs + half * 64)
+  bool masked;
+};
+
+// Start the asynchronous loads of one stage (K, V and, for masked permuted blocks, the original
+// positions of its keys) into LDS.  A spare chunk of a padded row re-reads chunk 0 of its row.
 template <int D, int BS>
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, __amdgpu_buffer_rsrc_t rk,
-                                           __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rp,
-                                           int j, bool masked, uint16_t* Kst, uint16_t* Vst,
-                                           int32_t* Pst, int w, int lane) {
+__device__ __forceinline__ void issue_stage(const AttnArgs& a, __amdgpu_buffer_rsrc_t rk,
+                                            __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rp,
+                                            Stage st, uint16_t* Kst, uint16_t* Vst, int32_t* Pst,
+                                            int w, int lane) {
   using C = Cfg<D, BS>;
-  const uint32_t tile = static_cast<uint32_t>(j) * BS * D * 2;
+  const uint32_t base = static_cast<uint32_t>(st.key0) * D * 2;
 #pragma unroll
   for (int n = w; n < C::NLDK; n += C::NW) {
     const int P = n * 64 + lane;
     const int r = P / (C::CPR + C::KPAD), pc = P - r * (C::CPR + C::KPAD);
-    load_lds16(rk, Kst + n * 512, static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2), tile);
+    load_lds16(rk, Kst + n * 512, static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2),
+               base);
   }
 #pragma unroll
   for (int n = w; n < C::NLDV; n += C::NW) {
     const int P = n * 64 + lane;
     const int r = P / (C::CPR + C::VPAD), pc = P - r * (C::CPR + C::VPAD);
-    load_lds16(rv, Vst + n * 512, static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2), tile);
+    load_lds16(rv, Vst + n * 512, static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2),
+               base);
   }
-  if (masked && a.mode == 1 && w < BS / 64)
-    load_lds4(rp, Pst + w * 64, static_cast<uint32_t>((w * 64 + lane) * 4),
-                static_cast<uint32_t>(j) * BS * 4);
+  if (st.masked && a.mode == 1 && w == 0)
+    load_lds4(rp, Pst, static_cast<uint32_t>(lane * 4), static_cast<uint32_t>(st.key0) * 4);
 }
 
-// One key block for one wave: 32-key steps of S^T = K Q^T, masking, online softmax and
-// O^T += V^T P^T.  Ks / Vs / Ps are the block's LDS stage.
+// One stage (64 keys) for one wave: 32-key steps of S^T = K Q^T, masking, softmax with the fixed
+// reference, and O^T += V^T P^T.
 template <int D, int BS, int MODE>
-__device__ __forceinline__ void attn_block(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vs,
-                                           const int32_t* Ps, int j, bool masked, int lane, int kh,
-                                           int row0,
-                                           const bf16x8 (&qf)[Cfg<D, BS>::NRF][Cfg<D, BS>::NKS],
-                                           f32x16 (&oacc)[Cfg<D, BS>::NRF][Cfg<D, BS>::NMT],
-                                           float (&mref)[Cfg<D, BS>::NRF],
-                                           float (&lsum)[Cfg<D, BS>::NRF],
-                                           float (&mseen)[Cfg<D, BS>::NRF], bool& bad) {
+__device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vs,
+                                           const int32_t* Ps, Stage st, int lane, int t,
+                                           const bf16x8 (&qf)[Cfg<D, BS>::NKS],
+                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], float& mref,
+                                           float& lsum, float& mseen, bool& bad) {
   using C = Cfg<D, BS>;
   const int hl = lane >> 5;
   const int c32 = lane & 31;
-    const int gp = lane >> 4, li = lane & 15;
+  const int gp = lane >> 4, li = lane & 15;
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt) {
-    // ---- S^T for 32 keys x this wave's rows
-    f32x16 s[C::NRF];
-    const int kr = kh * C::KW + kt * 32 + c32;
+    // ---- S^T for 32 keys x the wave's 32 rows
+    f32x16 s;
+    const int kr = kt * 32 + c32;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kr, ks * 16 + hl * 8)]);
-#pragma unroll
-      for (int f = 0; f < C::NRF; ++f)
-        s[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[f][ks], ks == 0 ? f32x16{} : s[f],
-                                                        0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s, 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- mask, online softmax.  Lane value r is key kh*KW + kt*32 + (r/4)*8 + hl*4 + r%4.
-    bf16x8 pb[C::NRF][2];
+    // ---- mask (one uniform branch touching only the scores).  Lane value r is stage key
+    //      kt*32 + (r/4)*8 + hl*4 + r%4.
+    if (st.masked) {
 #pragma unroll
-    for (int f = 0; f < C::NRF; ++f) {
-      const int t = row0 + f * 32 + c32;
-      // (one uniform branch that only touches the score registers)
-      if (masked) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const int key = kh * C::KW + kt * 32 + rb * 8 + hl * 4;
-          int4 pos;
-          if constexpr (MODE == 1) {
-            pos = *reinterpret_cast<const int4*>(&Ps[key]);
-          } else {
-            pos = make_int4(j * BS + key, j * BS + key + 1, j * BS + key + 2, j * BS + key + 3);
-          }
-          if (pos.x > t) s[f][rb * 4 + 0] = -INFINITY;
-          if (pos.y > t) s[f][rb * 4 + 1] = -INFINITY;
-          if (pos.z > t) s[f][rb * 4 + 2] = -INFINITY;
-          if (pos.w > t) s[f][rb * 4 + 3] = -INFINITY;
+      for (int rb = 0; rb < 4; ++rb) {
+        const int key = kt * 32 + rb * 8 + hl * 4;
+        int4 pos;
+        if constexpr (MODE == 1) {
+          pos = *reinterpret_cast<const int4*>(&Ps[key]);
+        } else {
+          const int p0 = st.key0 + key;
+          pos = make_int4(p0, p0 + 1, p0 + 2, p0 + 3);
         }
+        if (pos.x > t) s[rb * 4 + 0] = -INFINITY;
+        if (pos.y > t) s[rb * 4 + 1] = -INFINITY;
+        if (pos.z > t) s[rb * 4 + 2] = -INFINITY;
+        if (pos.w > t) s[rb * 4 + 3] = -INFINITY;
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[f][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c;
-      // Fixed reference: the first finite block max of the row (the accumulators are still
-      // zero when it is set, so nothing is rescaled).  A later max more than 2^64 above it is
-      // only recorded; the workgroup then recomputes with the exact row max (see the kernel).
-      mseen[f] = fmaxf(mseen[f], mx);
-      mref[f] = (mref[f] == -INFINITY) ? mx : mref[f];
-      bad |= mx > mref[f] + 64.f;
-      const float nm = (mref[f] == -INFINITY) ? 0.f : -mref[f];
-      float rs = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = fast_exp2(fmaf(s[f][8 * s2 + e], a.c, nm));
-          rs += p;
-          pb[f][s2][e] = static_cast<__bf16>(p);   // v_cvt_pk_bf16_f32, round to nearest even
-        }
-      }
-      lsum[f] += rs;
     }
-    __builtin_amdgcn_sched_barrier(0);
+    // ---- softmax against the fixed reference
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c;
+    mseen = fmaxf(mseen, mx);
+    mref = (mref == -INFINITY) ? mx : mref;   // the accumulator is still zero when this is set
+    bad |= mx > mref + 64.f;
+    const float nm = (mref == -INFINITY) ? 0.f : -mref;
+    bf16x8 pb[2];
+    float rs = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(fmaf(s[8 * s2 + e], a.c, nm));
+        rs += p;
+        pb[s2][e] = static_cast<__bf16>(p);   // v_cvt_pk_bf16_f32, round to nearest even
+      }
+    }
+    lsum += rs;
     // ---- O^T += V^T P^T over these 32 keys
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const int key0 = kh * C::KW + kt * 32 + 16 * s2 + 4 * (gp >> 1) + (li >> 2);
+      const int vr = kt * 32 + 16 * s2 + 4 * (gp >> 1) + (li >> 2);
 #pragma unroll
       for (int mt = 0; mt < C::NMT; ++mt) {
         const int dv = mt * 32 + (gp & 1) * 16 + 4 * (li & 3);
-        const u32x2 lo = ds_read_tr(&Vs[voff<D>(key0, dv)]);
-        const u32x2 hi = ds_read_tr(&Vs[voff<D>(key0 + 8, dv)]);
+        const u32x2 lo = ds_read_tr(&Vs[voff<D>(vr, dv)]);
+        const u32x2 hi = ds_read_tr(&Vs[voff<D>(vr + 8, dv)]);
         const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
-        const bf16x8 va = __builtin_bit_cast(bf16x8, w4);
-#pragma unroll
-        for (int f = 0; f < C::NRF; ++f)
-          oacc[f][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[f][s2], oacc[f][mt], 0, 0, 0);
+        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4), pb[s2],
+                                                           oacc[mt], 0, 0, 0);
       }
     }
   }
 }
 
 template <int D, int BS, int MODE>
-__global__ __launch_bounds__(BS * 4) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   using C = Cfg<D, BS>;
   // One LDS array laid out [K stage 0][K stage 1][V stage 0][V stage 1].
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::KTILE + 2 * C::VTILE];
-  __shared__ __attribute__((aligned(16))) int32_t Ps0[BS];
-  __shared__ __attribute__((aligned(16))) int32_t Ps1[BS];
+  __shared__ __attribute__((aligned(16))) int32_t Ps0[C::SK];
+  __shared__ __attribute__((aligned(16))) int32_t Ps1[C::SK];
   uint16_t* const Ks0 = smem + a.tile_off[0];
   uint16_t* const Ks1 = smem + a.tile_off[1];
   uint16_t* const Vs0 = smem + a.tile_off[2];
@@ -286,12 +290,9 @@ __global__ __launch_bounds__(BS * 4) void attn_fwd_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // wave index as a scalar: keeps LDS destinations and row/key offsets wave-uniform
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index as a scalar
   const int hl = lane >> 5;
   const int c32 = lane & 31;
-  const int rg = w % C::RG;  // 32-row group of the query block
-  const int kh = w / C::RG;  // key half of every key block
 
   // work item -> (b, g, i): heaviest query blocks first, one KV head per XCD run
   int b, g, i;
@@ -309,22 +310,24 @@ __global__ __launch_bounds__(BS * 4) void attn_fwd_kernel(AttnArgs a) {
   const int h = g / a.G;
   const size_t q_head = (static_cast<size_t>(b) * a.Hq + g) * a.N;
   const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;
-  const int row0 = i * BS + rg * C::RW;        // first query row of this wave
+  const int t = i * BS + w * 32 + c32;       // this lane's query row (both halves share it)
   const uint32_t head_bytes = static_cast<uint32_t>(a.N) * D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head * D, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head * D, head_bytes);
   const __amdgpu_buffer_rsrc_t rp =
       make_rsrc(a.perm ? a.perm + kv_head : nullptr, a.perm ? static_cast<uint32_t>(a.N) * 4 : 0u);
 
-  BlockIter it;
-  it.n = 0;
+  StageIter it;
   it.i = i;
   it.mode = MODE;
+  it.halves = C::HALVES;
   it.seg_first = (i / a.bps) * a.bps;
   it.last_row = i * BS + BS - 1;
   it.minpos = a.minpos ? a.minpos + kv_head / BS : nullptr;
   it.n_off = 0;
   it.list = nullptr;
+  it.j = 0;
+  it.masked = false;
   if (MODE != 0) {
     const size_t row = (static_cast<size_t>(b) * a.Hq + g) * a.nb + i;
     it.n_off = min(max(a.counts[row], 0), it.seg_first);
@@ -332,116 +335,79 @@ __global__ __launch_bounds__(BS * 4) void attn_fwd_kernel(AttnArgs a) {
   }
   it.n_total = (MODE == 0) ? (i + 1) : (it.n_off + a.bps);
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][ks*16 + hl*8 .. +8]
-  bf16x8 qf[C::NRF][C::NKS];
+  // Q fragments (B operand of S^T = K Q^T): lane holds q[t][ks*16 + hl*8 .. +8]
+  bf16x8 qf[C::NKS];
+  {
+    const uint16_t* qrow = a.q + (q_head + t) * D + hl * 8;
 #pragma unroll
-  for (int f = 0; f < C::NRF; ++f) {
-    const uint16_t* qrow = a.q + (q_head + row0 + f * 32 + c32) * D + hl * 8;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) qf[f][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+    for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
   }
-  f32x16 oacc[C::NRF][C::NMT];
-  float mref[C::NRF], lsum[C::NRF], mseen[C::NRF];
-#pragma unroll
-  for (int f = 0; f < C::NRF; ++f) mseen[f] = -INFINITY;   // largest row max seen, log2 units
+  f32x16 oacc[C::NMT];
+  float mref = -INFINITY, lsum = 0.f;   // log2 units; lsum is this lane's half of the row sum
+  float mseen = -INFINITY;
 
   // Pass 0 runs with the first-block reference; pass 1 (rare) reruns with the exact row max.
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int f = 0; f < C::NRF; ++f) {
+    for (int mt = 0; mt < C::NMT; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < C::NMT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[f][mt][r] = 0.f;
-      mref[f] = pass == 0 ? -INFINITY : mseen[f];   // reference max, log2 units
-      lsum[f] = 0.f;                                // this lane's half of the row sum
-    }
+      for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
+    mref = pass == 0 ? -INFINITY : mseen;
+    lsum = 0.f;
     bool bad = false;
     it.n = 0;
-    int j_cur = 0, j_next = 0;
-    bool m_cur = false, m_next = false;
-    bool have = it.next(j_cur, m_cur);
-    if (have) issue_tile<D, BS>(a, rk, rv, rp, j_cur, m_cur, Ks0, Vs0, Ps0, w, lane);
-    // Two stages, unrolled so that each stage's LDS offsets are compile-time constants.
+    it.half = -1;
+    Stage cur, nxt;
+    bool have = it.next();
+    cur.key0 = it.j * BS + it.half * C::SK;
+    cur.masked = it.masked;
+    if (have) issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
+    // Two LDS stages, unrolled so that each stage's LDS offsets are compile-time constants.
     while (have) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // stage 0 landed; stage 1 no longer read
-      const bool more = it.next(j_next, m_next);
-      if (more) issue_tile<D, BS>(a, rk, rv, rp, j_next, m_next, Ks1, Vs1, Ps1, w, lane);
-      attn_block<D, BS, MODE>(a, Ks0, Vs0, Ps0, j_cur, m_cur, lane, kh, row0, qf, oacc, mref,
-                              lsum, mseen, bad);
+      const bool more = it.next();
+      nxt.key0 = it.j * BS + it.half * C::SK;
+      nxt.masked = it.masked;
+      if (more) issue_stage<D, BS>(a, rk, rv, rp, nxt, Ks1, Vs1, Ps1, w, lane);
+      attn_stage<D, BS, MODE>(a, Ks0, Vs0, Ps0, cur, lane, t, qf, oacc, mref, lsum, mseen, bad);
       if (!more) break;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // stage 1 landed; stage 0 no longer read
-      have = it.next(j_cur, m_cur);
-      if (have) issue_tile<D, BS>(a, rk, rv, rp, j_cur, m_cur, Ks0, Vs0, Ps0, w, lane);
-      attn_block<D, BS, MODE>(a, Ks1, Vs1, Ps1, j_next, m_next, lane, kh, row0, qf, oacc, mref,
-                              lsum, mseen, bad);
+      have = it.next();
+      cur.key0 = it.j * BS + it.half * C::SK;
+      cur.masked = it.masked;
+      if (have) issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
+      attn_stage<D, BS, MODE>(a, Ks1, Vs1, Ps1, nxt, lane, t, qf, oacc, mref, lsum, mseen, bad);
     }
-    // Every wave has finished reading the stages before a second pass or the merge reuses them.
+    // Every wave has finished reading the stages before a second pass reuses them.
     if (!__syncthreads_or(bad ? 1 : 0)) break;
   }
 
-  // ---- merge the two key halves (kh = 1 hands its state to kh = 0) through LDS
-  __syncthreads();
-  float* xo = reinterpret_cast<float*>(smem);                // [rg][f][mt][r][lane] partial O
-  float* xm = reinterpret_cast<float*>(smem + 2 * C::KTILE + C::VTILE);  // [rg][f][2][lane]
-  static_assert(C::RG * C::NRF * C::NMT * 16 * 64 * 4 <= (2 * C::KTILE + C::VTILE) * 2,
-                "merge buffer must fit in the K/V stages");
-  if (kh == 1) {
+  const float l = lsum + __shfl_xor(lsum, 32);   // the two halves of the row
+  const float inv_l = (l > 0.f) ? 1.f / l : 0.f;
+  uint16_t* orow = a.o + (q_head + t) * D;
 #pragma unroll
-    for (int f = 0; f < C::NRF; ++f) {
+  for (int mt = 0; mt < C::NMT; ++mt) {
 #pragma unroll
-      for (int mt = 0; mt < C::NMT; ++mt)
+    for (int rb = 0; rb < 4; ++rb) {
+      bf16x4 pk;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          xo[(((rg * C::NRF + f) * C::NMT + mt) * 16 + r) * 64 + lane] = oacc[f][mt][r];
-      xm[((rg * C::NRF + f) * 2 + 0) * 64 + lane] = mref[f];
-      xm[((rg * C::NRF + f) * 2 + 1) * 64 + lane] = lsum[f];
+      for (int e = 0; e < 4; ++e) pk[e] = static_cast<__bf16>(oacc[mt][rb * 4 + e] * inv_l);
+      // O^T lane value r of tile mt is head-dim index mt*32 + (r/4)*8 + hl*4 + r%4 of row t
+      *reinterpret_cast<bf16x4*>(orow + mt * 32 + rb * 8 + hl * 4) = pk;
     }
   }
-  __syncthreads();
-  if (kh == 1) return;
-#pragma unroll
-  for (int f = 0; f < C::NRF; ++f) {
-    const float mb = xm[((rg * C::NRF + f) * 2 + 0) * 64 + lane];
-    const float lb = xm[((rg * C::NRF + f) * 2 + 1) * 64 + lane];
-    const float m = fmaxf(mref[f], mb);
-    const float mu = (m == -INFINITY) ? 0.f : m;
-    const float sa = fast_exp2(mref[f] - mu), sb = fast_exp2(mb - mu);
-    float la = lsum[f] * sa + lb * sb;
-    la += __shfl_xor(la, 32);                  // the two halves of the row
-    const float inv_l = (la > 0.f) ? 1.f / la : 0.f;
-    const int t = row0 + f * 32 + c32;
-    uint16_t* orow = a.o + (q_head + t) * D;
-#pragma unroll
-    for (int mt = 0; mt < C::NMT; ++mt) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        float v4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rb * 4 + e;
-          const float ob = xo[(((rg * C::NRF + f) * C::NMT + mt) * 16 + r) * 64 + lane];
-          v4[e] = (oacc[f][mt][r] * sa + ob * sb) * inv_l;
-        }
-        bf16x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = static_cast<__bf16>(v4[e]);
-        // O^T lane value r of tile mt is head-dim index mt*32 + (r/4)*8 + hl*4 + r%4 of row t
-        *reinterpret_cast<bf16x4*>(orow + mt * 32 + rb * 8 + hl * 4) = pk;
-      }
-    }
-    if (a.lse && hl == 0) a.lse[q_head + t] = (m + __log2f(la)) * kLn2;
-  }
+  if (a.lse && hl == 0) a.lse[q_head + t] = (mref + __log2f(l)) * kLn2;
 }
 
 template <int D, int BS>
 hipError_t launch_attn_t(const Dims& d, const AttnArgs& a, hipStream_t stream) {
   const int total = d.B * d.Hq * d.nb;
-  if (a.mode == 1) return launch(attn_fwd_kernel<D, BS, 1>, dim3(total), dim3(Cfg<D, BS>::NT), 0, stream, a);
-  if (a.mode == 2) return launch(attn_fwd_kernel<D, BS, 2>, dim3(total), dim3(Cfg<D, BS>::NT), 0, stream, a);
-  return launch(attn_fwd_kernel<D, BS, 0>, dim3(total), dim3(Cfg<D, BS>::NT), 0, stream, a);
+  const dim3 block(Cfg<D, BS>::NT);
+  if (a.mode == 1) return launch(attn_fwd_kernel<D, BS, 1>, dim3(total), block, 0, stream, a);
+  if (a.mode == 2) return launch(attn_fwd_kernel<D, BS, 2>, dim3(total), block, 0, stream, a);
+  return launch(attn_fwd_kernel<D, BS, 0>, dim3(total), block, 0, stream, a);
 }
 
 }  // namespace
@@ -460,7 +426,7 @@ hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, cons
   const long long total = static_cast<long long>(d.B) * d.Hq * d.nb;
   a.xcd_map = (total % 8 == 0) ? 1 : 0;
   a.c = scale * kLog2e;
-  const int ktile = d.Bs * (d.d + 8), vtile = d.Bs * (d.d + 32);
+  const int ktile = kStageKeys * (d.d + 8), vtile = kStageKeys * (d.d + 32);
   a.tile_off[0] = 0;
   a.tile_off[1] = ktile;
   a.tile_off[2] = 2 * ktile;

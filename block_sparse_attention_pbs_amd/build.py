@@ -20,6 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpbs.so")
 SOURCES = ["pbs_api.cpp", "pbs_score.hip", "pbs_permute.hip", "pbs_select.hip", "pbs_attn.hip"]
+# Per-source extra flags.  The attention kernel keeps its MFMA accumulators in VGPRs: its scores
+# feed VALU work directly (no v_accvgpr_read per score), and the whole kernel then fits the
+# 256-register budget of two waves per SIMD.
+EXTRA_FLAGS = {"pbs_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -41,7 +45,7 @@ def common_flags(debug: bool = False):
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
-    cmd = [hipcc(), "-x", "hip", *common_flags(), "-c", path, "-o", obj]
+    cmd = [hipcc(), "-x", "hip", *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

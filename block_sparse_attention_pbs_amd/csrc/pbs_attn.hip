@@ -17,7 +17,9 @@
 //    workgroups share a CU: while one waits for its next stage the other computes;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 (A = K rows from
 //    LDS, B = the wave's Q rows held in registers), so each lane owns one query row and the
-//    softmax statistics need one cross-half exchange per 32 keys;
+//    softmax statistics need one cross-half exchange per stage.  The two 32-key halves of a
+//    stage accumulate in two independent MFMA chains, and the accumulators live in VGPRs (built
+//    with the VGPR form of the MFMAs), so scores feed the softmax without register moves;
 //  * the output is accumulated transposed, O^T += V^T P^T: P leaves the score accumulators as the
 //    bf16 B operand without touching LDS (the key order inside a 16-key step is a relabelling
 //    shared by both operands); V^T comes from the row-major V tile through the transposing LDS
@@ -209,19 +211,23 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
   const int hl = lane >> 5;
   const int c32 = lane & 31;
   const int gp = lane >> 4, li = lane & 15;
+  // ---- S^T for the stage's 64 keys x the wave's 32 rows: two independent 32-key chains
+  f32x16 s[C::NKT];
 #pragma unroll
-  for (int kt = 0; kt < C::NKT; ++kt) {
-    // ---- S^T for 32 keys x the wave's 32 rows
-    f32x16 s;
-    const int kr = kt * 32 + c32;
+  for (int ks = 0; ks < C::NKS; ++ks) {
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kr, ks * 16 + hl * 8)]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s, 0, 0, 0);
+    for (int kt = 0; kt < C::NKT; ++kt) {
+      const bf16x8 kf =
+          *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kt * 32 + c32, ks * 16 + hl * 8)]);
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s[kt], 0,
+                                                      0, 0);
     }
-    // ---- mask (one uniform branch touching only the scores).  Lane value r is stage key
-    //      kt*32 + (r/4)*8 + hl*4 + r%4.
-    if (st.masked) {
+  }
+  // ---- mask (one uniform branch touching only the scores).  Lane value r of sub-tile kt is
+  //      stage key kt*32 + (r/4)*8 + hl*4 + r%4.
+  if (st.masked) {
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int key = kt * 32 + rb * 8 + hl * 4;
@@ -232,34 +238,40 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
           const int p0 = st.key0 + key;
           pos = make_int4(p0, p0 + 1, p0 + 2, p0 + 3);
         }
-        if (pos.x > t) s[rb * 4 + 0] = -INFINITY;
-        if (pos.y > t) s[rb * 4 + 1] = -INFINITY;
-        if (pos.z > t) s[rb * 4 + 2] = -INFINITY;
-        if (pos.w > t) s[rb * 4 + 3] = -INFINITY;
+        if (pos.x > t) s[kt][rb * 4 + 0] = -INFINITY;
+        if (pos.y > t) s[kt][rb * 4 + 1] = -INFINITY;
+        if (pos.z > t) s[kt][rb * 4 + 2] = -INFINITY;
+        if (pos.w > t) s[kt][rb * 4 + 3] = -INFINITY;
       }
     }
-    // ---- softmax against the fixed reference
-    float mx = -INFINITY;
+  }
+  // ---- softmax against the fixed reference
+  float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c;
-    mseen = fmaxf(mseen, mx);
-    mref = (mref == -INFINITY) ? mx : mref;   // the accumulator is still zero when this is set
-    bad |= mx > mref + 64.f;
-    const float nm = (mref == -INFINITY) ? 0.f : -mref;
-    bf16x8 pb[2];
-    float rs = 0.f;
+  for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c;
+  mseen = fmaxf(mseen, mx);
+  mref = (mref == -INFINITY) ? mx : mref;   // the accumulator is still zero when this is set
+  bad |= mx > mref + 64.f;
+  const float nm = (mref == -INFINITY) ? 0.f : -mref;
+  bf16x8 pb[C::NKT][2];
+  float rs = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(fmaf(s[8 * s2 + e], a.c, nm));
+        const float p = fast_exp2(fmaf(s[kt][8 * s2 + e], a.c, nm));
         rs += p;
-        pb[s2][e] = static_cast<__bf16>(p);   // v_cvt_pk_bf16_f32, round to nearest even
+        pb[kt][s2][e] = static_cast<__bf16>(p);   // v_cvt_pk_bf16_f32, round to nearest even
       }
-    }
-    lsum += rs;
-    // ---- O^T += V^T P^T over these 32 keys
+  lsum += rs;
+  // ---- O^T += V^T P^T over the stage's keys
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int vr = kt * 32 + 16 * s2 + 4 * (gp >> 1) + (li >> 2);
@@ -269,8 +281,8 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
         const u32x2 lo = ds_read_tr(&Vs[voff<D>(vr, dv)]);
         const u32x2 hi = ds_read_tr(&Vs[voff<D>(vr + 8, dv)]);
         const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4), pb[s2],
-                                                           oacc[mt], 0, 0, 0);
+        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4),
+                                                           pb[kt][s2], oacc[mt], 0, 0, 0);
       }
     }
   }

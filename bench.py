@@ -59,10 +59,10 @@ def read_traffic(workload: str):
         return None
 
 
-def cpu_oracle_baseline(w, inp, scale, param, counts_gpu):
+def cpu_oracle_baseline(w, inp, scale, param):
     """The oracle as it stands, on a bounded sample of the workload, extrapolated to one whole
     prefill.  Sample: key scores (twice) and permutation for KV head 0, pooled block scores +
-    selection for query head 0, and attention for 256 query blocks spread evenly over query
+    selection for query head 0, and attention for 640 query blocks spread evenly over query
     head 0 (every segment, early and late blocks alike)."""
     import numpy as np
     import oracle
@@ -86,8 +86,8 @@ def cpu_oracle_baseline(w, inp, scale, param, counts_gpu):
     counts, idx = oracle.select_blocks(Pm, block=w.block, segment=w.segment, mode=mode, param=param)
     t_sel = time.perf_counter() - t
     nb = w.seq_len // w.block
-    stride = max(1, nb // 256)
-    sample = [(0, 0, i) for i in range(nb - 1, -1, -stride)]
+    n_sample = min(nb, 640)
+    sample = [(0, 0, int(i)) for i in np.unique(np.round(np.linspace(0, nb - 1, n_sample)).astype(int))[::-1]]
     t = time.perf_counter()
     oracle.attention(q0[:, :1], k0, v0, block=w.block, segment=w.segment, scale=scale, perm=perm,
                      counts=counts, idx=idx, qblocks=sample)
@@ -98,7 +98,7 @@ def cpu_oracle_baseline(w, inp, scale, param, counts_gpu):
         "value": total_s * 1e3, "unit": "ms", "cores": threads, "kind": "oracle",
         "sample": (f"float64 numpy oracle on KV head 0 (scores, permutation), query head 0 "
                    f"(block scores, selection) and {len(sample)} of {nb} query blocks of query head 0 "
-                   f"(attention); extrapolated x{w.heads_kv} / x{w.heads_q} / x{w.heads_q * nb // len(sample)}; "
+                   f"(attention); extrapolated x{w.heads_kv} / x{w.heads_q} / x{w.heads_q * nb / len(sample):.1f}; "
                    f"{time.perf_counter() - t_all:.1f} s of CPU work"),
         "stage_s_sampled": {"score": round(t_score, 3), "permute": round(t_perm, 3),
                             "select": round(t_sel, 3), "attention": round(t_attn, 3)},
@@ -229,7 +229,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_oracle_baseline(w, inp, scale, param, counts)
+        cpu = cpu_oracle_baseline(w, inp, scale, param)
 
     traffic = read_traffic(w.name)
     # HBM bytes each stage must move at least (inputs read once, outputs written once).

@@ -93,22 +93,34 @@ __device__ __forceinline__ constexpr int voff(int r, int e) {
   return r * (D + 32) + e;
 }
 
-// Buffer resource over `bytes` bytes from `base` (gfx9 descriptor word 3).  Loads through it are
+// Buffer resource over `bytes` bytes from `base` (gfx9 descriptor: word 1 holds the top 16
+// address bits with stride 0, word 2 the size, word 3 the data format).  Loads through it are
 // bounds-checked by the hardware and take a 32-bit per-lane offset plus a scalar offset.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes,
+               0x00020000u};
 }
-// Direct buffer->LDS loads: lane l's 16 (or 4) bytes land at lds + l*16 (l*4).
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
-                                           uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, soff, 0, 0);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
 }
-__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
-                                          uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
-                                           voff, soff, 0, 0);
+// Direct buffer->LDS loads: lane l's 16 (or 4) bytes land at lds + l*16 (l*4).  Written as asm
+// on purpose: the compiler cannot tell that a stage's loads and the other stage's LDS reads touch
+// different tiles, and would otherwise wait for these loads before every LDS read that follows
+// them, serialising the double buffer.  Their completion is awaited explicitly (s_waitcnt +
+// barrier) before the stage they fill is read.
+__device__ __forceinline__ void load_lds16(u32x4 r, const void* lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr(lds)), "v"(voff), "s"(r), "s"(soff)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void load_lds4(u32x4 r, const void* lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr(lds)), "v"(voff), "s"(r), "s"(soff)
+               : "memory", "m0");
 }
 
 __device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* lds_ptr) {
@@ -175,8 +187,7 @@ struct Stage {
 // Start the asynchronous loads of one stage (K, V and, for masked permuted blocks, the original
 // positions of its keys) into LDS.  A spare chunk of a padded row re-reads chunk 0 of its row.
 template <int D, int BS>
-__device__ __forceinline__ void issue_stage(const AttnArgs& a, __amdgpu_buffer_rsrc_t rk,
-                                            __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rp,
+__device__ __forceinline__ void issue_stage(const AttnArgs& a, u32x4 rk, u32x4 rv, u32x4 rp,
                                             Stage st, uint16_t* Kst, uint16_t* Vst, int32_t* Pst,
                                             int w, int lane) {
   using C = Cfg<D, BS>;
@@ -199,79 +210,124 @@ __device__ __forceinline__ void issue_stage(const AttnArgs& a, __amdgpu_buffer_r
     load_lds4(rp, Pst, static_cast<uint32_t>(lane * 4), static_cast<uint32_t>(st.key0) * 4);
 }
 
-// One stage (64 keys) for one wave: 32-key steps of S^T = K Q^T, masking, softmax with the fixed
-// reference, and O^T += V^T P^T.
-template <int D, int BS, int MODE>
+// x combined with its value in the other half of the wave (lane l and lane l ^ 32).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Causal mask of a 32-key sub-tile as the initial value of its score accumulator: -inf for a key
+// whose original position is after the lane's query row t, else 0 (then -inf + the dot product
+// stays -inf).  Lane value r of sub-tile kt is stage key kt*32 + (r/4)*8 + hl*4 + r%4.
+template <int MODE>
+__device__ __forceinline__ f32x16 mask_init(const int32_t* Ps, int key0, int kt, int hl, int t) {
+  f32x16 m;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int key = kt * 32 + rb * 8 + hl * 4;
+    int4 pos;
+    if constexpr (MODE == 1) {
+      pos = *reinterpret_cast<const int4*>(&Ps[key]);
+    } else {
+      const int p0 = key0 + key;
+      pos = make_int4(p0, p0 + 1, p0 + 2, p0 + 3);
+    }
+    m[rb * 4 + 0] = pos.x > t ? -INFINITY : 0.f;
+    m[rb * 4 + 1] = pos.y > t ? -INFINITY : 0.f;
+    m[rb * 4 + 2] = pos.z > t ? -INFINITY : 0.f;
+    m[rb * 4 + 3] = pos.w > t ? -INFINITY : 0.f;
+  }
+  return m;
+}
+
+// Row state of one wave across the stages of a pass (log2 units).
+struct RowState {
+  float mref;     // fixed reference subtracted before exp2 (-inf until the row has seen a key)
+  float lsum;     // this lane's half of the row's sum of exp2
+  float mseen;    // exact row max (max-only pass)
+  bool need_ref;  // some row of the wave has no reference yet (wave-uniform)
+};
+
+// One stage (64 keys) for one wave.  S^T = K Q^T for the two 32-key halves as two independent MFMA
+// chains (masked keys enter as -inf through the accumulators' initial values); then, half by half,
+// exp2 against the fixed reference and O^T += V^T P^T, so that the exp2 work of one half overlaps
+// the matrix work of the other.  No running max: the reference is the first finite stage max of
+// the row, and an overflow of the row sum is caught after the pass (the row max is then found by a
+// max-only pass and the pass is repeated).
+template <int D, int BS, int MODE, bool MAXONLY>
 __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vs,
                                            const int32_t* Ps, Stage st, int lane, int t,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NKS],
-                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], float& mref,
-                                           float& lsum, float& mseen, bool& bad) {
+                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
   using C = Cfg<D, BS>;
   const int hl = lane >> 5;
   const int c32 = lane & 31;
   const int gp = lane >> 4, li = lane & 15;
-  // ---- S^T for the stage's 64 keys x the wave's 32 rows: two independent 32-key chains
   f32x16 s[C::NKT];
+  {
+    bf16x8 k0[C::NKT];
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
+    for (int kt = 0; kt < C::NKT; ++kt)
+      k0[kt] = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kt * 32 + c32, hl * 8)]);
+    if (st.masked) {
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
+      for (int kt = 0; kt < C::NKT; ++kt)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            k0[kt], qf[0], mask_init<MODE>(Ps, st.key0, kt, hl, t), 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0[kt], qf[0], f32x16{}, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt) {
+#pragma unroll
+    for (int ks = 1; ks < C::NKS; ++ks) {
       const bf16x8 kf =
           *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kt * 32 + c32, ks * 16 + hl * 8)]);
-      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s[kt], 0,
-                                                      0, 0);
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
     }
   }
-  // ---- mask (one uniform branch touching only the scores).  Lane value r of sub-tile kt is
-  //      stage key kt*32 + (r/4)*8 + hl*4 + r%4.
-  if (st.masked) {
+  if constexpr (MAXONLY) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
+    for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int key = kt * 32 + rb * 8 + hl * 4;
-        int4 pos;
-        if constexpr (MODE == 1) {
-          pos = *reinterpret_cast<const int4*>(&Ps[key]);
-        } else {
-          const int p0 = st.key0 + key;
-          pos = make_int4(p0, p0 + 1, p0 + 2, p0 + 3);
-        }
-        if (pos.x > t) s[kt][rb * 4 + 0] = -INFINITY;
-        if (pos.y > t) s[kt][rb * 4 + 1] = -INFINITY;
-        if (pos.z > t) s[kt][rb * 4 + 2] = -INFINITY;
-        if (pos.w > t) s[kt][rb * 4 + 3] = -INFINITY;
-      }
-    }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    rs.mseen = fmaxf(rs.mseen, pair_max(mx) * a.c);
+    return;
   }
-  // ---- softmax against the fixed reference
-  float mx = -INFINITY;
+  if (rs.need_ref) {  // wave-uniform; normally only the first stage of a pass
+    float mx = -INFINITY;
 #pragma unroll
-  for (int kt = 0; kt < C::NKT; ++kt)
+    for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c;
-  mseen = fmaxf(mseen, mx);
-  mref = (mref == -INFINITY) ? mx : mref;   // the accumulator is still zero when this is set
-  bad |= mx > mref + 64.f;
-  const float nm = (mref == -INFINITY) ? 0.f : -mref;
-  bf16x8 pb[C::NKT][2];
-  float rs = 0.f;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    mx = pair_max(mx) * a.c;
+    rs.mref = (rs.mref == -INFINITY) ? mx : rs.mref;   // such a row's accumulator is still zero
+    rs.need_ref = __builtin_amdgcn_ballot_w64(rs.mref == -INFINITY) != 0;
+  }
+  const float nm = (rs.mref == -INFINITY) ? 0.f : -rs.mref;
 #pragma unroll
-  for (int kt = 0; kt < C::NKT; ++kt)
+  for (int kt = 0; kt < C::NKT; ++kt) {
+    bf16x8 pb[2];
+    float sum = 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = fast_exp2(fmaf(s[kt][8 * s2 + e], a.c, nm));
-        rs += p;
-        pb[kt][s2][e] = static_cast<__bf16>(p);   // v_cvt_pk_bf16_f32, round to nearest even
+        sum += p;
+        pb[s2][e] = static_cast<__bf16>(p);   // v_cvt_pk_bf16_f32, round to nearest even
       }
-  lsum += rs;
-  // ---- O^T += V^T P^T over the stage's keys
-#pragma unroll
-  for (int kt = 0; kt < C::NKT; ++kt) {
+    rs.lsum += sum;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int vr = kt * 32 + 16 * s2 + 4 * (gp >> 1) + (li >> 2);
@@ -282,10 +338,48 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
         const u32x2 hi = ds_read_tr(&Vs[voff<D>(vr + 8, dv)]);
         const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
         oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4),
-                                                           pb[kt][s2], oacc[mt], 0, 0, 0);
+                                                           pb[s2], oacc[mt], 0, 0, 0);
       }
     }
   }
+}
+
+// One pass over the visited key blocks: two LDS stages, unrolled so that each stage's LDS offsets
+// are compile-time constants.  Each stage's loads are issued one stage ahead; the wait + barrier at
+// the top of a stage both lands the stage and frees the other buffer for the next loads.
+template <int D, int BS, int MODE, bool MAXONLY>
+__device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, u32x4 rk, u32x4 rv,
+                                          u32x4 rp, uint16_t* Ks0, uint16_t* Ks1, uint16_t* Vs0,
+                                          uint16_t* Vs1, int32_t* Ps0, int32_t* Ps1, int w,
+                                          int lane, int t, const bf16x8 (&qf)[Cfg<D, BS>::NKS],
+                                          f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
+  using C = Cfg<D, BS>;
+  it.n = 0;
+  it.half = -1;
+  Stage cur, nxt;
+  bool have = it.next();
+  cur.key0 = it.j * BS + it.half * C::SK;
+  cur.masked = it.masked;
+  if (have) issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
+  while (have) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // stage 0 landed; stage 1 no longer read
+    const bool more = it.next();
+    nxt.key0 = it.j * BS + it.half * C::SK;
+    nxt.masked = it.masked;
+    if (more) issue_stage<D, BS>(a, rk, rv, rp, nxt, Ks1, Vs1, Ps1, w, lane);
+    attn_stage<D, BS, MODE, MAXONLY>(a, Ks0, Vs0, Ps0, cur, lane, t, qf, oacc, rs);
+    if (!more) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // stage 1 landed; stage 0 no longer read
+    have = it.next();
+    cur.key0 = it.j * BS + it.half * C::SK;
+    cur.masked = it.masked;
+    if (have) issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
+    attn_stage<D, BS, MODE, MAXONLY>(a, Ks1, Vs1, Ps1, nxt, lane, t, qf, oacc, rs);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // every wave is done with both buffers before another pass refills them
 }
 
 template <int D, int BS, int MODE>
@@ -324,9 +418,9 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;
   const int t = i * BS + w * 32 + c32;       // this lane's query row (both halves share it)
   const uint32_t head_bytes = static_cast<uint32_t>(a.N) * D * 2;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_head * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_head * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t rp =
+  const u32x4 rk = make_rsrc(a.k + kv_head * D, head_bytes);
+  const u32x4 rv = make_rsrc(a.v + kv_head * D, head_bytes);
+  const u32x4 rp =
       make_rsrc(a.perm ? a.perm + kv_head : nullptr, a.perm ? static_cast<uint32_t>(a.N) * 4 : 0u);
 
   StageIter it;
@@ -355,48 +449,26 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
     for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
   }
   f32x16 oacc[C::NMT];
-  float mref = -INFINITY, lsum = 0.f;   // log2 units; lsum is this lane's half of the row sum
-  float mseen = -INFINITY;
-
-  // Pass 0 runs with the first-block reference; pass 1 (rare) reruns with the exact row max.
-  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int mt = 0; mt < C::NMT; ++mt)
+  for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
+  RowState rs{-INFINITY, 0.f, -INFINITY, true};
+  attn_pass<D, BS, MODE, false>(a, it, rk, rv, rp, Ks0, Ks1, Vs0, Vs1, Ps0, Ps1, w, lane, t, qf,
+                                oacc, rs);
+  // A row whose sum left [0, 2^64] (an exp2 overflow, or scores far above the reference) is
+  // recomputed: first its exact maximum, then the pass against that maximum.
+  if (__syncthreads_or(!(pair_sum(rs.lsum) <= 0x1p64f) ? 1 : 0)) {
+    attn_pass<D, BS, MODE, true>(a, it, rk, rv, rp, Ks0, Ks1, Vs0, Vs1, Ps0, Ps1, w, lane, t, qf,
+                                 oacc, rs);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
-    mref = pass == 0 ? -INFINITY : mseen;
-    lsum = 0.f;
-    bool bad = false;
-    it.n = 0;
-    it.half = -1;
-    Stage cur, nxt;
-    bool have = it.next();
-    cur.key0 = it.j * BS + it.half * C::SK;
-    cur.masked = it.masked;
-    if (have) issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
-    // Two LDS stages, unrolled so that each stage's LDS offsets are compile-time constants.
-    while (have) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();  // stage 0 landed; stage 1 no longer read
-      const bool more = it.next();
-      nxt.key0 = it.j * BS + it.half * C::SK;
-      nxt.masked = it.masked;
-      if (more) issue_stage<D, BS>(a, rk, rv, rp, nxt, Ks1, Vs1, Ps1, w, lane);
-      attn_stage<D, BS, MODE>(a, Ks0, Vs0, Ps0, cur, lane, t, qf, oacc, mref, lsum, mseen, bad);
-      if (!more) break;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();  // stage 1 landed; stage 0 no longer read
-      have = it.next();
-      cur.key0 = it.j * BS + it.half * C::SK;
-      cur.masked = it.masked;
-      if (have) issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
-      attn_stage<D, BS, MODE>(a, Ks1, Vs1, Ps1, nxt, lane, t, qf, oacc, mref, lsum, mseen, bad);
-    }
-    // Every wave has finished reading the stages before a second pass reuses them.
-    if (!__syncthreads_or(bad ? 1 : 0)) break;
+    for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
+    rs.mref = rs.mseen;
+    rs.lsum = 0.f;
+    rs.need_ref = false;
+    attn_pass<D, BS, MODE, false>(a, it, rk, rv, rp, Ks0, Ks1, Vs0, Vs1, Ps0, Ps1, w, lane, t, qf,
+                                  oacc, rs);
   }
 
-  const float l = lsum + __shfl_xor(lsum, 32);   // the two halves of the row
+  const float l = pair_sum(rs.lsum);   // the two halves of the row
   const float inv_l = (l > 0.f) ? 1.f / l : 0.f;
   uint16_t* orow = a.o + (q_head + t) * D;
 #pragma unroll
@@ -410,7 +482,7 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
       *reinterpret_cast<bf16x4*>(orow + mt * 32 + rb * 8 + hl * 4) = pk;
     }
   }
-  if (a.lse && hl == 0) a.lse[q_head + t] = (mref + __log2f(l)) * kLn2;
+  if (a.lse && hl == 0) a.lse[q_head + t] = (rs.mref + __log2f(l)) * kLn2;
 }
 
 template <int D, int BS>

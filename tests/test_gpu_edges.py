@@ -164,3 +164,53 @@ def test_empty_problem_launches_nothing():
     sh = shape(0, 4, 2, 1024, 128, 128, 256)
     P.pbs_attn_fwd(sh, 0, 0, 0, None, None, None, None, 0.1, 0)
     P.pbs_score(sh, 0, 0, 0.1, 0, 0, 0)
+
+
+def _dominant_key_inputs(seed, N=2048, d=128, big_at=700, big=400.0):
+    """Queries aligned with a direction u and one key far along u: its score exceeds the scores
+    of the keys visited before it by far more than float32 exp2 can represent (pass-0 overflow),
+    so the kernel has to fall back to the exact row maximum."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((1, 2, N, d)).astype(np.float32) + np.float32(3.0) * u.astype(np.float32)
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    v = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    k[0, 0, big_at] = (big * u).astype(np.float32)
+    return [pbs_synth.f32_to_bf16_bits(x) for x in (q, k, v)]
+
+
+def test_dominant_late_key_dense():
+    say("dominant late key, dense")
+    q, k, v = _dominant_key_inputs(21)
+    scale = oracle.default_scale(128)
+    od, ol = oracle.dense_causal(q, k, v, block=128, scale=scale)
+    assert ol.max() > 60.0  # the key's logit is far above every earlier one
+    sh = shape(1, 2, 1, 2048, 128, 128, 128)
+    o, lse = run_attn(sh, dev_bf16(q), dev_bf16(k), dev_bf16(v), None, None, None, None, scale)
+    check_attn(o.float().cpu().numpy(), od, "dominant key dense")
+    assert np.abs(lse.cpu().numpy() - ol).max() < 1e-3
+
+
+@pytest.mark.parametrize("permuted", [True, False])
+def test_dominant_late_key_pbs(permuted):
+    say(f"dominant late key, PBS permuted={permuted}")
+    q, k, v = _dominant_key_inputs(22)
+    scale = oracle.default_scale(128)
+    N, Bs, S = 2048, 128, 512
+    sc = oracle.key_scores(q, k, block=Bs, segment=S, scale=scale)
+    perm = oracle.segment_permutation(sc, segment=S) if permuted else \
+        np.broadcast_to(np.arange(N, dtype=np.int32), (1, 1, N)).copy()
+    kp, vp = oracle.apply_permutation(k, perm), oracle.apply_permutation(v, perm)
+    Pm = oracle.block_probabilities(q, kp, block=Bs, segment=S, scale=scale)
+    counts, idx = oracle.select_blocks(Pm, block=Bs, segment=S, mode=oracle.KEEP, param=0.5)
+    oo, ol = oracle.attention(q, k, v, block=Bs, segment=S, scale=scale, perm=perm, counts=counts,
+                              idx=idx)
+    assert ol.max() > 60.0
+    sh = shape(1, 2, 1, N, 128, Bs, S)
+    minpos = perm.reshape(1, 1, N // Bs, Bs).min(-1).astype(np.int32)
+    o, lse = run_attn(sh, dev_bf16(q), dev_bf16(kp), dev_bf16(vp),
+                      dev(perm) if permuted else None, dev(minpos) if permuted else None,
+                      dev(counts), dev(idx), scale)
+    check_attn(o.float().cpu().numpy(), oo, f"dominant key PBS permuted={permuted}")
+    assert np.abs(lse.cpu().numpy() - ol).max() < 1e-3

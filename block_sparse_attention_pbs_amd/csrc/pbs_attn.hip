@@ -62,6 +62,8 @@ struct AttnArgs {
 };
 
 constexpr int kStageKeys = 64;  // keys per LDS stage
+constexpr int kOffWindow = 1792; // off-diagonal list entries held in LDS at a time
+constexpr int kOwnMax = 256;     // own-segment blocks (S / Bs <= 16384 / 64)
 
 template <int D, int BS>
 struct Cfg {
@@ -131,51 +133,73 @@ __device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* lds_ptr) {
 }
 
 // The key blocks one query block visits, in order, each split into stages of 64 keys; uniform
-// across the workgroup (every value it returns is scalar).
+// across the workgroup (every value it returns is scalar).  The visit list lives in LDS as 16-bit
+// entries (block index, bit 15 = needs the causal mask): the query block's off-diagonal list, a
+// window of kOffWindow entries at a time, and the visible own-segment blocks, compacted once.
+// Each entry is read from LDS one stage before it is used, so no memory latency sits between two
+// stages.
 struct StageIter {
-  int n, n_total, n_off, seg_first, i, last_row, mode, halves;
+  int mode, halves, i, seg_first;
+  int n_off, n_own;     // list lengths (MODE != 0)
+  int m;                // next entry (MODE 0: next block)
+  int win;              // first off-diagonal entry held in the LDS window
   int j, half;
   bool masked;
-  const int32_t* list;
-  const int32_t* minpos;
+  const int32_t* list;  // off-diagonal list in global memory
+  uint16_t* offw;       // LDS window of the off-diagonal list
+  const uint16_t* ownl; // LDS list of the visible own-segment blocks
+  int ent;              // the next entry's LDS word, read ahead (per lane, all lanes equal)
 
-  __device__ __forceinline__ bool next_block() {
-    while (n < n_total) {
-      const int m = n++;
-      if (mode == 0) {
-        j = m;
-        masked = (j == i);
-        return true;
+  // Load off-diagonal entries [w0, w0 + kOffWindow) into LDS (all threads; barrier after).
+  __device__ __forceinline__ void fill(int w0, int tid, int nt) {
+    const int n = min(n_off - w0, kOffWindow);
+    for (int e = tid; e < n; e += nt)
+      offw[e] = static_cast<uint16_t>(min(max(list[w0 + e], 0), seg_first - 1));
+    win = w0;
+  }
+  __device__ __forceinline__ int read_entry(int k) const {
+    return k < n_off ? offw[k - win] : static_cast<int>(ownl[k - n_off]);
+  }
+  __device__ __forceinline__ void start(int tid, int nt) {
+    m = 0;
+    half = -1;
+    if (mode != 0) {
+      if (win != 0) {  // a long list left a later window in LDS
+        __syncthreads();
+        fill(0, tid, nt);
+        __syncthreads();
       }
-      if (m < n_off) {
-        j = __builtin_amdgcn_readfirstlane(min(max(list[m], 0), seg_first - 1));
-        masked = false;
-        return true;
-      }
-      j = seg_first + (m - n_off);
-      if (mode == 2) {
-        if (j > i) {  // identity order: blocks past the diagonal hold only future keys
-          n = n_total;
-          return false;
-        }
-        masked = (j == i);
-        return true;
-      }
-      if (minpos && __builtin_amdgcn_readfirstlane(minpos[j]) > last_row)
-        continue;  // no key of this block is visible
-      masked = true;
+      if (n_off + n_own > 0) ent = read_entry(0);
+    }
+  }
+  __device__ __forceinline__ bool next_block(int tid, int nt) {
+    if (mode == 0) {
+      if (m > i) return false;
+      j = m;
+      m = __builtin_amdgcn_readfirstlane(m + 1);
+      masked = (j == i);
       return true;
     }
-    return false;
+    if (m >= n_off + n_own) return false;
+    const int e = __builtin_amdgcn_readfirstlane(ent);
+    m = __builtin_amdgcn_readfirstlane(m + 1);
+    if (m < n_off && m == win + kOffWindow) {  // every wave is here, past its reads of the window
+      fill(m, tid, nt);
+      __syncthreads();
+    }
+    if (m < n_off + n_own) ent = read_entry(m);
+    j = e & 0x7fff;
+    masked = (e >> 15) != 0;
+    return true;
   }
   // Advance to the next stage; false when the list is exhausted.
-  __device__ __forceinline__ bool next() {
+  __device__ __forceinline__ bool next(int tid, int nt) {
     if (half >= 0 && half + 1 < halves) {
       ++half;
       return true;
     }
     half = 0;
-    return next_block();
+    return next_block(tid, nt);
   }
 };
 
@@ -248,19 +272,18 @@ __device__ __forceinline__ f32x16 mask_init(const int32_t* Ps, int key0, int kt,
 
 // Row state of one wave across the stages of a pass (log2 units).
 struct RowState {
-  float mref;     // fixed reference subtracted before exp2 (-inf until the row has seen a key)
+  float mref;     // fixed reference subtracted before exp2 (-inf until the first stage)
   float lsum;     // this lane's half of the row's sum of exp2
   float mseen;    // exact row max (max-only pass)
-  bool need_ref;  // some row of the wave has no reference yet (wave-uniform)
 };
 
 // One stage (64 keys) for one wave.  S^T = K Q^T for the two 32-key halves as two independent MFMA
 // chains (masked keys enter as -inf through the accumulators' initial values); then, half by half,
-// exp2 against the fixed reference and O^T += V^T P^T, so that the exp2 work of one half overlaps
-// the matrix work of the other.  No running max: the reference is the first finite stage max of
-// the row, and an overflow of the row sum is caught after the pass (the row max is then found by a
-// max-only pass and the pass is repeated).
-template <int D, int BS, int MODE, bool MAXONLY>
+// exp2 against the fixed reference and O^T += V^T P^T, so that the exp2 work of one half can
+// overlap the matrix work of the other.  There is no running max: the first stage of a pass sets
+// each row's reference to its max over that stage (0 for a row that sees no key of it), and a row
+// sum outside [2^-60, 2^64] after the pass sends the workgroup through the exact-max fallback.
+template <int D, int BS, int MODE, bool FIRST, bool MAXONLY>
 __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vs,
                                            const int32_t* Ps, Stage st, int lane, int t,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NKS],
@@ -295,26 +318,20 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
       s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
     }
   }
-  if constexpr (MAXONLY) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    rs.mseen = fmaxf(rs.mseen, pair_max(mx) * a.c);
-    return;
-  }
-  if (rs.need_ref) {  // wave-uniform; normally only the first stage of a pass
+  if constexpr (MAXONLY || FIRST) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
     mx = pair_max(mx) * a.c;
-    rs.mref = (rs.mref == -INFINITY) ? mx : rs.mref;   // such a row's accumulator is still zero
-    rs.need_ref = __builtin_amdgcn_ballot_w64(rs.mref == -INFINITY) != 0;
+    if constexpr (MAXONLY) {
+      rs.mseen = fmaxf(rs.mseen, mx);
+      return;
+    }
+    if (rs.mref == -INFINITY) rs.mref = (mx == -INFINITY) ? 0.f : mx;
   }
-  const float nm = (rs.mref == -INFINITY) ? 0.f : -rs.mref;
+  const float nm = -rs.mref;
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt) {
     bf16x8 pb[2];
@@ -344,9 +361,9 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
   }
 }
 
-// One pass over the visited key blocks: two LDS stages, unrolled so that each stage's LDS offsets
-// are compile-time constants.  Each stage's loads are issued one stage ahead; the wait + barrier at
-// the top of a stage both lands the stage and frees the other buffer for the next loads.
+// One pass over the visited key blocks through two LDS stage buffers.  Each stage's loads are
+// issued one stage ahead; the wait + barrier at the top of a stage both lands that stage and frees
+// the other buffer for the next loads.  The first stage is peeled (it sets the references).
 template <int D, int BS, int MODE, bool MAXONLY>
 __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, u32x4 rk, u32x4 rv,
                                           u32x4 rp, uint16_t* Ks0, uint16_t* Ks1, uint16_t* Vs0,
@@ -354,29 +371,38 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, u32x
                                           int lane, int t, const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
   using C = Cfg<D, BS>;
-  it.n = 0;
-  it.half = -1;
+  const int tid = threadIdx.x;
+  it.start(tid, C::NT);
   Stage cur, nxt;
-  bool have = it.next();
-  cur.key0 = it.j * BS + it.half * C::SK;
-  cur.masked = it.masked;
-  if (have) issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
-  while (have) {
+  bool have = it.next(tid, C::NT);
+  if (have) {
+    cur.key0 = it.j * BS + it.half * C::SK;
+    cur.masked = it.masked;
+    issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // stage 0 landed; stage 1 no longer read
-    const bool more = it.next();
+    __syncthreads();
+    bool more = it.next(tid, C::NT);
     nxt.key0 = it.j * BS + it.half * C::SK;
     nxt.masked = it.masked;
     if (more) issue_stage<D, BS>(a, rk, rv, rp, nxt, Ks1, Vs1, Ps1, w, lane);
-    attn_stage<D, BS, MODE, MAXONLY>(a, Ks0, Vs0, Ps0, cur, lane, t, qf, oacc, rs);
-    if (!more) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // stage 1 landed; stage 0 no longer read
-    have = it.next();
-    cur.key0 = it.j * BS + it.half * C::SK;
-    cur.masked = it.masked;
-    if (have) issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
-    attn_stage<D, BS, MODE, MAXONLY>(a, Ks1, Vs1, Ps1, nxt, lane, t, qf, oacc, rs);
+    attn_stage<D, BS, MODE, !MAXONLY, MAXONLY>(a, Ks0, Vs0, Ps0, cur, lane, t, qf, oacc, rs);
+    while (more) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // stage in buffer 1 landed; buffer 0 no longer read
+      have = it.next(tid, C::NT);
+      cur.key0 = it.j * BS + it.half * C::SK;
+      cur.masked = it.masked;
+      if (have) issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
+      attn_stage<D, BS, MODE, false, MAXONLY>(a, Ks1, Vs1, Ps1, nxt, lane, t, qf, oacc, rs);
+      if (!have) break;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // stage in buffer 0 landed; buffer 1 no longer read
+      more = it.next(tid, C::NT);
+      nxt.key0 = it.j * BS + it.half * C::SK;
+      nxt.masked = it.masked;
+      if (more) issue_stage<D, BS>(a, rk, rv, rp, nxt, Ks1, Vs1, Ps1, w, lane);
+      attn_stage<D, BS, MODE, false, MAXONLY>(a, Ks0, Vs0, Ps0, cur, lane, t, qf, oacc, rs);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // every wave is done with both buffers before another pass refills them
@@ -389,6 +415,9 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::KTILE + 2 * C::VTILE];
   __shared__ __attribute__((aligned(16))) int32_t Ps0[C::SK];
   __shared__ __attribute__((aligned(16))) int32_t Ps1[C::SK];
+  __shared__ uint16_t offw[kOffWindow];
+  __shared__ uint16_t ownl[kOwnMax];
+  __shared__ int own_count;
   uint16_t* const Ks0 = smem + a.tile_off[0];
   uint16_t* const Ks1 = smem + a.tile_off[1];
   uint16_t* const Vs0 = smem + a.tile_off[2];
@@ -424,22 +453,48 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
       make_rsrc(a.perm ? a.perm + kv_head : nullptr, a.perm ? static_cast<uint32_t>(a.N) * 4 : 0u);
 
   StageIter it;
-  it.i = i;
   it.mode = MODE;
   it.halves = C::HALVES;
+  it.i = i;
   it.seg_first = (i / a.bps) * a.bps;
-  it.last_row = i * BS + BS - 1;
-  it.minpos = a.minpos ? a.minpos + kv_head / BS : nullptr;
   it.n_off = 0;
+  it.n_own = 0;
+  it.win = 0;
   it.list = nullptr;
+  it.offw = offw;
+  it.ownl = ownl;
   it.j = 0;
   it.masked = false;
+  it.ent = 0;
   if (MODE != 0) {
     const size_t row = (static_cast<size_t>(b) * a.Hq + g) * a.nb + i;
     it.n_off = min(max(a.counts[row], 0), it.seg_first);
     it.list = a.idx + row * a.max_off;
+    it.fill(0, tid, C::NT);
+    // Visible own-segment blocks, compacted by wave 0.  Permuted order: a block is skipped when
+    // its smallest original position is after the query block's last row; every visited block
+    // is masked per key.  Identity order: blocks up to the diagonal, only the diagonal masked.
+    if (w == 0) {
+      const int last_row = i * BS + BS - 1;
+      const int32_t* mp = a.minpos ? a.minpos + kv_head / BS + it.seg_first : nullptr;
+      int n = 0;
+      for (int o0 = 0; o0 < a.bps; o0 += 64) {
+        const int o = o0 + lane;
+        const int jj = it.seg_first + o;
+        bool vis = false;
+        if (o < a.bps) vis = (MODE == 2) ? (jj <= i) : (mp == nullptr || mp[o] <= last_row);
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
+        const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+        if (vis)
+          ownl[n + before] = static_cast<uint16_t>(jj | ((MODE == 1 || jj == i) ? 0x8000 : 0));
+        n += __builtin_popcountll(bal);
+      }
+      if (lane == 0) own_count = n;
+    }
+    __syncthreads();
+    it.n_own = own_count;
   }
-  it.n_total = (MODE == 0) ? (i + 1) : (it.n_off + a.bps);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds q[t][ks*16 + hl*8 .. +8]
   bf16x8 qf[C::NKS];
@@ -451,19 +506,19 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   f32x16 oacc[C::NMT];
 #pragma unroll
   for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
-  RowState rs{-INFINITY, 0.f, -INFINITY, true};
+  RowState rs{-INFINITY, 0.f, -INFINITY};
   attn_pass<D, BS, MODE, false>(a, it, rk, rv, rp, Ks0, Ks1, Vs0, Vs1, Ps0, Ps1, w, lane, t, qf,
                                 oacc, rs);
-  // A row whose sum left [0, 2^64] (an exp2 overflow, or scores far above the reference) is
-  // recomputed: first its exact maximum, then the pass against that maximum.
-  if (__syncthreads_or(!(pair_sum(rs.lsum) <= 0x1p64f) ? 1 : 0)) {
+  // A row whose sum left [2^-60, 2^64] (scores far above or below its reference) is recomputed:
+  // first its exact maximum, then the pass against that maximum.
+  const float l0 = pair_sum(rs.lsum);
+  if (__syncthreads_or(!(l0 >= 0x1p-60f && l0 <= 0x1p64f) ? 1 : 0)) {
     attn_pass<D, BS, MODE, true>(a, it, rk, rv, rp, Ks0, Ks1, Vs0, Vs1, Ps0, Ps1, w, lane, t, qf,
                                  oacc, rs);
 #pragma unroll
     for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
     rs.mref = rs.mseen;
     rs.lsum = 0.f;
-    rs.need_ref = false;
     attn_pass<D, BS, MODE, false>(a, it, rk, rv, rp, Ks0, Ks1, Vs0, Vs1, Ps0, Ps1, w, lane, t, qf,
                                   oacc, rs);
   }

@@ -214,3 +214,38 @@ def test_dominant_late_key_pbs(permuted):
                       dev(counts), dev(idx), scale)
     check_attn(o.float().cpu().numpy(), oo, f"dominant key PBS permuted={permuted}")
     assert np.abs(lse.cpu().numpy() - ol).max() < 1e-3
+
+
+@pytest.mark.parametrize("dominant", [False, True])
+def test_long_lists_refill_the_window(dominant):
+    """Off-diagonal lists longer than the attention kernel's LDS window (1792 entries): N=131072,
+    Bs=64, S=256, keep ratio 1, so the last query blocks list up to 2044 blocks.  With keep 1 the
+    result equals dense causal attention.  With a dominant key in block 1000 the rows after it
+    overflow the first-stage reference, and the fallback passes start over from the first
+    window."""
+    say(f"long lists, dominant={dominant}")
+    N, d, Bs, S = 131072, 64, 64, 256
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    v = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    if dominant:
+        u = rng.standard_normal(d)
+        u /= np.linalg.norm(u)
+        q += np.float32(3.0) * u.astype(np.float32)
+        k[0, 0, 1000 * Bs + 17] = (300.0 * u).astype(np.float32)
+    q, k, v = (pbs_synth.f32_to_bf16_bits(x) for x in (q, k, v))
+    scale = oracle.default_scale(d)
+    nb = N // Bs
+    blocks = [nb - 1, nb - 2, nb - 5, nb - 64, 1500, 1000, 999, 3]
+    od, ol = oracle.dense_causal(q, k, v, block=Bs, scale=scale, qblocks=[(0, 0, i) for i in blocks])
+    bufs = P.prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), block=Bs, segment=S, keep=1.0, scale=scale)
+    torch.cuda.synchronize()
+    counts = bufs.counts.cpu().numpy()
+    assert counts[0, 0, nb - 1] == (nb - 1) // (S // Bs) * (S // Bs) > 1792
+    og = bufs.o.float().cpu().numpy()[0, 0]
+    lg = bufs.lse.cpu().numpy()[0, 0]
+    got = np.stack([og[i * Bs:(i + 1) * Bs] for i in blocks])
+    gl = np.stack([lg[i * Bs:(i + 1) * Bs] for i in blocks])
+    check_attn(got, od, f"long lists dominant={dominant}")
+    assert np.abs(gl - ol).max() < 1e-3

@@ -12,11 +12,14 @@
 // Kernels:
 //  * pool: float32 mean of every block of Bs rows (queries; keys too when the caller has no
 //    pooled keys from pbs_permute).  HBM-bound, one workgroup per (head, block).
-//  * select: one workgroup per (query head, query block).  Logits are plain fp32 dot products
-//    (n <= 8192 candidates x d), the softmax uses block-wide reductions, the ranking is a
-//    bitonic sort of 64-bit keys in LDS, the coverage prefix is one strictly sequential fp32
-//    sum (so it is bit-identical to any other sequential fp32 sum of the same values), and the
-//    kept blocks are compacted in ascending order with a workgroup prefix scan.
+//  * select: one workgroup per (query block, up to 4 query heads of one KV head), 256 threads per
+//    head.  Logits are plain fp32 dot products (n <= 8192 candidates x d), the softmax uses
+//    per-row reductions, the ranking is a bitonic sort of next_pow2(n) 64-bit keys in LDS, the
+//    coverage prefix is one strictly sequential fp32 sum (so it is bit-identical to any other
+//    sequential fp32 sum of the same values), and the kept blocks are compacted in ascending
+//    order with a per-row prefix scan.
+#include <cmath>
+
 #include "pbs_device.h"
 #include "pbs_internal.h"
 
@@ -67,148 +70,213 @@ struct SelArgs {
   float* P;            // [B*Hq, nb, nb] or null
   int32_t* counts;     // [B*Hq, nb]
   int32_t* idx;        // [B*Hq, nb, max_off]
-  int Hq, Hkv, G, nb, bps, max_off, n2;
+  int Hq, Hkv, G, hpw, nb, bps, max_off, n2max;
   int mode;            // 0 keep ratio, 1 coverage
   int p_in;            // read P instead of computing it
   double param;
+  float tau_f;         // least float f with (double)f >= param (coverage)
   float scale;
 };
 
-constexpr int kSelThreads = 256;
+constexpr int kSub = 256;   // threads per row (one row = one query head of the workgroup)
 
-__device__ __forceinline__ float block_reduce_max(float v, float* red) {
+// Sum / max over the kSub threads of one row (sub = the row's index in the workgroup).  Every thread
+// of the workgroup calls these together.
+__device__ __forceinline__ float row_reduce_max(float v, float* red, int sub, int st) {
   v = wave_max(v);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
-  if (lane == 0) red[w] = v;
+  if ((st & 63) == 0) red[sub * 4 + (st >> 6)] = v;
   __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < kSelThreads / 64; ++i) r = fmaxf(r, red[i]);
-  return r;
+  return fmaxf(fmaxf(red[sub * 4], red[sub * 4 + 1]), fmaxf(red[sub * 4 + 2], red[sub * 4 + 3]));
 }
-__device__ __forceinline__ float block_reduce_sum(float v, float* red) {
+__device__ __forceinline__ float row_reduce_sum(float v, float* red, int sub, int st) {
   v = wave_sum(v);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
-  if (lane == 0) red[w] = v;
+  if ((st & 63) == 0) red[sub * 4 + (st >> 6)] = v;
   __syncthreads();
-  float r = 0.f;
-  for (int i = 0; i < kSelThreads / 64; ++i) r += red[i];
-  return r;
+  return (red[sub * 4] + red[sub * 4 + 1]) + (red[sub * 4 + 2] + red[sub * 4 + 3]);
 }
 
+// Ascending bitonic sort of n2 (power of two) 64-bit keys by the kSub threads of one row; every
+// thread of the workgroup takes part in the barriers.
+__device__ __forceinline__ void bitonic_sort_row(uint64_t* keys, int n2, int st) {
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int t = st; t < (n2 >> 1); t += kSub) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = ((lo & size) == 0);
+        const uint64_t x = keys[lo], y = keys[hi];
+        if ((x > y) == up) {
+          keys[lo] = y;
+          keys[hi] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// One workgroup per (query block, group of hpw query heads sharing a KV head); kSub threads per
+// head.  The heads of a group have the same candidates, so their logits read each pooled key once
+// (through the cache) and their sorts run side by side.
 template <int D>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
+__global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);                 // n2
-  float* Ps = reinterpret_cast<float*>(keys + a.n2);                   // n2
-  int32_t* flag = reinterpret_cast<int32_t*>(Ps + a.n2);               // n2
-  __shared__ float qs[D];
-  __shared__ float red[kSelThreads / 64];
-  __shared__ int32_t scan[kSelThreads];
-  __shared__ int32_t kept;
+  __shared__ float red[4 * 4];
+  __shared__ int32_t scan[4 * kSub];
+  __shared__ int32_t kept[4];
 
   const int tid = threadIdx.x;
+  const int sub = tid / kSub, st = tid - sub * kSub;
   const int i = blockIdx.x;
-  const int bg = blockIdx.y;                  // b * Hq + g
-  const int b = bg / a.Hq, g = bg - b * a.Hq;
+  const int groups = a.Hq / a.hpw;
+  const int b = blockIdx.y / groups;
+  const int g = (blockIdx.y - b * groups) * a.hpw + sub;   // this row's query head
   const int h = g / a.G;
   const int n = (i / a.bps) * a.bps;          // candidates: blocks of earlier segments
-  const size_t row = static_cast<size_t>(bg) * a.nb + i;
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem) + static_cast<size_t>(sub) * a.n2max;
+  float* Ps = reinterpret_cast<float*>(reinterpret_cast<uint64_t*>(smem) + static_cast<size_t>(a.hpw) * a.n2max) +
+              static_cast<size_t>(sub) * a.n2max;
+  int32_t* flag = reinterpret_cast<int32_t*>(Ps + static_cast<size_t>(a.hpw - sub) * a.n2max) +
+                  static_cast<size_t>(sub) * a.n2max;
+  const size_t row = (static_cast<size_t>(b) * a.Hq + g) * a.nb + i;
   float* prow = a.P ? a.P + row * a.nb : nullptr;
 
-  if (n == 0) {
-    if (tid == 0) a.counts[row] = 0;
+  if (n == 0) {   // the whole workgroup takes this branch (n depends on the query block only)
+    if (st == 0) a.counts[row] = 0;
     if (prow && !a.p_in)
-      for (int j = tid; j < a.nb; j += kSelThreads) prow[j] = 0.f;
+      for (int j = st; j < a.nb; j += kSub) prow[j] = 0.f;
     return;
   }
 
   if (a.p_in) {
-    for (int j = tid; j < n; j += kSelThreads) Ps[j] = prow[j];
+    for (int j = st; j < n; j += kSub) Ps[j] = prow[j];
     __syncthreads();
   } else {
-    for (int dd = tid; dd < D; dd += kSelThreads) qs[dd] = a.qbar[row * D + dd];
-    __syncthreads();
-    const float* kb = a.kbar + (static_cast<size_t>(b) * a.Hkv + h) * a.nb * D;
-    float lmax = -INFINITY;
-    for (int j = tid; j < n; j += kSelThreads) {
-      const float4* kr = reinterpret_cast<const float4*>(kb + static_cast<size_t>(j) * D);
-      float acc = 0.f;
-#pragma unroll 8
-      for (int q4 = 0; q4 < D / 4; ++q4) {
-        const float4 kv = kr[q4];
-        acc += qs[4 * q4] * kv.x + qs[4 * q4 + 1] * kv.y + qs[4 * q4 + 2] * kv.z + qs[4 * q4 + 3] * kv.w;
+    // Logits of all hpw rows: TPC threads per candidate, each with an 8-wide slice of the head
+    // dimension (the rows' pooled queries in registers), so a wave reads whole pooled-key rows
+    // contiguously; the slices are summed across the TPC lanes.
+    constexpr int TPC = D / 8;
+    const int nt = kSub * a.hpw;
+    const int cpi = nt / TPC;                   // candidates per sweep
+    const int sl = tid % TPC, cj = tid / TPC;
+    const size_t row0 = (static_cast<size_t>(b) * a.Hq + (g - sub)) * a.nb + i;   // first row
+    float qv[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r < a.hpw) {
+        const float4* qp = reinterpret_cast<const float4*>(a.qbar + (row0 + static_cast<size_t>(r) * a.nb) * D + sl * 8);
+        const float4 x0 = qp[0], x1 = qp[1];
+        qv[r][0] = x0.x; qv[r][1] = x0.y; qv[r][2] = x0.z; qv[r][3] = x0.w;
+        qv[r][4] = x1.x; qv[r][5] = x1.y; qv[r][6] = x1.z; qv[r][7] = x1.w;
       }
-      const float lg = acc * a.scale;
-      Ps[j] = lg;
-      lmax = fmaxf(lmax, lg);
     }
-    const float mx = block_reduce_max(lmax, red);
+    const float* kb = a.kbar + (static_cast<size_t>(b) * a.Hkv + h) * a.nb * D;
+    float* Pall = reinterpret_cast<float*>(reinterpret_cast<uint64_t*>(smem) + static_cast<size_t>(a.hpw) * a.n2max);
+#pragma unroll 2
+    for (int j0 = 0; j0 < n; j0 += cpi) {
+      const int j = j0 + cj;
+      float4 k0 = make_float4(0.f, 0.f, 0.f, 0.f), k1 = k0;
+      if (j < n) {
+        const float4* kp = reinterpret_cast<const float4*>(kb + static_cast<size_t>(j) * D + sl * 8);
+        k0 = kp[0];
+        k1 = kp[1];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < a.hpw) {
+          float acc = qv[r][0] * k0.x + qv[r][1] * k0.y + qv[r][2] * k0.z + qv[r][3] * k0.w +
+                      qv[r][4] * k1.x + qv[r][5] * k1.y + qv[r][6] * k1.z + qv[r][7] * k1.w;
+#pragma unroll
+          for (int o = 1; o < TPC; o <<= 1) acc += __shfl_xor(acc, o);
+          if (sl == 0 && j < n) Pall[static_cast<size_t>(r) * a.n2max + j] = acc * a.scale;
+        }
+      }
+    }
+    __syncthreads();
+    float lmax = -INFINITY;
+    for (int j = st; j < n; j += kSub) lmax = fmaxf(lmax, Ps[j]);
+    const float mx = row_reduce_max(lmax, red, sub, st);
     float lsum = 0.f;
-    for (int j = tid; j < n; j += kSelThreads) {
+    for (int j = st; j < n; j += kSub) {
       const float e = __expf(Ps[j] - mx);
       Ps[j] = e;
       lsum += e;
     }
-    const float tot = block_reduce_sum(lsum, red);
+    const float tot = row_reduce_sum(lsum, red, sub, st);
     const float inv = 1.f / tot;
-    for (int j = tid; j < n; j += kSelThreads) {
+    for (int j = st; j < n; j += kSub) {
       const float p = Ps[j] * inv;
       Ps[j] = p;
       if (prow) prow[j] = p;
     }
     if (prow)
-      for (int j = n + tid; j < a.nb; j += kSelThreads) prow[j] = 0.f;
+      for (int j = n + st; j < a.nb; j += kSub) prow[j] = 0.f;
     __syncthreads();
   }
 
-  for (int p = tid; p < a.n2; p += kSelThreads)
+  for (int p = st; p < n2; p += kSub)
     keys[p] = (p < n) ? desc_sort_key(Ps[p], static_cast<uint32_t>(p)) : ~0ull;
-  bitonic_sort_lds(keys, a.n2);
+  bitonic_sort_row(keys, n2, st);
 
-  if (tid == 0) {
-    int kk;
-    if (a.mode == 0) {
-      kk = static_cast<int>(floor(a.param * static_cast<double>(n)));
-      kk = max(1, min(kk, n));
-    } else {
-      kk = n;
-      float c = 0.f;
-      for (int m = 0; m < n; ++m) {
-        c = __fadd_rn(c, Ps[static_cast<int>(keys[m] & 0xffffffffull)]);
-        if (static_cast<double>(c) >= a.param) {
-          kk = m + 1;
-          break;
-        }
+  if (a.mode == 0) {
+    if (st == 0) {
+      int kk = static_cast<int>(floor(a.param * static_cast<double>(n)));
+      kept[sub] = max(1, min(kk, n));
+    }
+  } else if (st < 64) {
+    // Shortest prefix of the ranking whose running float32 sum reaches tau: the sum is strictly
+    // sequential (one rounding per element, in ranking order); the first wave of the row gathers
+    // 64 ranked values at a time and adds them one by one from the lanes.  (double)c >= tau is
+    // tested as c >= tf, tf the least float with (double)tf >= tau.
+    const float tf = a.tau_f;
+    float c = 0.f;
+    int kk = n;
+    for (int m0 = 0; m0 < n; m0 += 64) {
+      const int m = m0 + st;
+      const float pv = (m < n) ? Ps[static_cast<int>(keys[m] & 0xffffffffull)] : 0.f;
+      const int cnt = min(64, n - m0);
+      int e = 0;
+      for (; e < cnt; ++e) {
+        c = __fadd_rn(c, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pv), e)));
+        if (c >= tf) break;
+      }
+      if (e < cnt) {
+        kk = m0 + e + 1;
+        break;
       }
     }
-    kept = kk;
+    if (st == 0) kept[sub] = kk;
   }
-  for (int j = tid; j < n; j += kSelThreads) flag[j] = 0;
+  for (int j = st; j < n; j += kSub) flag[j] = 0;
   __syncthreads();
-  const int kk = kept;
-  for (int m = tid; m < kk; m += kSelThreads) flag[static_cast<int>(keys[m] & 0xffffffffull)] = 1;
+  const int kk = kept[sub];
+  for (int m = st; m < kk; m += kSub) flag[static_cast<int>(keys[m] & 0xffffffffull)] = 1;
   __syncthreads();
 
-  // ascending compaction: thread tid owns candidates [tid*per, (tid+1)*per)
-  const int per = (n + kSelThreads - 1) / kSelThreads;
-  const int lo = min(tid * per, n), hi = min(lo + per, n);
+  // ascending compaction: thread st of the row owns candidates [st*per, (st+1)*per)
+  const int per = (n + kSub - 1) / kSub;
+  const int lo = min(st * per, n), hi = min(lo + per, n);
   int cnt = 0;
   for (int j = lo; j < hi; ++j) cnt += flag[j];
-  scan[tid] = cnt;
+  int32_t* sc = scan + sub * kSub;
+  sc[st] = cnt;
   __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    const int v = (tid >= off) ? scan[tid - off] : 0;
+  for (int off = 1; off < kSub; off <<= 1) {
+    const int v = (st >= off) ? sc[st - off] : 0;
     __syncthreads();
-    scan[tid] += v;
+    sc[st] += v;
     __syncthreads();
   }
-  int pos = scan[tid] - cnt;
+  int pos = sc[st] - cnt;
   int32_t* out = a.idx + row * a.max_off;
   for (int j = lo; j < hi; ++j)
     if (flag[j]) out[pos++] = j;
-  if (tid == 0) a.counts[row] = kk;
+  if (st == 0) a.counts[row] = kk;
 }
 
 template <int D, int BS>
@@ -260,14 +328,22 @@ hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t*
   sa.Hq = d.Hq; sa.Hkv = d.Hkv; sa.G = d.G; sa.nb = d.nb; sa.bps = d.bps; sa.max_off = d.max_off;
   int n2 = 1;
   while (n2 < d.max_off) n2 <<= 1;
-  sa.n2 = n2;
+  sa.n2max = n2;
+  // Heads per workgroup: the largest of 4, 2, 1 that divides the group size and keeps the
+  // workgroup's LDS within 64 KiB (two workgroups per CU).
+  const size_t per_row = static_cast<size_t>(n2) * (sizeof(uint64_t) + sizeof(float) + sizeof(int32_t));
+  int hpw = 4;
+  while (hpw > 1 && (d.G % hpw != 0 || hpw * per_row > 65536)) hpw >>= 1;
+  sa.hpw = hpw;
   sa.mode = mode; sa.p_in = scores_in ? 1 : 0; sa.param = param; sa.scale = scale;
-  const size_t shmem = static_cast<size_t>(n2) * (sizeof(uint64_t) + sizeof(float) + sizeof(int32_t));
+  sa.tau_f = static_cast<float>(param);
+  if (static_cast<double>(sa.tau_f) < param) sa.tau_f = std::nextafter(sa.tau_f, INFINITY);
+  const size_t shmem = hpw * per_row;
   auto kern = d.d == 128 ? select_kernel<128> : select_kernel<64>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
   if (e != hipSuccess) return e;
-  return launch(kern, dim3(d.nb, d.B * d.Hq), dim3(kSelThreads), shmem, stream, sa);
+  return launch(kern, dim3(d.nb, d.B * (d.Hq / hpw)), dim3(kSub * hpw), shmem, stream, sa);
 }
 
 }  // namespace pbs

@@ -344,6 +344,79 @@ def dense_causal(q, k, v, *, block: int, scale: float, qblocks=None):
     return attention(q, k, v, block=block, segment=N, scale=scale, dense=True, qblocks=qblocks)
 
 
+# --------------------------------------------------------------------------- density, coverage
+
+def attention_coverage(q, k, *, block: int, segment: int, scale: float,
+                       perm: Optional[np.ndarray] = None, counts: Optional[np.ndarray] = None,
+                       idx: Optional[np.ndarray] = None,
+                       qblocks: Optional[Iterable[Tuple[int, int, int]]] = None) -> np.ndarray:
+    """Attention coverage of each query row: the part of its dense causal attention that the
+    computed key set A(t) holds, sum over j in A(t) of softmax_{j' <= t}(scale <q_t, k_j'>)_j.
+
+    [SS Fig. 2]: coverage is the total attention of the selected blocks; [SS Fig. 4] and [GS
+    Ergebnisse] compare how many blocks the permuted and the natural order need for a given
+    coverage.  ``perm=None`` is the natural (unpermuted) order.  ``qblocks`` as in
+    ``attention``; returns ``[len, Bs]`` or ``[B, Hq, N]`` (float64)."""
+    B, Hq, Hkv, N, d, G = _check_shape(q.shape, k.shape, block, segment)
+    nb = N // block
+    sampled = qblocks is not None
+    todo = list(qblocks) if sampled else [(b, g, i) for b in range(B) for g in range(Hq) for i in range(nb)]
+    out = np.zeros((len(todo), block)) if sampled else np.zeros((B, Hq, N))
+    cache = {}
+    for n_out, (b, g, i) in enumerate(todo):
+        h = g // G
+        if (b, h) not in cache:
+            cache.clear()
+            cache[(b, h)] = bf16_to_f64(k[b, h])
+        Kf = cache[(b, h)]
+        t = np.arange(i * block, (i + 1) * block)
+        Qb = bf16_to_f64(q[b, g, i * block:(i + 1) * block])
+        Z = scale * (Qb @ Kf[:t[-1] + 1].T)                         # every key up to the block
+        Z = np.where(np.arange(t[-1] + 1)[None, :] <= t[:, None], Z, -np.inf)
+        E = np.exp(Z - Z.max(axis=1, keepdims=True))
+        Pd = E / E.sum(axis=1, keepdims=True)                       # dense causal softmax
+        sel = [int(j) for j in idx[b, g, i, :counts[b, g, i]]] if counts is not None else []
+        keys = visible_keys(int(t[-1]), block=block, segment=segment,
+                            perm_row=None if perm is None else perm[b, h], sel_blocks=sel, dense=False)
+        cov = Pd[:, keys].sum(axis=1)                               # keys > t carry no mass
+        if sampled:
+            out[n_out] = cov
+        else:
+            out[b, g, t] = cov
+    return out
+
+
+def block_density(counts: np.ndarray, *, block: int, segment: int, N: int,
+                  perm: Optional[np.ndarray] = None) -> dict:
+    """Block counts of one selection ([SS Fig. 4]: block-level density).
+
+    ``selected`` = kept earlier-segment blocks, ``candidates`` = earlier-segment blocks
+    offered; ``computed`` adds the own-segment blocks the attention visits (natural order:
+    the blocks up to the diagonal; permuted order: every block of the segment holding a key
+    at or before the query block's last row), ``dense`` counts the blocks of dense causal
+    attention.  ``counts`` is ``[B, Hq, nb]``; ``perm`` ``[B, Hkv, N]`` or None."""
+    B, Hq, nb = counts.shape
+    bps = segment // block
+    selected = int(counts.sum())
+    candidates = B * Hq * sum((i // bps) * bps for i in range(nb))
+    own = 0
+    for b in range(B):
+        for g in range(Hq):
+            for i in range(nb):
+                s0 = (i // bps) * bps
+                if perm is None:
+                    own += i - s0 + 1
+                else:
+                    Hkv = perm.shape[1]
+                    h = g // (Hq // Hkv)
+                    last = (i + 1) * block - 1
+                    for j in range(s0, s0 + bps):
+                        if perm[b, h, j * block:(j + 1) * block].min() <= last:
+                            own += 1
+    dense = B * Hq * nb * (nb + 1) // 2
+    return dict(selected=selected, candidates=candidates, computed=selected + own, dense=dense)
+
+
 # --------------------------------------------------------------------------- whole pipeline
 
 def prefill(q, k, v, *, block: int, segment: int, scale: float, mode: str, param: float):

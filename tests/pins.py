@@ -375,4 +375,81 @@ def pin_segment0_rows_are_dense(O):
     assert np.abs(out["o"][:, :, 8:] - od[:, :, 8:]).max() > 1e-3
 
 
+# ----------------------------------------------------------------------------- density, coverage
+
+def _bf_coverage(Q, K, vis, scale, t):
+    """Dense causal softmax of row t summed over the keys vis marks (brute force)."""
+    p = bf.softmax_over({j: scale * bf.dot(Q[t], K[j]) for j in range(t + 1)})
+    return math.fsum(p[j] for j in p if vis[t][j])
+
+
+def pin_coverage_definitions(O):
+    """[SS Fig. 2] coverage = the dense attention mass held by the computed keys: against brute
+    force (explicit visibility matrix, dense softmax over j <= t), against exp(lse_sparse -
+    lse_dense) from the attention routines, in both key orders; 1 wherever the key set is the
+    whole causal prefix (segment-0 rows, keep ratio 1), below 1 elsewhere at a low ratio."""
+    N, Bs, S, Hq, Hkv = 32, 4, 8, 4, 2
+    G = Hq // Hkv
+    for permuted in (True, False):
+        q, k, v = _tiny(101, Hq=Hq, Hkv=Hkv, N=N, d=8, scale_k=1.7)
+        if permuted:
+            out = O.prefill(q, k, v, block=Bs, segment=S, scale=0.4, mode=O.KEEP, param=0.25)
+            perm, counts, idx, lse = out["perm"], out["counts"], out["idx"], out["lse"]
+        else:
+            P = O.block_probabilities(q, k, block=Bs, segment=S, scale=0.4)
+            counts, idx = O.select_blocks(P, block=Bs, segment=S, mode=O.KEEP, param=0.25)
+            perm = None
+            _, lse = O.attention(q, k, v, block=Bs, segment=S, scale=0.4, counts=counts, idx=idx)
+        cov = O.attention_coverage(q, k, block=Bs, segment=S, scale=0.4, perm=perm, counts=counts, idx=idx)
+        _, lsed = O.dense_causal(q, k, v, block=Bs, scale=0.4)
+        assert np.abs(cov - np.exp(lse - lsed)).max() < 1e-12
+        for g in range(Hq):
+            h = g // G
+            Q, K = bf.mat(q[0, g]), bf.mat(k[0, h])
+            vis = _vis_matrix(N, Bs, S, None if perm is None else perm[0, h], counts[0, g], idx[0, g])
+            for t in (0, 7, 8, 13, 21, 31):
+                assert math.isclose(cov[0, g, t], _bf_coverage(Q, K, vis, 0.4, t), rel_tol=1e-12), (g, t)
+        assert np.abs(cov[:, :, :S] - 1).max() < 1e-12
+        assert cov[:, :, S:].min() < 0.999 and cov.max() <= 1 + 1e-12
+        one = O.select_blocks(O.block_probabilities(q, k if perm is None else O.apply_permutation(k, perm),
+                                                    block=Bs, segment=S, scale=0.4),
+                              block=Bs, segment=S, mode=O.KEEP, param=1.0)
+        cov1 = O.attention_coverage(q, k, block=Bs, segment=S, scale=0.4, perm=perm, counts=one[0], idx=one[1])
+        assert np.abs(cov1 - 1).max() < 1e-12
+
+
+def pin_block_density_handworked(O):
+    """Block counts worked by hand for N=16, Bs=4, S=8 (two segments of two blocks), one head,
+    one kept block per second-segment row: 2 selected of 4 candidates, 10 dense causal blocks.
+    Own-segment blocks: natural order 1+2+1+2; permuted with a segment-1 order whose first
+    permuted block holds keys 12..15 only (invisible to rows 8..11) 1+2+1+2; with a mixed order
+    1+2+2+2 (segment 0 in natural order).  Then the same counts by brute force over the
+    visibility matrix of a random tiny pipeline."""
+    counts = np.array([[[0, 0, 1, 1]]], np.int32)
+    d = O.block_density(counts, block=4, segment=8, N=16)
+    assert d == dict(selected=2, candidates=4, computed=8, dense=10), d
+    seg0 = list(range(8))
+    late = np.array([[seg0 + [12, 13, 14, 15, 8, 9, 10, 11]]], np.int32)
+    mixed = np.array([[seg0 + [15, 8, 13, 10, 12, 9, 14, 11]]], np.int32)
+    assert O.block_density(counts, block=4, segment=8, N=16, perm=late)["computed"] == 8
+    assert O.block_density(counts, block=4, segment=8, N=16, perm=mixed)["computed"] == 9
+    N, Bs, S, Hq, Hkv = 32, 4, 8, 4, 2
+    q, k, v, out = _tiny_pbs(O, 111, param=0.34)
+    dd = O.block_density(out["counts"], block=Bs, segment=S, N=N, perm=out["perm"])
+    G, nb = Hq // Hkv, N // Bs
+    computed = 0
+    for g in range(Hq):
+        h = g // G
+        perm = out["perm"][0, h]
+        vis = _vis_matrix(N, Bs, S, perm, out["counts"][0, g], out["idx"][0, g])
+        for i in range(nb):
+            rows = range(i * Bs, (i + 1) * Bs)
+            for p in range(nb):   # permuted key block p holds original keys perm[p*Bs:(p+1)*Bs]
+                if any(vis[t][int(perm[s])] for t in rows for s in range(p * Bs, (p + 1) * Bs)):
+                    computed += 1
+    assert dd["computed"] == computed, (dd, computed)
+    assert dd["selected"] == int(out["counts"].sum())
+    assert dd["dense"] == Hq * nb * (nb + 1) // 2
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

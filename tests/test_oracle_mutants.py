@@ -33,9 +33,15 @@ MUTANTS = {
                          "Z = np.where(keys[None, :] < t[:, None], Z, -np.inf)"),
     "attn_no_scale": ("Z = scale * (Qb @ Kf[keys].T)", "Z = (Qb @ Kf[keys].T)"),
     "attn_values_are_keys": ("ob = (E @ Vf[keys]) / l", "ob = (E @ Kf[keys]) / l"),
-    "attn_gqa_modulo": ("    for n_out, (b, g, i) in enumerate(todo):\n        h = g // G",
-                        "    for n_out, (b, g, i) in enumerate(todo):\n        h = g % Hkv"),
+    "attn_gqa_modulo": ("        h = g // G\n        if (b, h) not in cache:\n            cache.clear()\n            cache[(b, h)] = (bf16_to_f64(k[b, h])",
+                        "        h = g % Hkv\n        if (b, h) not in cache:\n            cache.clear()\n            cache[(b, h)] = (bf16_to_f64(k[b, h])"),
     "attn_lse_log2": ("lb = (m + np.log(l))[:, 0]", "lb = (m + np.log2(l))[:, 0]"),
+    "coverage_sparse_softmax": ("cov = Pd[:, keys].sum(axis=1)",
+                                "cov = Pd[:, keys].sum(axis=1) / Pd[:, keys].sum(axis=1)"),
+    "coverage_no_causal_mask": ("Z = np.where(np.arange(t[-1] + 1)[None, :] <= t[:, None], Z, -np.inf)", "Z = Z"),
+    "density_own_off_by_one": ("own += i - s0 + 1", "own += i - s0"),
+    "density_perm_max_position": ("perm[b, h, j * block:(j + 1) * block].min() <= last",
+                                  "perm[b, h, j * block:(j + 1) * block].max() <= last"),
 }
 
 

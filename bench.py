@@ -105,6 +105,101 @@ def cpu_oracle_baseline(w, inp, scale, param):
     }
 
 
+def density_main(args):
+    """Block density against attention coverage, permuted vs natural key order (the pages'
+    Fig. 4 comparison).  For each coverage threshold tau of the block selection, both orders
+    run on the GPU: selection, then attention with its log-normaliser; the true attention
+    coverage of a row is exp(lse_sparse - lse_dense), lse_dense from the dense causal pass.
+    The selected-block counts at equal mean coverage (interpolated in tau) give the relative
+    sparsity improvement delta = 1 - selected_permuted / selected_natural."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_pbs_amd as P
+    import pbs_synth
+
+    names = args.density.split(",")
+    taus = [float(x) for x in args.taus.split(",")]
+    target = args.coverage_target
+    for name in names:
+        w = pbs_synth.WORKLOADS[name]
+        if args.k_boost is not None:
+            w = w.scaled(k_boost=args.k_boost)
+        inp = pbs_synth.make_inputs(w)
+        dev = torch.device("cuda:0")
+
+        def to_dev(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+        sh = P.shape_of(q, k, w.block, w.segment)
+        scale = P.default_scale(w.head_dim)
+        B, Hq, Hkv, N, d, Bs, S = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment
+        nb, bps, G = N // Bs, S // Bs, Hq // Hkv
+        bf = P.Buffers(sh, dev)
+        P.pbs_score(sh, q, k, scale, bf.scores, bf.workspace)
+        P.pbs_permute(sh, bf.scores, k, v, bf.perm, bf.k_perm, bf.v_perm, bf.k_pool, bf.blk_minpos)
+        o = torch.empty_like(q)
+        lse_d = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale, o, lse_d)
+        lse = torch.empty_like(lse_d)
+        torch.cuda.synchronize()
+        seg_rows = torch.arange(N, device=dev) >= S          # rows that have candidates
+        i_idx = np.arange(nb)
+        candidates = B * Hq * int(((i_idx // bps) * bps).sum())
+        dense_blocks = B * Hq * nb * (nb + 1) // 2
+        minpos = bf.blk_minpos.cpu().numpy()
+        last_row = (i_idx + 1) * Bs - 1
+        own_perm = 0
+        for i in range(nb):
+            s0 = (i // bps) * bps
+            own_perm += int((minpos[:, :, s0:s0 + bps] <= last_row[i]).sum()) * G
+        own_nat = B * Hq * int((i_idx - (i_idx // bps) * bps + 1).sum())
+        res = {}
+        for order in ("permuted", "natural"):
+            rows = []
+            for tau in taus:
+                if order == "permuted":
+                    P.pbs_block_select(sh, q, bf.k_perm, bf.k_pool, scale, P.PBS_SELECT_COVERAGE, tau, None, 0,
+                                       bf.counts, bf.idx, bf.workspace)
+                    P.pbs_attn_fwd(sh, q, bf.k_perm, bf.v_perm, bf.perm, bf.blk_minpos, bf.counts, bf.idx,
+                                   scale, o, lse)
+                    own = own_perm
+                else:
+                    P.pbs_block_select(sh, q, k, None, scale, P.PBS_SELECT_COVERAGE, tau, None, 0,
+                                       bf.counts, bf.idx, bf.workspace)
+                    P.pbs_attn_fwd(sh, q, k, v, None, None, bf.counts, bf.idx, scale, o, lse)
+                    own = own_nat
+                cov = torch.exp(lse - lse_d)
+                sel = int(bf.counts.sum().item())
+                rows.append({"tau": tau, "selected": sel, "density_offdiag": round(sel / candidates, 5),
+                             "computed": sel + own, "density_computed": round((sel + own) / dense_blocks, 5),
+                             "coverage_mean": round(float(cov.mean().item()), 5),
+                             "coverage_mean_later_segments": round(float(cov[..., seg_rows].mean().item()), 5),
+                             "coverage_p10": round(float(torch.quantile(cov[..., seg_rows].flatten()[::97].float(), 0.1).item()), 5)})
+            res[order] = rows
+
+        def at_target(rows):
+            """Selected blocks at mean coverage (later segments) = target, interpolated."""
+            pts = sorted((r["coverage_mean_later_segments"], r["selected"]) for r in rows)
+            for (c0, s0_), (c1, s1_) in zip(pts, pts[1:]):
+                if c0 <= target <= c1 and c1 > c0:
+                    return s0_ + (s1_ - s0_) * (target - c0) / (c1 - c0)
+            return None
+
+        sp, sn = at_target(res["permuted"]), at_target(res["natural"])
+        delta = (1.0 - sp / sn) if (sp is not None and sn) else None
+        print(json.dumps({
+            "workload": name, "shape": f"B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} block={Bs} segment={S}",
+            "salient_key_boost": w.k_boost, "salient_frac": w.salient_frac,
+            "candidates": candidates, "dense_blocks": dense_blocks, "coverage_target": target,
+            "selected_at_target": {"permuted": None if sp is None else round(sp, 1),
+                                   "natural": None if sn is None else round(sn, 1)},
+            "delta_at_target": None if delta is None else round(delta, 4),
+            "sweep": res}), flush=True)
+        del bf, q, k, v, o
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,7 +212,20 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of 1 GiB (5 times): the known-size "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--density", default=None,
+                    help="comma-separated workloads: block density vs attention coverage, permuted vs "
+                         "natural order (one JSON line per workload instead of the bench line)")
+    ap.add_argument("--taus", default="0.5,0.7,0.8,0.9,0.95,0.98,0.99,0.995")
+    ap.add_argument("--coverage-target", type=float, default=0.975)
+    ap.add_argument("--k-boost", type=float, default=None,
+                    help="density mode: override the planted salient-key boost (attention concentration)")
     args = ap.parse_args()
+    if args.density:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            sys.exit(2)
+        density_main(args)
+        return
     if args.copy_calibration:
         import torch
         src = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")

@@ -278,14 +278,15 @@ struct RowState {
 };
 
 // One stage (64 keys) for one wave.  S^T = K Q^T for the two 32-key halves as two independent MFMA
-// chains (masked keys enter as -inf through the accumulators' initial values); then, half by half,
-// exp2 against the fixed reference and O^T += V^T P^T, so that the exp2 work of one half can
-// overlap the matrix work of the other.  There is no running max: the first stage of a pass sets
-// each row's reference to its max over that stage (0 for a row that sees no key of it), and a row
-// sum outside [2^-60, 2^64] after the pass sends the workgroup through the exact-max fallback.
-template <int D, int BS, int MODE, bool FIRST, bool MAXONLY>
+// chains (for a masked stage, masked keys enter as -inf through the accumulators' initial values);
+// then, half by half, exp2 against the fixed reference and O^T += V^T P^T, so that the exp2 work of
+// one half can overlap the matrix work of the other.  There is no running max: the first stage of a
+// pass (`first`, uniform) sets each row's reference to its max over that stage (0 for a row that
+// sees no key of it), and a row sum outside [2^-60, 2^64] after the pass sends the workgroup
+// through the exact-max fallback.
+template <int D, int BS, int MODE, bool MASKED, bool MAXONLY>
 __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vs,
-                                           const int32_t* Ps, Stage st, int lane, int t,
+                                           const int32_t* Ps, int key0, bool first, int lane, int t,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                            f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
   using C = Cfg<D, BS>;
@@ -298,11 +299,11 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
       k0[kt] = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kt * 32 + c32, hl * 8)]);
-    if (st.masked) {
+    if constexpr (MASKED) {
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            k0[kt], qf[0], mask_init<MODE>(Ps, st.key0, kt, hl, t), 0, 0, 0);
+            k0[kt], qf[0], mask_init<MODE>(Ps, key0, kt, hl, t), 0, 0, 0);
     } else {
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
@@ -318,7 +319,7 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
       s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
     }
   }
-  if constexpr (MAXONLY || FIRST) {
+  if (MAXONLY || first) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
@@ -331,78 +332,102 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
     }
     if (rs.mref == -INFINITY) rs.mref = (mx == -INFINITY) ? 0.f : mx;
   }
-  const float nm = -rs.mref;
+  if constexpr (!MAXONLY) {
+    const float nm = -rs.mref;
 #pragma unroll
-  for (int kt = 0; kt < C::NKT; ++kt) {
-    bf16x8 pb[2];
-    float sum = 0.f;
+    for (int kt = 0; kt < C::NKT; ++kt) {
+      bf16x8 pb[2];
+      float sum = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(fmaf(s[kt][8 * s2 + e], a.c, nm));
-        sum += p;
-        pb[s2][e] = static_cast<__bf16>(p);   // v_cvt_pk_bf16_f32, round to nearest even
-      }
-    rs.lsum += sum;
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(fmaf(s[kt][8 * s2 + e], a.c, nm));
+          sum += p;
+          pb[s2][e] = static_cast<__bf16>(p);   // v_cvt_pk_bf16_f32, round to nearest even
+        }
+      rs.lsum += sum;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int vr = kt * 32 + 16 * s2 + 4 * (gp >> 1) + (li >> 2);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int vr = kt * 32 + 16 * s2 + 4 * (gp >> 1) + (li >> 2);
 #pragma unroll
-      for (int mt = 0; mt < C::NMT; ++mt) {
-        const int dv = mt * 32 + (gp & 1) * 16 + 4 * (li & 3);
-        const u32x2 lo = ds_read_tr(&Vs[voff<D>(vr, dv)]);
-        const u32x2 hi = ds_read_tr(&Vs[voff<D>(vr + 8, dv)]);
-        const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4),
-                                                           pb[s2], oacc[mt], 0, 0, 0);
+        for (int mt = 0; mt < C::NMT; ++mt) {
+          const int dv = mt * 32 + (gp & 1) * 16 + 4 * (li & 3);
+          const u32x2 lo = ds_read_tr(&Vs[voff<D>(vr, dv)]);
+          const u32x2 hi = ds_read_tr(&Vs[voff<D>(vr + 8, dv)]);
+          const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4),
+                                                             pb[s2], oacc[mt], 0, 0, 0);
+        }
       }
     }
   }
 }
 
-// One pass over the visited key blocks through two LDS stage buffers.  Each stage's loads are
-// issued one stage ahead; the wait + barrier at the top of a stage both lands that stage and frees
-// the other buffer for the next loads.  The first stage is peeled (it sets the references).
+// Pipeline state carried from one stage to the next within a pass.
+struct Pipe {
+  Stage cur;    // the stage whose loads are in flight or landed in buffer `p`
+  int p;        // LDS buffer of `cur`
+  bool first;   // `cur` is the first stage of the pass
+};
+
+// `count` stages of one mask kind, one per iteration.  The loads of the next stage go into the
+// other buffer before the current stage is computed; the wait + barrier at the top of an iteration
+// both lands the current stage and frees the other buffer.  Buffers are picked by parity through
+// uniform offsets, so the loop body is one straight copy of the stage code and the accumulators
+// stay in place from one iteration to the next.
+template <int D, int BS, int MODE, bool MASKED, bool MAXONLY>
+__device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int count, Pipe& pp,
+                                           u32x4 rk, u32x4 rv, u32x4 rp, uint16_t* smem,
+                                           int32_t* Ps0, int32_t* Ps1, int w, int lane, int t,
+                                           const bf16x8 (&qf)[Cfg<D, BS>::NKS],
+                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
+  using C = Cfg<D, BS>;
+  const int tid = threadIdx.x;
+  for (int n = 0; n < count; ++n) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // the current stage landed; the other buffer is no longer read
+    const int p = pp.p;
+    const bool more = it.next(tid, C::NT);
+    Stage nxt;
+    nxt.key0 = it.j * BS + it.half * C::SK;
+    nxt.masked = it.masked;
+    if (more)
+      issue_stage<D, BS>(a, rk, rv, rp, nxt, smem + (p ? a.tile_off[0] : a.tile_off[1]),
+                         smem + (p ? a.tile_off[2] : a.tile_off[3]), p ? Ps0 : Ps1, w, lane);
+    attn_stage<D, BS, MODE, MASKED, MAXONLY>(
+        a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
+        p ? Ps1 : Ps0, pp.cur.key0, pp.first, lane, t, qf, oacc, rs);
+    pp.cur = nxt;
+    pp.p = p ^ 1;
+    pp.first = false;
+  }
+}
+
+// One pass over the visited stages: every visit list is its unmasked blocks followed by its masked
+// ones (off-diagonal then own-segment blocks in permuted order; blocks before the diagonal then the
+// diagonal in identity and dense order), so a pass is two loops, one per mask kind.
 template <int D, int BS, int MODE, bool MAXONLY>
-__device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, u32x4 rk, u32x4 rv,
-                                          u32x4 rp, uint16_t* Ks0, uint16_t* Ks1, uint16_t* Vs0,
-                                          uint16_t* Vs1, int32_t* Ps0, int32_t* Ps1, int w,
+__device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int n_unmasked,
+                                          int n_masked, u32x4 rk, u32x4 rv, u32x4 rp,
+                                          uint16_t* smem, int32_t* Ps0, int32_t* Ps1, int w,
                                           int lane, int t, const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
   using C = Cfg<D, BS>;
   const int tid = threadIdx.x;
   it.start(tid, C::NT);
-  Stage cur, nxt;
-  bool have = it.next(tid, C::NT);
-  if (have) {
-    cur.key0 = it.j * BS + it.half * C::SK;
-    cur.masked = it.masked;
-    issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    bool more = it.next(tid, C::NT);
-    nxt.key0 = it.j * BS + it.half * C::SK;
-    nxt.masked = it.masked;
-    if (more) issue_stage<D, BS>(a, rk, rv, rp, nxt, Ks1, Vs1, Ps1, w, lane);
-    attn_stage<D, BS, MODE, !MAXONLY, MAXONLY>(a, Ks0, Vs0, Ps0, cur, lane, t, qf, oacc, rs);
-    while (more) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();  // stage in buffer 1 landed; buffer 0 no longer read
-      have = it.next(tid, C::NT);
-      cur.key0 = it.j * BS + it.half * C::SK;
-      cur.masked = it.masked;
-      if (have) issue_stage<D, BS>(a, rk, rv, rp, cur, Ks0, Vs0, Ps0, w, lane);
-      attn_stage<D, BS, MODE, false, MAXONLY>(a, Ks1, Vs1, Ps1, nxt, lane, t, qf, oacc, rs);
-      if (!have) break;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();  // stage in buffer 0 landed; buffer 1 no longer read
-      more = it.next(tid, C::NT);
-      nxt.key0 = it.j * BS + it.half * C::SK;
-      nxt.masked = it.masked;
-      if (more) issue_stage<D, BS>(a, rk, rv, rp, nxt, Ks1, Vs1, Ps1, w, lane);
-      attn_stage<D, BS, MODE, false, MAXONLY>(a, Ks0, Vs0, Ps0, cur, lane, t, qf, oacc, rs);
-    }
+  if (it.next(tid, C::NT)) {
+    Pipe pp;
+    pp.cur.key0 = it.j * BS + it.half * C::SK;
+    pp.cur.masked = it.masked;
+    pp.p = 0;
+    pp.first = true;
+    issue_stage<D, BS>(a, rk, rv, rp, pp.cur, smem + a.tile_off[0], smem + a.tile_off[2], Ps0, w,
+                       lane);
+    run_stages<D, BS, MODE, false, MAXONLY>(a, it, n_unmasked * C::HALVES, pp, rk, rv, rp, smem,
+                                            Ps0, Ps1, w, lane, t, qf, oacc, rs);
+    run_stages<D, BS, MODE, true, MAXONLY>(a, it, n_masked * C::HALVES, pp, rk, rv, rp, smem, Ps0,
+                                           Ps1, w, lane, t, qf, oacc, rs);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // every wave is done with both buffers before another pass refills them
@@ -418,10 +443,6 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   __shared__ uint16_t offw[kOffWindow];
   __shared__ uint16_t ownl[kOwnMax];
   __shared__ int own_count;
-  uint16_t* const Ks0 = smem + a.tile_off[0];
-  uint16_t* const Ks1 = smem + a.tile_off[1];
-  uint16_t* const Vs0 = smem + a.tile_off[2];
-  uint16_t* const Vs1 = smem + a.tile_off[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -495,6 +516,18 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
     __syncthreads();
     it.n_own = own_count;
   }
+  // Unmasked entries come first in every visit list, masked ones last.
+  int n_unm, n_msk;
+  if (MODE == 0) {
+    n_unm = i;
+    n_msk = 1;
+  } else if (MODE == 1) {
+    n_unm = it.n_off;
+    n_msk = it.n_own;
+  } else {
+    n_msk = it.n_own > 0 ? 1 : 0;   // the diagonal block closes the identity-order list
+    n_unm = it.n_off + it.n_own - n_msk;
+  }
 
   // Q fragments (B operand of S^T = K Q^T): lane holds q[t][ks*16 + hl*8 .. +8]
   bf16x8 qf[C::NKS];
@@ -507,19 +540,19 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
   RowState rs{-INFINITY, 0.f, -INFINITY};
-  attn_pass<D, BS, MODE, false>(a, it, rk, rv, rp, Ks0, Ks1, Vs0, Vs1, Ps0, Ps1, w, lane, t, qf,
+  attn_pass<D, BS, MODE, false>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
                                 oacc, rs);
   // A row whose sum left [2^-60, 2^64] (scores far above or below its reference) is recomputed:
   // first its exact maximum, then the pass against that maximum.
   const float l0 = pair_sum(rs.lsum);
   if (__syncthreads_or(!(l0 >= 0x1p-60f && l0 <= 0x1p64f) ? 1 : 0)) {
-    attn_pass<D, BS, MODE, true>(a, it, rk, rv, rp, Ks0, Ks1, Vs0, Vs1, Ps0, Ps1, w, lane, t, qf,
+    attn_pass<D, BS, MODE, true>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
                                  oacc, rs);
 #pragma unroll
     for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
     rs.mref = rs.mseen;
     rs.lsum = 0.f;
-    attn_pass<D, BS, MODE, false>(a, it, rk, rv, rp, Ks0, Ks1, Vs0, Vs1, Ps0, Ps1, w, lane, t, qf,
+    attn_pass<D, BS, MODE, false>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
                                   oacc, rs);
   }
 

@@ -249,6 +249,11 @@ __device__ __forceinline__ float pair_sum(float x) {
 // Causal mask of a 32-key sub-tile as the initial value of its score accumulator: -inf for a key
 // whose original position is after the lane's query row t, else 0 (then -inf + the dot product
 // stays -inf).  Lane value r of sub-tile kt is stage key kt*32 + (r/4)*8 + hl*4 + r%4.
+// -inf for d < 0 (a key after the row), +0 for d >= 0, for |d| < 2^23 (positions are below
+// N <= 2^20): a negative d has its nine top bits set, which is exactly the bit pattern of -inf;
+// a small non-negative d has them clear.  Two independent integer operations per element.
+__device__ __forceinline__ float mask_bits(int d) { return __int_as_float(d & 0xff800000); }
+
 template <int MODE>
 __device__ __forceinline__ f32x16 mask_init(const int32_t* Ps, int key0, int kt, int hl, int t) {
   f32x16 m;
@@ -262,10 +267,10 @@ __device__ __forceinline__ f32x16 mask_init(const int32_t* Ps, int key0, int kt,
       const int p0 = key0 + key;
       pos = make_int4(p0, p0 + 1, p0 + 2, p0 + 3);
     }
-    m[rb * 4 + 0] = pos.x > t ? -INFINITY : 0.f;
-    m[rb * 4 + 1] = pos.y > t ? -INFINITY : 0.f;
-    m[rb * 4 + 2] = pos.z > t ? -INFINITY : 0.f;
-    m[rb * 4 + 3] = pos.w > t ? -INFINITY : 0.f;
+    m[rb * 4 + 0] = mask_bits(t - pos.x);
+    m[rb * 4 + 1] = mask_bits(t - pos.y);
+    m[rb * 4 + 2] = mask_bits(t - pos.z);
+    m[rb * 4 + 3] = mask_bits(t - pos.w);
   }
   return m;
 }
@@ -280,13 +285,13 @@ struct RowState {
 // One stage (64 keys) for one wave.  S^T = K Q^T for the two 32-key halves as two independent MFMA
 // chains (for a masked stage, masked keys enter as -inf through the accumulators' initial values);
 // then, half by half, exp2 against the fixed reference and O^T += V^T P^T, so that the exp2 work of
-// one half can overlap the matrix work of the other.  There is no running max: the first stage of a
-// pass (`first`, uniform) sets each row's reference to its max over that stage (0 for a row that
-// sees no key of it), and a row sum outside [2^-60, 2^64] after the pass sends the workgroup
-// through the exact-max fallback.
+// one half can overlap the matrix work of the other.  There is no running max: before a pass each
+// row's reference is set to its max over the pass's first stage (0 for a row that sees no key of
+// it; the MAXONLY form of this function computes that max), and a row sum outside [2^-60, 2^64]
+// after the pass sends the workgroup through the exact-max fallback.
 template <int D, int BS, int MODE, bool MASKED, bool MAXONLY>
 __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vs,
-                                           const int32_t* Ps, int key0, bool first, int lane, int t,
+                                           const int32_t* Ps, int key0, int lane, int t,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                            f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
   using C = Cfg<D, BS>;
@@ -319,20 +324,14 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
       s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
     }
   }
-  if (MAXONLY || first) {
+  if constexpr (MAXONLY) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = pair_max(mx) * a.c;
-    if constexpr (MAXONLY) {
-      rs.mseen = fmaxf(rs.mseen, mx);
-      return;
-    }
-    if (rs.mref == -INFINITY) rs.mref = (mx == -INFINITY) ? 0.f : mx;
-  }
-  if constexpr (!MAXONLY) {
+    rs.mseen = fmaxf(rs.mseen, pair_max(mx) * a.c);
+  } else {
     const float nm = -rs.mref;
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt) {
@@ -341,10 +340,11 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = fast_exp2(fmaf(s[kt][8 * s2 + e], a.c, nm));
-          sum += p;
-          pb[s2][e] = static_cast<__bf16>(p);   // v_cvt_pk_bf16_f32, round to nearest even
+        for (int e = 0; e < 8; ++e)   // v_cvt_pk_bf16_f32, round to nearest even
+        {
+          const float pe = fast_exp2(fmaf(s[kt][8 * s2 + e], a.c, nm));
+          sum += pe;
+          pb[s2][e] = static_cast<__bf16>(pe);
         }
       rs.lsum += sum;
 #pragma unroll
@@ -368,7 +368,6 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
 struct Pipe {
   Stage cur;    // the stage whose loads are in flight or landed in buffer `p`
   int p;        // LDS buffer of `cur`
-  bool first;   // `cur` is the first stage of the pass
 };
 
 // `count` stages of one mask kind, one per iteration.  The loads of the next stage go into the
@@ -397,17 +396,18 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
                          smem + (p ? a.tile_off[2] : a.tile_off[3]), p ? Ps0 : Ps1, w, lane);
     attn_stage<D, BS, MODE, MASKED, MAXONLY>(
         a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
-        p ? Ps1 : Ps0, pp.cur.key0, pp.first, lane, t, qf, oacc, rs);
+        p ? Ps1 : Ps0, pp.cur.key0, lane, t, qf, oacc, rs);
     pp.cur = nxt;
     pp.p = p ^ 1;
-    pp.first = false;
   }
 }
 
 // One pass over the visited stages: every visit list is its unmasked blocks followed by its masked
 // ones (off-diagonal then own-segment blocks in permuted order; blocks before the diagonal then the
-// diagonal in identity and dense order), so a pass is two loops, one per mask kind.
-template <int D, int BS, int MODE, bool MAXONLY>
+// diagonal in identity and dense order), so a pass is two loops, one per mask kind.  With PRIME,
+// the rows' references are first set from the max of the pass's first stage (computed once more,
+// scores only, as soon as that stage has landed).
+template <int D, int BS, int MODE, bool MAXONLY, bool PRIME>
 __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int n_unmasked,
                                           int n_masked, u32x4 rk, u32x4 rv, u32x4 rp,
                                           uint16_t* smem, int32_t* Ps0, int32_t* Ps1, int w,
@@ -421,9 +421,20 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
     pp.cur.key0 = it.j * BS + it.half * C::SK;
     pp.cur.masked = it.masked;
     pp.p = 0;
-    pp.first = true;
     issue_stage<D, BS>(a, rk, rv, rp, pp.cur, smem + a.tile_off[0], smem + a.tile_off[2], Ps0, w,
                        lane);
+    if constexpr (PRIME) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      RowState first{0.f, 0.f, -INFINITY};
+      if (n_unmasked > 0)
+        attn_stage<D, BS, MODE, false, true>(a, smem + a.tile_off[0], smem + a.tile_off[2], Ps0,
+                                             pp.cur.key0, lane, t, qf, oacc, first);
+      else
+        attn_stage<D, BS, MODE, true, true>(a, smem + a.tile_off[0], smem + a.tile_off[2], Ps0,
+                                            pp.cur.key0, lane, t, qf, oacc, first);
+      rs.mref = (first.mseen == -INFINITY) ? 0.f : first.mseen;
+    }
     run_stages<D, BS, MODE, false, MAXONLY>(a, it, n_unmasked * C::HALVES, pp, rk, rv, rp, smem,
                                             Ps0, Ps1, w, lane, t, qf, oacc, rs);
     run_stages<D, BS, MODE, true, MAXONLY>(a, it, n_masked * C::HALVES, pp, rk, rv, rp, smem, Ps0,
@@ -540,19 +551,19 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
   RowState rs{-INFINITY, 0.f, -INFINITY};
-  attn_pass<D, BS, MODE, false>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
+  attn_pass<D, BS, MODE, false, true>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
                                 oacc, rs);
   // A row whose sum left [2^-60, 2^64] (scores far above or below its reference) is recomputed:
   // first its exact maximum, then the pass against that maximum.
   const float l0 = pair_sum(rs.lsum);
   if (__syncthreads_or(!(l0 >= 0x1p-60f && l0 <= 0x1p64f) ? 1 : 0)) {
-    attn_pass<D, BS, MODE, true>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
+    attn_pass<D, BS, MODE, true, false>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
                                  oacc, rs);
 #pragma unroll
     for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
     rs.mref = rs.mseen;
     rs.lsum = 0.f;
-    attn_pass<D, BS, MODE, false>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
+    attn_pass<D, BS, MODE, false, false>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
                                   oacc, rs);
   }
 

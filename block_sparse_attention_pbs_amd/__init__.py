@@ -31,7 +31,7 @@ PBS_SELECT_COVERAGE = 1
 PBS_FLAG_SCORES_IN = 1
 
 ENTRY_POINTS = ("pbs_workspace_bytes", "pbs_max_offdiag", "pbs_strerror", "pbs_score",
-                "pbs_permute", "pbs_block_select", "pbs_attn_fwd")
+                "pbs_permute", "pbs_block_select", "pbs_attn_fwd", "pbs_attn_fwd_hybrid")
 
 
 class PbsError(RuntimeError):
@@ -76,7 +76,9 @@ def lib():
     L.pbs_block_select.argtypes = [S, _P, _P, _P, ctypes.c_float, ctypes.c_int, ctypes.c_double,
                                    _P, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]
     L.pbs_attn_fwd.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
-    for name in ("pbs_score", "pbs_permute", "pbs_block_select", "pbs_attn_fwd"):
+    L.pbs_attn_fwd_hybrid.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
+    for name in ("pbs_score", "pbs_permute", "pbs_block_select", "pbs_attn_fwd",
+                 "pbs_attn_fwd_hybrid"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -154,6 +156,13 @@ def pbs_attn_fwd(shape, q, k, v, perm, blk_minpos, counts, idx, scale, o, lse=No
     _check(lib().pbs_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm),
                               _ptr(blk_minpos), _ptr(counts), _ptr(idx), scale, _ptr(o), _ptr(lse),
                               _stream(stream)))
+
+
+def pbs_attn_fwd_hybrid(shape, q, k_perm, v_perm, k, v, counts, idx, scale, o, lse=None,
+                        stream=None):
+    _check(lib().pbs_attn_fwd_hybrid(ctypes.byref(shape), _ptr(q), _ptr(k_perm), _ptr(v_perm),
+                                     _ptr(k), _ptr(v), _ptr(counts), _ptr(idx), scale, _ptr(o),
+                                     _ptr(lse), _stream(stream)))
 
 
 def default_scale(head_dim: int) -> float:

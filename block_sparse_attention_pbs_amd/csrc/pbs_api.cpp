@@ -162,8 +162,24 @@ int pbs_attn_fwd(const pbs_shape* shape, const uint16_t* q, const uint16_t* k,
   for (const void* p : opt)
     if ((st = check_optional(p)) != PBS_OK) return st;
   const int mode = !counts ? 0 : (perm ? 1 : 2);
-  return status_of(pbs::launch_attn(d, q, k, v, perm, blk_minpos, counts, idx, mode, scale, o, lse,
-                                    static_cast<hipStream_t>(stream)));
+  return status_of(pbs::launch_attn(d, q, k, v, perm, blk_minpos, counts, idx, nullptr, nullptr,
+                                    mode, scale, o, lse, static_cast<hipStream_t>(stream)));
+}
+
+int pbs_attn_fwd_hybrid(const pbs_shape* shape, const uint16_t* q, const uint16_t* k_perm,
+                        const uint16_t* v_perm, const uint16_t* k, const uint16_t* v,
+                        const int32_t* counts, const int32_t* idx, float scale, uint16_t* o,
+                        float* lse, void* stream) {
+  Dims d;
+  int st = check_shape(shape, &d);
+  if (st != PBS_OK) return st;
+  if (!finite_positive(scale)) return PBS_E_ARG;
+  if (empty(d)) return PBS_OK;
+  const void* const req[] = {q, k_perm, v_perm, k, v, counts, idx, o};
+  if ((st = check_required(req)) != PBS_OK) return st;
+  if ((st = check_optional(lse)) != PBS_OK) return st;
+  return status_of(pbs::launch_attn(d, q, k_perm, v_perm, nullptr, nullptr, counts, idx, k, v, 3,
+                                    scale, o, lse, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

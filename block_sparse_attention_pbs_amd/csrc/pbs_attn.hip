@@ -49,10 +49,13 @@ struct AttnArgs {
   const int32_t* minpos;
   const int32_t* counts;
   const int32_t* idx;
+  const uint16_t* k2;   // mode 3: the original (unpermuted) keys and values, read for the own
+  const uint16_t* v2;   //         segment in natural order
   uint16_t* o;
   float* lse;
   int B, Hq, Hkv, G, N, nb, bps, max_off;
-  int mode;      // 0 dense causal, 1 permuted PBS, 2 identity-order PBS
+  int mode;      // 0 dense causal, 1 permuted PBS, 2 identity-order PBS, 3 permuted off-diagonal
+                 // blocks with the own segment in natural order
   int xcd_map;   // 1: total work items divisible by 8, use the XCD-grouped order
   float c;       // scale * log2(e)
   // Element offsets of the K/V stage tiles in LDS.  Passed at run time on purpose: the compiler
@@ -145,6 +148,7 @@ struct StageIter {
   int win;              // first off-diagonal entry held in the LDS window
   int j, half;
   bool masked;
+  bool orig;            // mode 3: the entry is an own-segment block of the original keys
   const int32_t* list;  // off-diagonal list in global memory
   uint16_t* offw;       // LDS window of the off-diagonal list
   const uint16_t* ownl; // LDS list of the visible own-segment blocks
@@ -190,6 +194,7 @@ struct StageIter {
     if (m < n_off + n_own) ent = read_entry(m);
     j = e & 0x7fff;
     masked = (e >> 15) != 0;
+    orig = (mode == 3) && (m - 1 >= n_off);
     return true;
   }
   // Advance to the next stage; false when the list is exhausted.
@@ -206,16 +211,26 @@ struct StageIter {
 struct Stage {
   int key0;     // first key of the stage in the head's key order (block * Bs + half * 64)
   bool masked;
+  bool orig;    // read from the original keys and values (mode 3 own segment)
+};
+
+// Buffer resources of one head: keys, values, key positions, and (mode 3) the original keys
+// and values.
+struct Rsrc {
+  u32x4 k, v, p, k2, v2;
 };
 
 // Start the asynchronous loads of one stage (K, V and, for masked permuted blocks, the original
 // positions of its keys) into LDS.  A spare chunk of a padded row re-reads chunk 0 of its row.
 template <int D, int BS>
-__device__ __forceinline__ void issue_stage(const AttnArgs& a, u32x4 rk, u32x4 rv, u32x4 rp,
-                                            Stage st, uint16_t* Kst, uint16_t* Vst, int32_t* Pst,
-                                            int w, int lane) {
+__device__ __forceinline__ void issue_stage(const AttnArgs& a, const Rsrc& rr, Stage st,
+                                            uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
+                                            int lane) {
   using C = Cfg<D, BS>;
   const uint32_t base = static_cast<uint32_t>(st.key0) * D * 2;
+  const u32x4 rk = st.orig ? rr.k2 : rr.k;
+  const u32x4 rv = st.orig ? rr.v2 : rr.v;
+  const u32x4 rp = rr.p;
 #pragma unroll
   for (int n = w; n < C::NLDK; n += C::NW) {
     const int P = n * 64 + lane;
@@ -377,7 +392,7 @@ struct Pipe {
 // stay in place from one iteration to the next.
 template <int D, int BS, int MODE, bool MASKED, bool MAXONLY>
 __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int count, Pipe& pp,
-                                           u32x4 rk, u32x4 rv, u32x4 rp, uint16_t* smem,
+                                           const Rsrc& rr, uint16_t* smem,
                                            int32_t* Ps0, int32_t* Ps1, int w, int lane, int t,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                            f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
@@ -391,8 +406,9 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
     Stage nxt;
     nxt.key0 = it.j * BS + it.half * C::SK;
     nxt.masked = it.masked;
+    nxt.orig = it.orig;
     if (more)
-      issue_stage<D, BS>(a, rk, rv, rp, nxt, smem + (p ? a.tile_off[0] : a.tile_off[1]),
+      issue_stage<D, BS>(a, rr, nxt, smem + (p ? a.tile_off[0] : a.tile_off[1]),
                          smem + (p ? a.tile_off[2] : a.tile_off[3]), p ? Ps0 : Ps1, w, lane);
     attn_stage<D, BS, MODE, MASKED, MAXONLY>(
         a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
@@ -409,7 +425,7 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
 // scores only, as soon as that stage has landed).
 template <int D, int BS, int MODE, bool MAXONLY, bool PRIME>
 __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int n_unmasked,
-                                          int n_masked, u32x4 rk, u32x4 rv, u32x4 rp,
+                                          int n_masked, const Rsrc& rr,
                                           uint16_t* smem, int32_t* Ps0, int32_t* Ps1, int w,
                                           int lane, int t, const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
@@ -420,9 +436,9 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
     Pipe pp;
     pp.cur.key0 = it.j * BS + it.half * C::SK;
     pp.cur.masked = it.masked;
+    pp.cur.orig = it.orig;
     pp.p = 0;
-    issue_stage<D, BS>(a, rk, rv, rp, pp.cur, smem + a.tile_off[0], smem + a.tile_off[2], Ps0, w,
-                       lane);
+    issue_stage<D, BS>(a, rr, pp.cur, smem + a.tile_off[0], smem + a.tile_off[2], Ps0, w, lane);
     if constexpr (PRIME) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -435,9 +451,9 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
                                             pp.cur.key0, lane, t, qf, oacc, first);
       rs.mref = (first.mseen == -INFINITY) ? 0.f : first.mseen;
     }
-    run_stages<D, BS, MODE, false, MAXONLY>(a, it, n_unmasked * C::HALVES, pp, rk, rv, rp, smem,
+    run_stages<D, BS, MODE, false, MAXONLY>(a, it, n_unmasked * C::HALVES, pp, rr, smem,
                                             Ps0, Ps1, w, lane, t, qf, oacc, rs);
-    run_stages<D, BS, MODE, true, MAXONLY>(a, it, n_masked * C::HALVES, pp, rk, rv, rp, smem, Ps0,
+    run_stages<D, BS, MODE, true, MAXONLY>(a, it, n_masked * C::HALVES, pp, rr, smem, Ps0,
                                            Ps1, w, lane, t, qf, oacc, rs);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -479,9 +495,12 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;
   const int t = i * BS + w * 32 + c32;       // this lane's query row (both halves share it)
   const uint32_t head_bytes = static_cast<uint32_t>(a.N) * D * 2;
-  const u32x4 rk = make_rsrc(a.k + kv_head * D, head_bytes);
-  const u32x4 rv = make_rsrc(a.v + kv_head * D, head_bytes);
-  const u32x4 rp =
+  Rsrc rr;
+  rr.k = make_rsrc(a.k + kv_head * D, head_bytes);
+  rr.v = make_rsrc(a.v + kv_head * D, head_bytes);
+  rr.k2 = make_rsrc(MODE == 3 ? a.k2 + kv_head * D : nullptr, MODE == 3 ? head_bytes : 0u);
+  rr.v2 = make_rsrc(MODE == 3 ? a.v2 + kv_head * D : nullptr, MODE == 3 ? head_bytes : 0u);
+  rr.p =
       make_rsrc(a.perm ? a.perm + kv_head : nullptr, a.perm ? static_cast<uint32_t>(a.N) * 4 : 0u);
 
   StageIter it;
@@ -497,6 +516,7 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   it.ownl = ownl;
   it.j = 0;
   it.masked = false;
+  it.orig = false;
   it.ent = 0;
   if (MODE != 0) {
     const size_t row = (static_cast<size_t>(b) * a.Hq + g) * a.nb + i;
@@ -514,7 +534,7 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
         const int o = o0 + lane;
         const int jj = it.seg_first + o;
         bool vis = false;
-        if (o < a.bps) vis = (MODE == 2) ? (jj <= i) : (mp == nullptr || mp[o] <= last_row);
+        if (o < a.bps) vis = (MODE != 1) ? (jj <= i) : (mp == nullptr || mp[o] <= last_row);
         const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
         const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
@@ -551,19 +571,19 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
   RowState rs{-INFINITY, 0.f, -INFINITY};
-  attn_pass<D, BS, MODE, false, true>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
+  attn_pass<D, BS, MODE, false, true>(a, it, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
                                 oacc, rs);
   // A row whose sum left [2^-60, 2^64] (scores far above or below its reference) is recomputed:
   // first its exact maximum, then the pass against that maximum.
   const float l0 = pair_sum(rs.lsum);
   if (__syncthreads_or(!(l0 >= 0x1p-60f && l0 <= 0x1p64f) ? 1 : 0)) {
-    attn_pass<D, BS, MODE, true, false>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
+    attn_pass<D, BS, MODE, true, false>(a, it, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
                                  oacc, rs);
 #pragma unroll
     for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
     rs.mref = rs.mseen;
     rs.lsum = 0.f;
-    attn_pass<D, BS, MODE, false, false>(a, it, n_unm, n_msk, rk, rv, rp, smem, Ps0, Ps1, w, lane, t, qf,
+    attn_pass<D, BS, MODE, false, false>(a, it, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
                                   oacc, rs);
   }
 
@@ -590,6 +610,7 @@ hipError_t launch_attn_t(const Dims& d, const AttnArgs& a, hipStream_t stream) {
   const dim3 block(Cfg<D, BS>::NT);
   if (a.mode == 1) return launch(attn_fwd_kernel<D, BS, 1>, dim3(total), block, 0, stream, a);
   if (a.mode == 2) return launch(attn_fwd_kernel<D, BS, 2>, dim3(total), block, 0, stream, a);
+  if (a.mode == 3) return launch(attn_fwd_kernel<D, BS, 3>, dim3(total), block, 0, stream, a);
   return launch(attn_fwd_kernel<D, BS, 0>, dim3(total), block, 0, stream, a);
 }
 
@@ -597,10 +618,11 @@ hipError_t launch_attn_t(const Dims& d, const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const int32_t* perm, const int32_t* blk_minpos, const int32_t* counts,
-                       const int32_t* idx, int mode, float scale, uint16_t* o, float* lse,
-                       hipStream_t stream) {
+                       const int32_t* idx, const uint16_t* k_orig, const uint16_t* v_orig,
+                       int mode, float scale, uint16_t* o, float* lse, hipStream_t stream) {
   AttnArgs a;
   a.q = q; a.k = k; a.v = v;
+  a.k2 = k_orig; a.v2 = v_orig;
   a.perm = perm; a.minpos = blk_minpos; a.counts = counts; a.idx = idx;
   a.o = o; a.lse = lse;
   a.B = d.B; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.N = d.N; a.nb = d.nb; a.bps = d.bps;

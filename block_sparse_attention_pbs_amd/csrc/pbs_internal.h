@@ -43,10 +43,11 @@ hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t*
                                float* blk_scores, bool scores_in, int32_t* counts, int32_t* idx,
                                void* ws, hipStream_t stream);
 
-// mode: 0 dense causal, 1 PBS with a permutation, 2 PBS in the identity order.
+// mode: 0 dense causal, 1 PBS with a permutation, 2 PBS in the identity order, 3 PBS with
+// permuted off-diagonal blocks and the own segment read from k_orig/v_orig in natural order.
 hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const int32_t* perm, const int32_t* blk_minpos, const int32_t* counts,
-                       const int32_t* idx, int mode, float scale, uint16_t* o, float* lse,
-                       hipStream_t stream);
+                       const int32_t* idx, const uint16_t* k_orig, const uint16_t* v_orig,
+                       int mode, float scale, uint16_t* o, float* lse, hipStream_t stream);
 
 }  // namespace pbs

@@ -178,6 +178,29 @@ int pbs_attn_fwd(const pbs_shape* shape, const uint16_t* q, const uint16_t* k,
                  const int32_t* counts, const int32_t* idx, float scale, uint16_t* o,
                  float* lse, void* stream);
 
+/*
+ * pbs_attn_fwd_hybrid -- the same attention as pbs_attn_fwd in PBS mode, with the own segment
+ * read from the ORIGINAL keys and values in natural order.
+ * Passage: sciencestack.ai page, Lemma 3.1 (attention is unchanged when keys and values are
+ * permuted together and the mask follows them) and Fig. 1 caption (the own segment is computed
+ * under the causal mask).  Row t of query block i, segment s, sees the keys of segment s with
+ * original position <= t whatever order they are stored in, so they can be read from the
+ * unpermuted k/v: only blocks s*(S/Bs) .. i are visited (the diagonal one under the causal
+ * mask), about half the own-segment blocks the permuted order needs, since almost every
+ * permuted block holds some key at or before the query block.  The kept earlier-segment
+ * blocks still come from the permuted copies.  Same output as pbs_attn_fwd(k_perm, v_perm,
+ * perm, ...) up to floating-point summation order.
+ *   q              [B,Hq,N,d] bf16
+ *   k_perm, v_perm [B,Hkv,N,d] bf16 from pbs_permute (read for the kept blocks)
+ *   k, v           [B,Hkv,N,d] bf16 original keys and values (read for the own segment)
+ *   counts, idx    from pbs_block_select (required); o, lse as in pbs_attn_fwd
+ * Errors as pbs_attn_fwd; every pointer except lse is required.
+ */
+int pbs_attn_fwd_hybrid(const pbs_shape* shape, const uint16_t* q, const uint16_t* k_perm,
+                        const uint16_t* v_perm, const uint16_t* k, const uint16_t* v,
+                        const int32_t* counts, const int32_t* idx, float scale, uint16_t* o,
+                        float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -70,6 +70,12 @@ def test_errors_before_any_launch():
     assert attn(None, None, fake, None) == P.PBS_E_ARG          # counts without idx
     assert attn(fake, None, None, None) == P.PBS_E_ARG          # permutation in dense mode
     assert attn(fake, fake + 4, fake, fake) == P.PBS_E_ALIGN
+    hyb = lambda kp, k, counts, lse=None: _call(
+        "pbs_attn_fwd_hybrid", S, fake, kp, fake, k, fake, counts, fake, 0.1, fake, lse, None)
+    assert hyb(fake, fake, None) == P.PBS_E_ARG                  # lists are required
+    assert hyb(fake, None, fake) == P.PBS_E_ARG                  # original keys are required
+    assert hyb(fake + 2, fake, fake) == P.PBS_E_ALIGN
+    assert hyb(fake, fake, fake, lse=fake + 4) == P.PBS_E_ALIGN
 
 
 def test_empty_problem_is_ok_without_pointers():

@@ -7,7 +7,7 @@ times (the same entry points, shapes and parameters), on outputs the oracle can 
   * block selection: every row, bit-exact, given the oracle's float32 block probabilities;
   * attention with the oracle's permutation and lists: sampled query blocks (the first and last
     block of every segment and every 16th block) of a few query heads, max-abs 2e-2 / mean-abs
-    2e-3;
+    2e-3, through pbs_attn_fwd and through pbs_attn_fwd_hybrid;
   * the whole GPU pipeline end to end: the same sampled blocks against the whole oracle pipeline.
 
 Each workload is generated once per module (seconds) and the oracle stages cost tens of seconds
@@ -116,6 +116,17 @@ def test_full_attention_sampled(full):
         got = np.stack([og[b, g, i * w.block:(i + 1) * w.block] for b, g, i in samples])
         gl = np.stack([lg[b, g, i * w.block:(i + 1) * w.block] for b, g, i in samples])
         check_attn(got, oo, f"{full['name']} attention param {param} ({len(samples)} blocks)")
+        assert np.abs(gl - ol).max() < 1e-3
+        # the hybrid entry point (own segment from the original K/V in natural order), same lists
+        oh = torch.empty_like(o)
+        lh = torch.empty_like(lse)
+        P.pbs_attn_fwd_hybrid(full["sh"], full["g"]["q"], kp, vp, full["g"]["k"], full["g"]["v"],
+                              dev(rc), dev(ri), full["scale"], oh, lh)
+        torch.cuda.synchronize()
+        ohg, lhg = oh.float().cpu().numpy(), lh.cpu().numpy()
+        got = np.stack([ohg[b, g, i * w.block:(i + 1) * w.block] for b, g, i in samples])
+        gl = np.stack([lhg[b, g, i * w.block:(i + 1) * w.block] for b, g, i in samples])
+        check_attn(got, oo, f"{full['name']} hybrid attention param {param}")
         assert np.abs(gl - ol).max() < 1e-3
 
 

@@ -130,6 +130,21 @@ def test_attention_given_oracle_lists(case):
     assert torch.equal(o, o2)
 
 
+def test_hybrid_own_segment_natural(case):
+    """pbs_attn_fwd_hybrid: kept blocks from the permuted copies, own segment from the original
+    keys in natural order; the visible key set of every row is the same, so the oracle's output
+    is the reference (Lemma 3.1 of the sciencestack.ai page)."""
+    say(case["name"], "pbs_attn_fwd_hybrid (oracle permutation and lists)")
+    ref, sh, g = case["ref"], case["sh"], case["g"]
+    o = torch.empty_like(g["q"])
+    lse = torch.empty(g["q"].shape[:3], dtype=torch.float32, device="cuda")
+    P.pbs_attn_fwd_hybrid(sh, g["q"], dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]), g["k"],
+                          g["v"], dev(ref["counts"]), dev(ref["idx"]), case["scale"], o, lse)
+    torch.cuda.synchronize()
+    check_attn(o.float().cpu().numpy(), ref["o"], f"{case['name']} hybrid attention")
+    assert np.abs(lse.cpu().numpy() - ref["lse"]).max() < 1e-3
+
+
 def test_dense_causal(case):
     say(case["name"], "pbs_attn_fwd dense")
     ref, sh = case["ref"], case["sh"]

@@ -29,6 +29,7 @@ PBS_E_LAUNCH = -5
 PBS_SELECT_KEEP_RATIO = 0
 PBS_SELECT_COVERAGE = 1
 PBS_FLAG_SCORES_IN = 1
+PBS_FLAG_KEEP_FIRST = 2
 
 ENTRY_POINTS = ("pbs_workspace_bytes", "pbs_max_offdiag", "pbs_strerror", "pbs_score",
                 "pbs_permute", "pbs_block_select", "pbs_attn_fwd", "pbs_attn_fwd_hybrid")

@@ -124,7 +124,7 @@ int pbs_block_select(const pbs_shape* shape, const uint16_t* q, const uint16_t* 
   if (st != PBS_OK) return st;
   if (mode != PBS_SELECT_KEEP_RATIO && mode != PBS_SELECT_COVERAGE) return PBS_E_ARG;
   if (!(param > 0.0 && param <= 1.0)) return PBS_E_ARG;
-  if (flags & ~PBS_FLAG_SCORES_IN) return PBS_E_ARG;
+  if (flags & ~(PBS_FLAG_SCORES_IN | PBS_FLAG_KEEP_FIRST)) return PBS_E_ARG;
   const bool scores_in = (flags & PBS_FLAG_SCORES_IN) != 0;
   if (!scores_in && !finite_positive(scale)) return PBS_E_ARG;
   if (empty(d)) return PBS_OK;
@@ -140,8 +140,9 @@ int pbs_block_select(const pbs_shape* shape, const uint16_t* q, const uint16_t* 
   if ((st = check_optional(k_pool)) != PBS_OK) return st;
   if ((st = check_optional(blk_scores)) != PBS_OK) return st;
   if (workspace_bytes < pbs::select_workspace_bytes(d)) return PBS_E_WORKSPACE;
+  const bool keep_first = (flags & PBS_FLAG_KEEP_FIRST) != 0;
   return status_of(pbs::launch_block_select(d, q, k_perm, k_pool, scale, mode, param, blk_scores,
-                                            scores_in, counts, idx, workspace,
+                                            scores_in, keep_first, counts, idx, workspace,
                                             static_cast<hipStream_t>(stream)));
 }
 

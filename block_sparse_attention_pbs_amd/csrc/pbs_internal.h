@@ -40,8 +40,8 @@ hipError_t launch_permute(const Dims& d, const float* scores, const uint16_t* k,
 size_t select_workspace_bytes(const Dims& d);
 hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t* k_perm,
                                const float* k_pool, float scale, int mode, double param,
-                               float* blk_scores, bool scores_in, int32_t* counts, int32_t* idx,
-                               void* ws, hipStream_t stream);
+                               float* blk_scores, bool scores_in, bool keep_first, int32_t* counts,
+                               int32_t* idx, void* ws, hipStream_t stream);
 
 // mode: 0 dense causal, 1 PBS with a permutation, 2 PBS in the identity order, 3 PBS with
 // permuted off-diagonal blocks and the own segment read from k_orig/v_orig in natural order.

@@ -7,7 +7,10 @@
 // Implementation Steps: the active-block count max(1, int(num_blocks * keep))):
 //   P[i, j] = softmax over candidates j < seg(i)*bps of scale * <qbar_i, kbar_j>,
 // ranked by P descending (ties to the lower j); keep ratio r keeps max(1, floor(r*n)) of them,
-// coverage tau keeps the shortest prefix whose sequential float32 sum reaches tau.
+// coverage tau keeps the shortest prefix whose sequential float32 sum reaches tau.  Optionally key
+// block 0 (the block of the first tokens, where the attention sink lands) is ranked ahead of
+// every other candidate; the pages name a first-token mask in the authors' code without defining
+// it (codewithpapers.app record), and this is its plainest reading.
 //
 // Kernels:
 //  * pool: float32 mean of every block of Bs rows (queries; keys too when the caller has no
@@ -73,6 +76,7 @@ struct SelArgs {
   int Hq, Hkv, G, hpw, nb, bps, max_off, n2max;
   int mode;            // 0 keep ratio, 1 coverage
   int p_in;            // read P instead of computing it
+  int keep_first;      // rank key block 0 ahead of every other candidate
   double param;
   float tau_f;         // least float f with (double)f >= param (coverage)
   float scale;
@@ -219,8 +223,11 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
     __syncthreads();
   }
 
+  // Sort keys: (descending P, ascending block); with keep_first, block 0 gets key 0, below every
+  // real key (whose top word, the complemented orderable value, is never 0).
   for (int p = st; p < n2; p += kSub)
-    keys[p] = (p < n) ? desc_sort_key(Ps[p], static_cast<uint32_t>(p)) : ~0ull;
+    keys[p] = (p < n) ? ((a.keep_first && p == 0) ? 0ull : desc_sort_key(Ps[p], static_cast<uint32_t>(p)))
+                      : ~0ull;
   bitonic_sort_row(keys, n2, st);
 
   if (a.mode == 0) {
@@ -307,8 +314,8 @@ size_t select_workspace_bytes(const Dims& d) {
 
 hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t* k_perm,
                                const float* k_pool, float scale, int mode, double param,
-                               float* blk_scores, bool scores_in, int32_t* counts, int32_t* idx,
-                               void* ws, hipStream_t stream) {
+                               float* blk_scores, bool scores_in, bool keep_first, int32_t* counts,
+                               int32_t* idx, void* ws, hipStream_t stream) {
   float* qbar = static_cast<float*>(ws);
   float* kbar_ws = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                             align256(static_cast<size_t>(d.B) * d.Hq * d.nb * d.d * sizeof(float)));
@@ -336,6 +343,7 @@ hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t*
   while (hpw > 1 && (d.G % hpw != 0 || hpw * per_row > 65536)) hpw >>= 1;
   sa.hpw = hpw;
   sa.mode = mode; sa.p_in = scores_in ? 1 : 0; sa.param = param; sa.scale = scale;
+  sa.keep_first = keep_first ? 1 : 0;
   sa.tau_f = static_cast<float>(param);
   if (static_cast<double>(sa.tau_f) < param) sa.tau_f = std::nextafter(sa.tau_f, INFINITY);
   const size_t shmem = hpw * per_row;

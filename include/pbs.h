@@ -66,6 +66,12 @@ typedef enum pbs_select_mode {
 /* pbs_block_select flag: read the block probabilities from `blk_scores` instead of
    computing them (selection only). */
 #define PBS_FLAG_SCORES_IN 1
+/* pbs_block_select flag: rank key block 0 ahead of every other candidate, so every query block
+   with candidates keeps it and, for coverage, its probability is counted first.  Key block 0
+   holds the first tokens in natural order and the top-ranked keys of segment 0 in permuted
+   order, where the attention sink lands.  The pages name a first-token mask in the authors'
+   code (codewithpapers.app record) without defining it; this is its plainest reading. */
+#define PBS_FLAG_KEEP_FIRST 2
 
 /* Bytes of device workspace that pbs_score and pbs_block_select need for `shape`
    (the larger of the two).  0 for an invalid shape. */
@@ -129,7 +135,7 @@ int pbs_permute(const pbs_shape* shape, const float* scores, const uint16_t* k,
  * For query block i of segment s = i / (S/Bs), the candidates are key blocks j < s*(S/Bs):
  *   P[i,j] = softmax over candidates of scale * <mean of q rows of block i,
  *                                              mean of k_perm rows of block j>
- * ranked by P descending, ties to the lower j; kept:
+ * ranked by P descending, ties to the lower j (with PBS_FLAG_KEEP_FIRST block 0 first); kept:
  *   PBS_SELECT_KEEP_RATIO (param = r):   the first max(1, floor(r*n)) (in double), n = #candidates
  *   PBS_SELECT_COVERAGE   (param = tau): the shortest prefix whose sequential float32 sum of
  *                                        P (compared in double) is >= tau; all n if none.

@@ -207,7 +207,7 @@ def keep_count(n: int, ratio: float) -> int:
 
 
 def select_blocks(P: np.ndarray, *, block: int, segment: int, mode: str, param: float,
-                  ) -> Tuple[np.ndarray, np.ndarray]:
+                  keep_first: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """Per query block, which candidate key blocks are computed.
 
     Returns ``counts`` int32 ``[B, Hq, nb]`` and ``idx`` int32 ``[B, Hq, nb, (nseg-1)*bps]``
@@ -221,7 +221,12 @@ def select_blocks(P: np.ndarray, *, block: int, segment: int, mode: str, param: 
                 reaches tau, i.e. the fewest top blocks that cover tau of the block-level
                 attention mass
                 ([SS Fig. 2] defines coverage as the attention covered by selected blocks);
-                all n if the sum never reaches tau."""
+                all n if the sum never reaches tau.
+    ``keep_first``: key block 0 is ranked ahead of every other candidate (so it is always
+    kept and its mass counts first), the rest keep their order.  The pages name a
+    ``first_token_mask`` in the authors' code ([CP] record) without defining it; this is the
+    plainest reading: the block holding the first tokens (the attention sink) is always
+    computed."""
     B, Hq, nb, _ = P.shape
     bps = segment // block
     nseg = nb // bps
@@ -234,6 +239,9 @@ def select_blocks(P: np.ndarray, *, block: int, segment: int, mode: str, param: 
         rows = slice(sigma * bps, (sigma + 1) * bps)
         cand = P[:, :, rows, :n]                              # [B, Hq, bps, n]
         order = descending_order(cand)
+        if keep_first:
+            rest = order[order != 0].reshape(order.shape[:-1] + (n - 1,))
+            order = np.concatenate([np.zeros(order.shape[:-1] + (1,), order.dtype), rest], axis=-1)
         if mode == KEEP:
             kk = np.full(cand.shape[:-1], keep_count(n, param), dtype=np.int64)
         elif mode == COVERAGE:

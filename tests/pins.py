@@ -195,13 +195,14 @@ def pin_keep_count_golden(O):
         assert O.keep_count(int(n), float(r)) == int(want), (n, r, want)
 
 
-def _select_case(O, rows, mode, param):
+def _select_case(O, rows, mode, param, keep_first=False):
     """rows: list of 5-value P rows for query blocks 5..9 of a block=1, segment=5, N=10
     layout (5 candidates each)."""
     P = np.zeros((1, 1, 10, 10), np.float32)
     for r, vals in enumerate(rows):
         P[0, 0, 5 + r, :5] = np.array(vals, np.float32)
-    counts, idx = O.select_blocks(P, block=1, segment=5, mode=mode, param=param)
+    counts, idx = O.select_blocks(P, block=1, segment=5, mode=mode, param=param,
+                                  keep_first=keep_first)
     assert counts.dtype == np.int32 and idx.dtype == np.int32 and idx.shape == (1, 1, 10, 5)
     assert (counts[0, 0, :5] == 0).all()
     return [idx[0, 0, 5 + r, :counts[0, 0, 5 + r]].tolist() for r in range(len(rows))]
@@ -221,6 +222,71 @@ def pin_select_handworked(O):
     assert _select_case(O, rows, O.COVERAGE, 0.75) == [[0, 1, 2, 4], [0, 1, 2, 3], [4], [2, 3], [0, 1]]
     assert _select_case(O, rows, O.COVERAGE, 1.0)[4] == [0, 1, 2, 3]
     assert _select_case(O, [[0.125] * 5], O.COVERAGE, 0.9) == [[0, 1, 2, 3, 4]]
+
+
+def pin_select_keep_first_handworked(O):
+    """Block 0 forced to the front of the ranking (the first-token block): it is always kept,
+    the rest follow by P descending (ties to the lower block), and for coverage block 0's mass
+    is counted first.  Worked by hand on the rows above:
+      row [0.125, 0.25, 0.25, 0.0625, 0.125], keep 0.5 (2 blocks): 0, then 1 (tie 1/2 to the
+        lower block)                                      -> [0, 1]
+      row [0.0, 0.0, 0.0, 0.0, 1.0], keep 0.5: 0, then 4  -> [0, 4] (the same as without)
+      row [0.25, 0.5, 0.125, 0.125, 0.0], coverage 0.75: 0.25 (block 0) + 0.5 (block 1)
+        = 0.75 reaches tau                                -> [0, 1]
+      row [0.0, 0.0, 0.5, 0.25, 0.25], coverage 0.75: 0 + 0.5 (block 2) + 0.25 (block 3)
+        = 0.75                                            -> [0, 2, 3] (without: [2, 3])
+      row [0.0, 0.0, 0.0, 0.0, 1.0], keep 0.1 (1 block)   -> [0] (without: [4])"""
+    rows = [[0.125, 0.25, 0.25, 0.0625, 0.125],
+            [0.0, 0.0, 0.0, 0.0, 1.0],
+            [0.25, 0.5, 0.125, 0.125, 0.0],
+            [0.0, 0.0, 0.5, 0.25, 0.25]]
+    assert _select_case(O, rows[:2], O.KEEP, 0.5, keep_first=True) == [[0, 1], [0, 4]]
+    assert _select_case(O, rows[2:], O.COVERAGE, 0.75, keep_first=True) == [[0, 1], [0, 2, 3]]
+    assert _select_case(O, rows[3:], O.COVERAGE, 0.75) == [[2, 3]]
+    assert _select_case(O, rows[1:2], O.KEEP, 0.1, keep_first=True) == [[0]]
+    assert _select_case(O, rows[1:2], O.KEEP, 0.1) == [[4]]
+
+
+def pin_select_keep_first_laws(O):
+    """With block 0 forced first, on random rows: block 0 is always kept, the keep count law
+    is unchanged, every other kept block outranks every other dropped one, and the coverage
+    prefix (block 0, then by rank) is minimal."""
+    rng = np.random.default_rng(19)
+    nb, bps = 24, 4
+    P = np.zeros((1, 2, nb, nb), np.float32)
+    for g in range(2):
+        for i in range(bps, nb):
+            n = (i // bps) * bps
+            e = np.exp(rng.normal(size=n))
+            P[0, g, i, :n] = (e / e.sum()).astype(np.float32)
+    for mode, param in ((O.KEEP, 0.3), (O.COVERAGE, 0.6)):
+        counts, idx = O.select_blocks(P, block=1, segment=bps, mode=mode, param=param,
+                                      keep_first=True)
+        for g in range(2):
+            for i in range(bps, nb):
+                n = (i // bps) * bps
+                kk = int(counts[0, g, i])
+                sel = idx[0, g, i, :kk].tolist()
+                assert sel[0] == 0 and sel == sorted(set(sel))
+                if mode == O.KEEP:
+                    assert kk == max(1, int(param * n))
+                row = P[0, g, i, :n]
+                others = [j for j in sel if j != 0]
+                rest = [j for j in range(1, n) if j not in sel]
+                for a in others:
+                    for b in rest:
+                        assert row[a] > row[b] or (row[a] == row[b] and a < b)
+                if mode == O.COVERAGE:
+                    ranked = [0] + sorted(others, key=lambda j: (-row[j], j))
+                    c = np.float32(0)
+                    partial = []
+                    for j in ranked:
+                        c = np.float32(c + row[j])
+                        partial.append(float(c))
+                    if kk < n:
+                        assert partial[-1] >= param
+                    if kk > 1:
+                        assert partial[-2] < param
 
 
 def pin_select_sequential_fp32(O):

@@ -63,6 +63,8 @@ def test_errors_before_any_launch():
     assert sel(0, 0.0, 0) == P.PBS_E_ARG
     assert sel(1, 1.5, 0) == P.PBS_E_ARG
     assert sel(0, 0.5, 4) == P.PBS_E_ARG
+    assert sel(0, 0.5, P.PBS_FLAG_KEEP_FIRST, ws=16) == P.PBS_E_WORKSPACE   # flag accepted
+    assert sel(0, 0.5, P.PBS_FLAG_KEEP_FIRST | 8, ws=16) == P.PBS_E_ARG
     assert sel(0, 0.5, P.PBS_FLAG_SCORES_IN) == P.PBS_E_ARG   # probabilities in, but none given
     assert sel(0, 0.5, 0, ws=16) == P.PBS_E_WORKSPACE
     attn = lambda perm, minpos, counts, idx: _call(

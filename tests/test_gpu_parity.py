@@ -93,6 +93,32 @@ def test_select_bitexact_given_oracle_probabilities(case):
     assert lists_equal(counts.cpu().numpy(), idx.cpu().numpy(), ref["counts"], ref["idx"])
 
 
+def test_select_keep_first_bitexact(case):
+    """PBS_FLAG_KEEP_FIRST (key block 0 ranked first) against the oracle's keep_first selection,
+    both given the oracle's float32 block probabilities; then the whole attention with those
+    lists against the oracle."""
+    say(case["name"], "pbs_block_select keep-first (probabilities in)")
+    ref, w, sh = case["ref"], case["w"], case["sh"]
+    mode = oracle.KEEP if w.mode == "keep" else oracle.COVERAGE
+    rc, ri = oracle.select_blocks(ref["P"], block=w.block, segment=w.segment, mode=mode,
+                                  param=w.params[0], keep_first=True)
+    counts, idx = run_select(sh, None, None, None, case["scale"], case["cmode"], w.params[0],
+                             blk_scores=dev(ref["P"]),
+                             flags=P.PBS_FLAG_SCORES_IN | P.PBS_FLAG_KEEP_FIRST)
+    assert lists_equal(counts.cpu().numpy(), idx.cpu().numpy(), rc, ri)
+    c = counts.cpu().numpy()
+    first = idx.cpu().numpy()[..., 0]
+    assert ((c == 0) | (first == 0)).all()
+    B, H, N = ref["perm"].shape
+    minpos = ref["perm"].reshape(B, H, N // w.block, w.block).min(-1).astype(np.int32)
+    o, _ = run_attn(sh, case["g"]["q"], dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
+                    dev(ref["perm"]), dev(minpos), counts, idx, case["scale"], want_lse=False)
+    oo, _ = oracle.attention(case["inp"]["q"], case["inp"]["k"], case["inp"]["v"], block=w.block,
+                             segment=w.segment, scale=case["scale"], perm=ref["perm"], counts=rc,
+                             idx=ri)
+    check_attn(o.float().cpu().numpy(), oo, f"{case['name']} keep-first attention")
+
+
 def test_block_probabilities(case):
     say(case["name"], "pbs_block_select (probabilities computed)")
     ref, sh, w = case["ref"], case["sh"], case["w"]

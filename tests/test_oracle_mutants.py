@@ -40,6 +40,9 @@ MUTANTS = {
                                 "cov = Pd[:, keys].sum(axis=1) / Pd[:, keys].sum(axis=1)"),
     "coverage_no_causal_mask": ("Z = np.where(np.arange(t[-1] + 1)[None, :] <= t[:, None], Z, -np.inf)", "Z = Z"),
     "density_own_off_by_one": ("own += i - s0 + 1", "own += i - s0"),
+    "keep_first_at_end": ("order = np.concatenate([np.zeros(order.shape[:-1] + (1,), order.dtype), rest], axis=-1)",
+                          "order = np.concatenate([rest, np.zeros(order.shape[:-1] + (1,), order.dtype)], axis=-1)"),
+    "keep_first_ignored": ("        if keep_first:\n            rest", "        if False:\n            rest"),
     "density_perm_max_position": ("perm[b, h, j * block:(j + 1) * block].min() <= last",
                                   "perm[b, h, j * block:(j + 1) * block].max() <= last"),
 }

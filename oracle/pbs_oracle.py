@@ -262,6 +262,28 @@ def select_blocks(P: np.ndarray, *, block: int, segment: int, mode: str, param: 
 
 # --------------------------------------------------------------------------- O5/O6 attention
 
+def _head_kv(cache: dict, k, v, b: int, h: int):
+    """float64 K and V of KV head (b, h), converted once per head (one head cached)."""
+    if (b, h) not in cache:
+        cache.clear()
+        cache[(b, h)] = (bf16_to_f64(k[b, h]), bf16_to_f64(v[b, h]))
+    return cache[(b, h)]
+
+
+def _attend_rows(Qb, Kf, Vf, keys, t, scale: float):
+    """Rows of queries ``Qb`` (original positions ``t``) over the candidate original keys
+    ``keys``: row r sees the keys with position <= t[r].  Returns the softmax-weighted values
+    and the natural-log normaliser of each row (float64, two passes: max, then sums)."""
+    Z = scale * (Qb @ Kf[keys].T)                               # [rows, |keys|]
+    Z = np.where(keys[None, :] <= t[:, None], Z, -np.inf)
+    m = Z.max(axis=1, keepdims=True)
+    E = np.exp(Z - m)
+    l = E.sum(axis=1, keepdims=True)
+    ob = (E @ Vf[keys]) / l
+    lb = (m + np.log(l))[:, 0]
+    return ob, lb
+
+
 def visible_keys(t: int, *, block: int, segment: int, perm_row: Optional[np.ndarray],
                  sel_blocks: Optional[Sequence[int]], dense: bool) -> np.ndarray:
     """Original positions query t attends to (the set A(t)).
@@ -317,10 +339,7 @@ def attention(q, k, v, *, block: int, segment: int, scale: float,
     cache = {}
     for n_out, (b, g, i) in enumerate(todo):
         h = g // G
-        if (b, h) not in cache:
-            cache.clear()
-            cache[(b, h)] = (bf16_to_f64(k[b, h]), bf16_to_f64(v[b, h]))
-        Kf, Vf = cache[(b, h)]
+        Kf, Vf = _head_kv(cache, k, v, b, h)
         sel = None
         if not dense and counts is not None:
             sel = [int(j) for j in idx[b, g, i, :counts[b, g, i]]]
@@ -331,17 +350,75 @@ def attention(q, k, v, *, block: int, segment: int, scale: float,
         if len(np.unique(keys)) != len(keys):
             raise AssertionError("a key would be counted twice")
         Qb = bf16_to_f64(q[b, g, i * block:(i + 1) * block])
-        Z = scale * (Qb @ Kf[keys].T)                               # [Bs, |A(t_last)|]
-        Z = np.where(keys[None, :] <= t[:, None], Z, -np.inf)
-        m = Z.max(axis=1, keepdims=True)
-        E = np.exp(Z - m)
-        l = E.sum(axis=1, keepdims=True)
-        ob = (E @ Vf[keys]) / l
-        lb = (m + np.log(l))[:, 0]
+        ob, lb = _attend_rows(Qb, Kf, Vf, keys, t, scale)
         if sampled:
             o[n_out], lse[n_out] = ob, lb
         else:
             o[b, g, t], lse[b, g, t] = ob, lb
+    return o, lse
+
+
+def permute_queries(q, perm: np.ndarray) -> np.ndarray:
+    """Queries moved with their tokens: ``q_perm[b, g, p] = q[b, g, perm[b, g // G, p]]``, every
+    query head in its KV head's segment permutation.
+
+    [GS Methodik 1] (Permutationsäquivarianz der Query) and [SS Lemma 3.2]: permuting the
+    queries permutes the output rows the same way.  The default path keeps queries in natural
+    order ([GS Methodik 3, Handling von Queries]); this is the variant that moves them too."""
+    B, Hq = q.shape[:2]
+    Hkv = perm.shape[1]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    return apply_permutation(q, np.repeat(perm, Hq // Hkv, axis=1))
+
+
+def attention_permuted_queries(q_perm, k, v, *, block: int, segment: int, scale: float,
+                               perm: np.ndarray, counts: np.ndarray, idx: np.ndarray,
+                               qblocks: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """Attention with queries and keys both in the segment permutation, output returned in
+    ORIGINAL token order, float64, with its natural-log normaliser.
+
+    Query slot p of head g holds the token at original position t = perm[b, g // G, p]; it
+    belongs to the permuted query block i = p // Bs, whose selected blocks are
+    ``idx[b, g, i, :counts]`` (a selection made on the permuted queries).  It sees
+      A(t) = {j in t's segment, j <= t}  union  {perm[s] : s in a selected key block},
+    the causal test going through the original positions ([SS Fig. 1]; [SS Lemma 3.1] for the
+    keys).  [SS Lemma 3.2]: the rows come out in the permuted order; [SS Theorem 3.3]: putting
+    each row back at its original position t (the inverse permutation) restores the
+    unpermuted result, which is what this returns.
+
+    ``qblocks``: optional (b, g, i) PERMUTED query blocks; then ``o`` is ``[len, Bs, d]`` and
+    ``lse`` ``[len, Bs]`` in slot order (row r of entry n is original position
+    perm[b, g // G, i*Bs + r]), else ``[B, Hq, N, d]`` / ``[B, Hq, N]`` in original order."""
+    B, Hq, Hkv, N, d, G = _check_shape(q_perm.shape, k.shape, block, segment)
+    nb = N // block
+    sampled = qblocks is not None
+    todo = list(qblocks) if sampled else [(b, g, i) for b in range(B) for g in range(Hq) for i in range(nb)]
+    if sampled:
+        o = np.zeros((len(todo), block, d))
+        lse = np.zeros((len(todo), block))
+    else:
+        o = np.zeros((B, Hq, N, d))
+        lse = np.zeros((B, Hq, N))
+    cache = {}
+    for n_out, (b, g, i) in enumerate(todo):
+        h = g // G
+        Kf, Vf = _head_kv(cache, k, v, b, h)
+        slots = np.arange(i * block, (i + 1) * block)
+        t = perm[b, h, slots].astype(np.int64)                      # original positions
+        s0 = (i * block // segment) * segment
+        sel = [int(j) for j in idx[b, g, i, :counts[b, g, i]]]
+        picked = [perm[b, h, j * block:(j + 1) * block].astype(np.int64) for j in sel]
+        own = np.arange(s0, int(t.max()) + 1)
+        keys = np.concatenate(picked + [own]) if picked else own
+        if len(np.unique(keys)) != len(keys):
+            raise AssertionError("a key would be counted twice")
+        Qb = bf16_to_f64(q_perm[b, g, slots])
+        ob, lb = _attend_rows(Qb, Kf, Vf, keys, t, scale)     # causal test on original positions
+        if sampled:
+            o[n_out], lse[n_out] = ob, lb
+        else:
+            o[b, g, t], lse[b, g, t] = ob, lb                 # the inverse permutation of the rows
     return o, lse
 
 

@@ -6,7 +6,8 @@ oracle and ``test_oracle_mutants`` runs them on copies of the oracle with a plan
 Pages (arXiv 2510.21270, "Sparser Block-Sparse Attention via Token Permutation"):
   [SS] sciencestack.ai page: Fig. 1 caption (B=1, S=4 segmented permutation; own-segment
        blocks computed, inter-segment blocks skippable), Fig. 2 caption (coverage), Lemma 3.1
-       (joint key/value permutation invariance).
+       (joint key/value permutation invariance), Lemma 3.2 (query permutation equivariance),
+       Theorem 3.3 (invariance under the inverse transformation).
   [GS] gist.science summary, Methodik 1-4.
   [SK] skillmd.com "Sparser Block Attention", Implementation Steps (active-block count rule,
        inverse permutation).
@@ -413,6 +414,73 @@ def pin_lemma_3_1(O):
         ref = bf.attention(bf.mat(q[0, g]), bf.mat(out["k_perm"][0, h]), bf.mat(out["v_perm"][0, h]),
                            vis_perm, 0.4)
         assert np.allclose(out["o"][0, g], ref, atol=1e-12), g
+
+
+def _tiny_qperm(O, seed, mode, param, N=32, Bs=4, S=8, Hq=4, Hkv=2, d=8, scale=0.4):
+    """The query-permutation variant end to end in the oracle: scores, permutation, queries
+    moved with their tokens, selection on the permuted queries, attention."""
+    q, k, v = _tiny(seed, Hq=Hq, Hkv=Hkv, N=N, d=d, scale_k=1.7)
+    sc = O.key_scores(q, k, block=Bs, segment=S, scale=scale)
+    perm = O.segment_permutation(sc, segment=S)
+    qp = O.permute_queries(q, perm)
+    kp = O.apply_permutation(k, perm)
+    P = O.block_probabilities(qp, kp, block=Bs, segment=S, scale=scale)
+    counts, idx = O.select_blocks(P, block=Bs, segment=S, mode=mode, param=param)
+    o, lse = O.attention_permuted_queries(qp, k, v, block=Bs, segment=S, scale=scale, perm=perm,
+                                          counts=counts, idx=idx)
+    return q, k, v, perm, qp, counts, idx, o, lse
+
+
+def pin_qperm_bruteforce(O):
+    """Queries and keys both permuted, computed by brute force entirely in permuted slots:
+    slot p (token perm[p]) sees key slot s when s is in p's segment and perm[s] <= perm[p],
+    or s lies in a block selected for p's permuted query block; softmax over the permuted
+    copies, then each row is put back at its original position ([SS Lemma 3.2, Theorem 3.3]).
+    Also checks the query gather head by head from its definition (query head g moves with KV
+    head g // G)."""
+    N, Bs, S, Hq, Hkv, d = 32, 4, 8, 4, 2, 8
+    G = Hq // Hkv
+    q, k, v, perm, qp, counts, idx, o, lse = _tiny_qperm(O, 71, O.KEEP, 0.5)
+    for g in range(Hq):
+        h = g // G
+        pr = perm[0, h]
+        assert any(pr[pr[p]] != p for p in range(N))
+        for p in range(N):
+            assert (qp[0, g, p] == q[0, g, int(pr[p])]).all()
+        kp = [k[0, h, int(pr[s])] for s in range(N)]
+        vp = [v[0, h, int(pr[s])] for s in range(N)]
+        vis = [[0] * N for _ in range(N)]
+        for p in range(N):
+            i = p // Bs
+            sel = set(int(j) for j in idx[0, g, i, :counts[0, g, i]])
+            for sl in range(N):
+                same = sl // S == p // S and int(pr[sl]) <= int(pr[p])
+                vis[p][sl] = int(same or (sl // Bs) in sel)
+        ref = bf.attention(bf.mat(qp[0, g]), bf.mat(np.array(kp)), bf.mat(np.array(vp)), vis, 0.4)
+        for p in range(N):
+            assert np.allclose(o[0, g, int(pr[p])], ref[p], atol=1e-12), (g, p)
+
+
+def pin_qperm_keep_one_is_dense(O):
+    """[SS Theorem 3.3]: with every candidate block kept, attention on permuted queries and
+    keys followed by the inverse permutation of the output equals plain causal attention."""
+    q, k, v, perm, qp, counts, idx, o, lse = _tiny_qperm(O, 73, O.KEEP, 1.0)
+    od, ld = O.dense_causal(q, k, v, block=4, scale=0.4)
+    assert np.abs(o - od).max() < 1e-12 and np.abs(lse - ld).max() < 1e-12
+
+
+def pin_qperm_identity_is_natural_order(O):
+    """The identity permutation reduces the variant to plain block-sparse attention in the
+    natural order (the same lists give the same output)."""
+    N, Bs, S = 32, 4, 8
+    q, k, v = _tiny(77, Hq=4, Hkv=2, N=N, d=8)
+    ident = np.broadcast_to(np.arange(N, dtype=np.int32), (1, 2, N)).copy()
+    P = O.block_probabilities(q, k, block=Bs, segment=S, scale=0.4)
+    counts, idx = O.select_blocks(P, block=Bs, segment=S, mode=O.KEEP, param=0.3)
+    o1, l1 = O.attention_permuted_queries(O.permute_queries(q, ident), k, v, block=Bs, segment=S,
+                                          scale=0.4, perm=ident, counts=counts, idx=idx)
+    o2, l2 = O.attention(q, k, v, block=Bs, segment=S, scale=0.4, perm=None, counts=counts, idx=idx)
+    assert np.abs(o1 - o2).max() < 1e-12 and np.abs(l1 - l2).max() < 1e-12
 
 
 def pin_keep_one_is_dense(O):

@@ -33,8 +33,8 @@ MUTANTS = {
                          "Z = np.where(keys[None, :] < t[:, None], Z, -np.inf)"),
     "attn_no_scale": ("Z = scale * (Qb @ Kf[keys].T)", "Z = (Qb @ Kf[keys].T)"),
     "attn_values_are_keys": ("ob = (E @ Vf[keys]) / l", "ob = (E @ Kf[keys]) / l"),
-    "attn_gqa_modulo": ("        h = g // G\n        if (b, h) not in cache:\n            cache.clear()\n            cache[(b, h)] = (bf16_to_f64(k[b, h])",
-                        "        h = g % Hkv\n        if (b, h) not in cache:\n            cache.clear()\n            cache[(b, h)] = (bf16_to_f64(k[b, h])"),
+    "attn_gqa_modulo": ("        h = g // G\n        Kf, Vf = _head_kv(cache, k, v, b, h)\n        sel = None",
+                        "        h = g % Hkv\n        Kf, Vf = _head_kv(cache, k, v, b, h)\n        sel = None"),
     "attn_lse_log2": ("lb = (m + np.log(l))[:, 0]", "lb = (m + np.log2(l))[:, 0]"),
     "coverage_sparse_softmax": ("cov = Pd[:, keys].sum(axis=1)",
                                 "cov = Pd[:, keys].sum(axis=1) / Pd[:, keys].sum(axis=1)"),
@@ -43,6 +43,12 @@ MUTANTS = {
     "keep_first_at_end": ("order = np.concatenate([np.zeros(order.shape[:-1] + (1,), order.dtype), rest], axis=-1)",
                           "order = np.concatenate([rest, np.zeros(order.shape[:-1] + (1,), order.dtype)], axis=-1)"),
     "keep_first_ignored": ("        if keep_first:\n            rest", "        if False:\n            rest"),
+    "qperm_mask_on_slots": ("ob, lb = _attend_rows(Qb, Kf, Vf, keys, t, scale)     # causal test",
+                            "ob, lb = _attend_rows(Qb, Kf, Vf, keys, slots, scale)     # causal test"),
+    "qperm_output_not_inverted": ("o[b, g, t], lse[b, g, t] = ob, lb                 # the inverse",
+                                  "o[b, g, slots], lse[b, g, slots] = ob, lb                 # the inverse"),
+    "qperm_heads_modulo": ("return apply_permutation(q, np.repeat(perm, Hq // Hkv, axis=1))",
+                           "return apply_permutation(q, np.tile(perm, (1, Hq // Hkv, 1)))"),
     "density_perm_max_position": ("perm[b, h, j * block:(j + 1) * block].min() <= last",
                                   "perm[b, h, j * block:(j + 1) * block].max() <= last"),
 }

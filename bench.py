@@ -208,6 +208,8 @@ def main():
     ap.add_argument("--keep", type=float, default=None, help="override the keep ratio")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-qperm", action="store_true",
+                    help="skip timing the query-permutation variant")
     ap.add_argument("--no-hybrid", action="store_true",
                     help="skip timing pbs_attn_fwd_hybrid (own segment from the original K/V)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -368,6 +370,46 @@ def main():
                   "max_abs_diff_vs_main_output": max_diff}
         del o_h
 
+    # The query-permutation variant (queries moved with their tokens, selection on the permuted
+    # queries, output rows written back in original order): the steps after the key permutation.
+    qperm = None
+    if not args.no_qperm:
+        qp = torch.empty_like(q)
+        c2, i2 = torch.empty_like(bf.counts), torch.empty_like(bf.idx)
+        o_q = torch.empty_like(q)
+        eq = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+        def qstep(rec):
+            if rec:
+                eq[0].record(stream)
+            P.pbs_permute_queries(sh, bf.perm, q, qp, stream=stream)
+            if rec:
+                eq[1].record(stream)
+            P.pbs_block_select(sh, qp, bf.k_perm, bf.k_pool, scale, mode, param, None, 0, c2, i2,
+                               bf.workspace, stream=stream)
+            if rec:
+                eq[2].record(stream)
+            P.pbs_attn_fwd_permuted_queries(sh, qp, bf.k_perm, bf.v_perm, bf.perm, bf.blk_minpos,
+                                            c2, i2, scale, o_q, None, stream=stream)
+            if rec:
+                eq[3].record(stream)
+
+        for _ in range(max(1, args.warmup)):
+            qstep(False)
+        torch.cuda.synchronize()
+        qt = np.zeros(3)
+        for _ in range(args.steps):
+            qstep(True)
+            eq[3].synchronize()
+            qt += [eq[j].elapsed_time(eq[j + 1]) for j in range(3)]
+        qt /= args.steps
+        qprefill = float(stage[0] + stage[1] + qt.sum())
+        qperm = {"permute_queries_ms": round(float(qt[0]), 4), "select_ms": round(float(qt[1]), 4),
+                 "attention_ms": round(float(qt[2]), 4), "prefill_ms": round(qprefill, 4),
+                 "selected_blocks": int(c2.sum().item()),
+                 "max_abs_diff_vs_main_output": float((o_q.float() - bf.o.float()).abs().max().item())}
+        del qp, c2, i2, o_q
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -423,6 +465,7 @@ def main():
             "work_per_launch": f"{computed} computed blocks x {flop_per_block / 1e6:.3f} MFLOP",
         },
         "hybrid_own_segment_natural": hybrid,
+        "permuted_queries": qperm,
         "cpu_baseline": cpu,
         "input_generation_s": round(gen_s, 1),
         "context": "pages report up to 2.75x end-to-end TTFT vs FlashAttention at 256K on unnamed hardware",

@@ -32,7 +32,8 @@ PBS_FLAG_SCORES_IN = 1
 PBS_FLAG_KEEP_FIRST = 2
 
 ENTRY_POINTS = ("pbs_workspace_bytes", "pbs_max_offdiag", "pbs_strerror", "pbs_score",
-                "pbs_permute", "pbs_block_select", "pbs_attn_fwd", "pbs_attn_fwd_hybrid")
+                "pbs_permute", "pbs_block_select", "pbs_attn_fwd", "pbs_attn_fwd_hybrid",
+                "pbs_permute_queries", "pbs_attn_fwd_permuted_queries")
 
 
 class PbsError(RuntimeError):
@@ -78,8 +79,11 @@ def lib():
                                    _P, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]
     L.pbs_attn_fwd.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
     L.pbs_attn_fwd_hybrid.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
+    L.pbs_permute_queries.argtypes = [S, _P, _P, _P, _P]
+    L.pbs_attn_fwd_permuted_queries.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                                _P, _P, _P]
     for name in ("pbs_score", "pbs_permute", "pbs_block_select", "pbs_attn_fwd",
-                 "pbs_attn_fwd_hybrid"):
+                 "pbs_attn_fwd_hybrid", "pbs_permute_queries", "pbs_attn_fwd_permuted_queries"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -164,6 +168,19 @@ def pbs_attn_fwd_hybrid(shape, q, k_perm, v_perm, k, v, counts, idx, scale, o, l
     _check(lib().pbs_attn_fwd_hybrid(ctypes.byref(shape), _ptr(q), _ptr(k_perm), _ptr(v_perm),
                                      _ptr(k), _ptr(v), _ptr(counts), _ptr(idx), scale, _ptr(o),
                                      _ptr(lse), _stream(stream)))
+
+
+def pbs_permute_queries(shape, perm, q, q_perm, stream=None):
+    _check(lib().pbs_permute_queries(ctypes.byref(shape), _ptr(perm), _ptr(q), _ptr(q_perm),
+                                     _stream(stream)))
+
+
+def pbs_attn_fwd_permuted_queries(shape, q_perm, k_perm, v_perm, perm, blk_minpos, counts, idx,
+                                  scale, o, lse=None, stream=None):
+    _check(lib().pbs_attn_fwd_permuted_queries(ctypes.byref(shape), _ptr(q_perm), _ptr(k_perm),
+                                               _ptr(v_perm), _ptr(perm), _ptr(blk_minpos),
+                                               _ptr(counts), _ptr(idx), scale, _ptr(o), _ptr(lse),
+                                               _stream(stream)))
 
 
 def default_scale(head_dim: int) -> float:

@@ -115,6 +115,19 @@ int pbs_permute(const pbs_shape* shape, const float* scores, const uint16_t* k,
                                        static_cast<hipStream_t>(stream)));
 }
 
+int pbs_permute_queries(const pbs_shape* shape, const int32_t* perm, const uint16_t* q,
+                        uint16_t* q_perm, void* stream) {
+  Dims d;
+  int st = check_shape(shape, &d);
+  if (st != PBS_OK) return st;
+  if (empty(d)) return PBS_OK;
+  const void* const req[] = {perm, q, q_perm};
+  if ((st = check_required(req)) != PBS_OK) return st;
+  if (static_cast<const void*>(q) == static_cast<const void*>(q_perm)) return PBS_E_ARG;
+  return status_of(pbs::launch_permute_queries(d, perm, q, q_perm,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int pbs_block_select(const pbs_shape* shape, const uint16_t* q, const uint16_t* k_perm,
                      const float* k_pool, float scale, int mode, double param,
                      float* blk_scores, int flags, int32_t* counts, int32_t* idx,
@@ -165,6 +178,25 @@ int pbs_attn_fwd(const pbs_shape* shape, const uint16_t* q, const uint16_t* k,
   const int mode = !counts ? 0 : (perm ? 1 : 2);
   return status_of(pbs::launch_attn(d, q, k, v, perm, blk_minpos, counts, idx, nullptr, nullptr,
                                     mode, scale, o, lse, static_cast<hipStream_t>(stream)));
+}
+
+int pbs_attn_fwd_permuted_queries(const pbs_shape* shape, const uint16_t* q_perm,
+                                  const uint16_t* k_perm, const uint16_t* v_perm,
+                                  const int32_t* perm, const int32_t* blk_minpos,
+                                  const int32_t* counts, const int32_t* idx, float scale,
+                                  uint16_t* o, float* lse, void* stream) {
+  Dims d;
+  int st = check_shape(shape, &d);
+  if (st != PBS_OK) return st;
+  if (!finite_positive(scale)) return PBS_E_ARG;
+  if (empty(d)) return PBS_OK;
+  const void* const req[] = {q_perm, k_perm, v_perm, perm, counts, idx, o};
+  if ((st = check_required(req)) != PBS_OK) return st;
+  if ((st = check_optional(blk_minpos)) != PBS_OK) return st;
+  if ((st = check_optional(lse)) != PBS_OK) return st;
+  return status_of(pbs::launch_attn(d, q_perm, k_perm, v_perm, perm, blk_minpos, counts, idx,
+                                    nullptr, nullptr, 4, scale, o, lse,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 int pbs_attn_fwd_hybrid(const pbs_shape* shape, const uint16_t* q, const uint16_t* k_perm,

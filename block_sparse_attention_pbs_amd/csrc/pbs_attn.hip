@@ -55,7 +55,8 @@ struct AttnArgs {
   float* lse;
   int B, Hq, Hkv, G, N, nb, bps, max_off;
   int mode;      // 0 dense causal, 1 permuted PBS, 2 identity-order PBS, 3 permuted off-diagonal
-                 // blocks with the own segment in natural order
+                 // blocks with the own segment in natural order, 4 permuted PBS with permuted
+                 // queries (output rows written back at their original positions)
   int xcd_map;   // 1: total work items divisible by 8, use the XCD-grouped order
   float c;       // scale * log2(e)
   // Element offsets of the K/V stage tiles in LDS.  Passed at run time on purpose: the compiler
@@ -245,7 +246,7 @@ __device__ __forceinline__ void issue_stage(const AttnArgs& a, const Rsrc& rr, S
     load_lds16(rv, Vst + n * 512, static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2),
                base);
   }
-  if (st.masked && a.mode == 1 && w == 0)
+  if (st.masked && (a.mode == 1 || a.mode == 4) && w == 0)
     load_lds4(rp, Pst, static_cast<uint32_t>(lane * 4), static_cast<uint32_t>(st.key0) * 4);
 }
 
@@ -276,7 +277,7 @@ __device__ __forceinline__ f32x16 mask_init(const int32_t* Ps, int key0, int kt,
   for (int rb = 0; rb < 4; ++rb) {
     const int key = kt * 32 + rb * 8 + hl * 4;
     int4 pos;
-    if constexpr (MODE == 1) {
+    if constexpr (MODE == 1 || MODE == 4) {
       pos = *reinterpret_cast<const int4*>(&Ps[key]);
     } else {
       const int p0 = key0 + key;
@@ -470,6 +471,9 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   __shared__ uint16_t offw[kOffWindow];
   __shared__ uint16_t ownl[kOwnMax];
   __shared__ int own_count;
+  __shared__ int qmax_w[C::NW];
+  // Visit-list and key-mask rules: mode 4 (permuted queries) walks the permuted keys like mode 1.
+  constexpr int LM = (MODE == 4) ? 1 : MODE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -493,7 +497,11 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   const int h = g / a.G;
   const size_t q_head = (static_cast<size_t>(b) * a.Hq + g) * a.N;
   const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;
-  const int t = i * BS + w * 32 + c32;       // this lane's query row (both halves share it)
+  // This lane's query row (both halves share it): slot ts of the query tensor; its original
+  // position t drives the causal test and the output row.  Queries are in natural order except
+  // in mode 4, where slot ts holds the token at perm[ts] and the row is written back there.
+  const int ts = i * BS + w * 32 + c32;
+  const int t = (MODE == 4) ? min(max(a.perm[kv_head + ts], 0), a.N - 1) : ts;
   const uint32_t head_bytes = static_cast<uint32_t>(a.N) * D * 2;
   Rsrc rr;
   rr.k = make_rsrc(a.k + kv_head * D, head_bytes);
@@ -504,7 +512,7 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
       make_rsrc(a.perm ? a.perm + kv_head : nullptr, a.perm ? static_cast<uint32_t>(a.N) * 4 : 0u);
 
   StageIter it;
-  it.mode = MODE;
+  it.mode = LM;
   it.halves = C::HALVES;
   it.i = i;
   it.seg_first = (i / a.bps) * a.bps;
@@ -526,20 +534,30 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
     // Visible own-segment blocks, compacted by wave 0.  Permuted order: a block is skipped when
     // its smallest original position is after the query block's last row; every visited block
     // is masked per key.  Identity order: blocks up to the diagonal, only the diagonal masked.
+    int last_row = i * BS + BS - 1;   // the latest original position among the block's rows
+    if constexpr (MODE == 4) {
+      int mx = t;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+      if (lane == 0) qmax_w[w] = mx;
+      __syncthreads();
+      last_row = qmax_w[0];
+#pragma unroll
+      for (int ww = 1; ww < C::NW; ++ww) last_row = max(last_row, qmax_w[ww]);
+    }
     if (w == 0) {
-      const int last_row = i * BS + BS - 1;
       const int32_t* mp = a.minpos ? a.minpos + kv_head / BS + it.seg_first : nullptr;
       int n = 0;
       for (int o0 = 0; o0 < a.bps; o0 += 64) {
         const int o = o0 + lane;
         const int jj = it.seg_first + o;
         bool vis = false;
-        if (o < a.bps) vis = (MODE != 1) ? (jj <= i) : (mp == nullptr || mp[o] <= last_row);
+        if (o < a.bps) vis = (LM != 1) ? (jj <= i) : (mp == nullptr || mp[o] <= last_row);
         const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
         const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
         if (vis)
-          ownl[n + before] = static_cast<uint16_t>(jj | ((MODE == 1 || jj == i) ? 0x8000 : 0));
+          ownl[n + before] = static_cast<uint16_t>(jj | ((LM == 1 || jj == i) ? 0x8000 : 0));
         n += __builtin_popcountll(bal);
       }
       if (lane == 0) own_count = n;
@@ -552,7 +570,7 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   if (MODE == 0) {
     n_unm = i;
     n_msk = 1;
-  } else if (MODE == 1) {
+  } else if (LM == 1) {
     n_unm = it.n_off;
     n_msk = it.n_own;
   } else {
@@ -563,7 +581,7 @@ __global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
   // Q fragments (B operand of S^T = K Q^T): lane holds q[t][ks*16 + hl*8 .. +8]
   bf16x8 qf[C::NKS];
   {
-    const uint16_t* qrow = a.q + (q_head + t) * D + hl * 8;
+    const uint16_t* qrow = a.q + (q_head + ts) * D + hl * 8;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
   }
@@ -611,6 +629,7 @@ hipError_t launch_attn_t(const Dims& d, const AttnArgs& a, hipStream_t stream) {
   if (a.mode == 1) return launch(attn_fwd_kernel<D, BS, 1>, dim3(total), block, 0, stream, a);
   if (a.mode == 2) return launch(attn_fwd_kernel<D, BS, 2>, dim3(total), block, 0, stream, a);
   if (a.mode == 3) return launch(attn_fwd_kernel<D, BS, 3>, dim3(total), block, 0, stream, a);
+  if (a.mode == 4) return launch(attn_fwd_kernel<D, BS, 4>, dim3(total), block, 0, stream, a);
   return launch(attn_fwd_kernel<D, BS, 0>, dim3(total), block, 0, stream, a);
 }
 

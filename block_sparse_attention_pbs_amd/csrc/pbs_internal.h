@@ -36,6 +36,10 @@ hipError_t launch_permute(const Dims& d, const float* scores, const uint16_t* k,
                           const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
                           float* k_pool, int32_t* blk_minpos, hipStream_t stream);
 
+// The query-permutation variant: q_perm[b, g, p] = q[b, g, perm[b, g / G, p]].
+hipError_t launch_permute_queries(const Dims& d, const int32_t* perm, const uint16_t* q,
+                                  uint16_t* q_perm, hipStream_t stream);
+
 // Workspace of pbs_block_select: pooled queries (and pooled keys when not supplied).
 size_t select_workspace_bytes(const Dims& d);
 hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t* k_perm,
@@ -44,7 +48,8 @@ hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t*
                                int32_t* idx, void* ws, hipStream_t stream);
 
 // mode: 0 dense causal, 1 PBS with a permutation, 2 PBS in the identity order, 3 PBS with
-// permuted off-diagonal blocks and the own segment read from k_orig/v_orig in natural order.
+// permuted off-diagonal blocks and the own segment read from k_orig/v_orig in natural order,
+// 4 PBS with permuted queries (q holds them; rows are written back at their original positions).
 hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const int32_t* perm, const int32_t* blk_minpos, const int32_t* counts,
                        const int32_t* idx, const uint16_t* k_orig, const uint16_t* v_orig,

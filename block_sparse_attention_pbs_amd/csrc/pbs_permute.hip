@@ -107,7 +107,46 @@ hipError_t launch_gather_t(const Dims& d, const GatherArgs& a, hipStream_t strea
   return launch(gather_kernel<D, BS>, dim3(d.nb, d.B * d.Hkv), dim3(256), 0, stream, a);
 }
 
+struct QGatherArgs {
+  const uint16_t* q;
+  const int32_t* perm;
+  uint16_t* q_perm;
+  int N, Hq, Hkv, G;
+};
+
+// Queries moved with their tokens (the query-permutation variant): row p of query head g takes
+// the query row perm[b, g / G, p] (sciencestack.ai page, Lemma 3.2; gist.science summary,
+// Methodik 1, query permutation equivariance).  One workgroup per (batch * query head, 64 rows);
+// D/8 lanes per row, each moving 16 bytes, so every row read and write is one coalesced run.
+template <int D>
+__global__ __launch_bounds__(256) void qgather_kernel(QGatherArgs a) {
+  constexpr int CH = D / 8;
+  constexpr int ROWS = 64;
+  const int bg = blockIdx.y;                       // b * Hq + g
+  const int b = bg / a.Hq, g = bg - b * a.Hq;
+  const size_t qhead = static_cast<size_t>(bg) * a.N;
+  const size_t phead = (static_cast<size_t>(b) * a.Hkv + g / a.G) * a.N;
+  const int c = threadIdx.x % CH;
+  for (int r = threadIdx.x / CH; r < ROWS; r += 256 / CH) {
+    const int p = blockIdx.x * ROWS + r;
+    if (p >= a.N) break;
+    const int src = min(max(a.perm[phead + p], 0), a.N - 1);
+    const u32x4 x = *reinterpret_cast<const u32x4*>(a.q + (qhead + src) * D + c * 8);
+    *reinterpret_cast<u32x4*>(a.q_perm + (qhead + p) * D + c * 8) = x;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_permute_queries(const Dims& d, const int32_t* perm, const uint16_t* q,
+                                  uint16_t* q_perm, hipStream_t stream) {
+  QGatherArgs qa;
+  qa.q = q; qa.perm = perm; qa.q_perm = q_perm;
+  qa.N = d.N; qa.Hq = d.Hq; qa.Hkv = d.Hkv; qa.G = d.G;
+  const dim3 grid((d.N + 63) / 64, d.B * d.Hq);
+  if (d.d == 128) return launch(qgather_kernel<128>, grid, dim3(256), 0, stream, qa);
+  return launch(qgather_kernel<64>, grid, dim3(256), 0, stream, qa);
+}
 
 hipError_t launch_permute(const Dims& d, const float* scores, const uint16_t* k,
                           const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,

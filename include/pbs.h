@@ -125,6 +125,22 @@ int pbs_permute(const pbs_shape* shape, const float* scores, const uint16_t* k,
                 float* k_pool, int32_t* blk_minpos, void* stream);
 
 /*
+ * pbs_permute_queries -- queries moved with their tokens (the query-permutation variant).
+ * Passage: sciencestack.ai page, Lemma 3.2 (permuting the queries permutes the output rows the
+ * same way) and Theorem 3.3 (permuting queries and keys/values, then applying the inverse
+ * permutation to the output, restores the result); gist.science summary, Methodik 1 and
+ * Methodik 3 ("Handling von Queries": the default keeps queries in natural order because
+ * moving them gave only marginal gains; this entry point is the variant that moves them).
+ *
+ *   q_perm[b,g,p,:] = q[b,g,perm[b,g/G,p],:]   (bit copy; query head g follows its KV head)
+ *   perm   [B,Hkv,N] int32 from pbs_permute
+ *   q      [B,Hq,N,d] bf16;  q_perm [B,Hq,N,d] bf16, written (must not alias q)
+ * Out-of-range perm entries are clamped into [0, N) (memory-safe, result unspecified).
+ */
+int pbs_permute_queries(const pbs_shape* shape, const int32_t* perm, const uint16_t* q,
+                        uint16_t* q_perm, void* stream);
+
+/*
  * pbs_block_select -- which earlier-segment key blocks each query block computes.
  * Passage: gist.science summary, Methodik 4 ("Block-Auswahl": block importance from mean
  * pooling on the permuted keys); sciencestack.ai page, Fig. 1 caption (blocks of the own,
@@ -183,6 +199,32 @@ int pbs_attn_fwd(const pbs_shape* shape, const uint16_t* q, const uint16_t* k,
                  const uint16_t* v, const int32_t* perm, const int32_t* blk_minpos,
                  const int32_t* counts, const int32_t* idx, float scale, uint16_t* o,
                  float* lse, void* stream);
+
+/*
+ * pbs_attn_fwd_permuted_queries -- PBS attention with the queries in the segment permutation
+ * too; the output comes back in ORIGINAL token order.
+ * Passage: sciencestack.ai page, Lemma 3.2 and Theorem 3.3 (the inverse permutation of the
+ * output restores the unpermuted result), Fig. 1 caption (own segment under the causal mask);
+ * gist.science summary, Methodik 4 ("Kernel": permutation, block selection and inverse
+ * permutation handled by the attention kernels).
+ *
+ * Query slot p of head g holds the token at original position t = perm[b,g/G,p]; it belongs
+ * to permuted query block i = p / Bs and attends to every key of the kept blocks
+ * idx[b,g,i,0..counts) (a selection made on q_perm with pbs_block_select) and to every key of
+ * its own segment with original position <= t.  Its output row is written at o[b,g,t,:] (and
+ * lse[b,g,t]), so no separate inverse-permutation pass is needed.
+ *   q_perm         [B,Hq,N,d] bf16 from pbs_permute_queries
+ *   k_perm, v_perm [B,Hkv,N,d] bf16 from pbs_permute;  perm [B,Hkv,N] int32 (required)
+ *   blk_minpos     [B,Hkv,N/Bs] int32 or NULL (own-segment blocks whose smallest position is
+ *                  after every row of the query block are skipped)
+ *   counts, idx    required; o [B,Hq,N,d] bf16 and lse [B,Hq,N] (or NULL) in original order
+ * Errors as pbs_attn_fwd.
+ */
+int pbs_attn_fwd_permuted_queries(const pbs_shape* shape, const uint16_t* q_perm,
+                                  const uint16_t* k_perm, const uint16_t* v_perm,
+                                  const int32_t* perm, const int32_t* blk_minpos,
+                                  const int32_t* counts, const int32_t* idx, float scale,
+                                  uint16_t* o, float* lse, void* stream);
 
 /*
  * pbs_attn_fwd_hybrid -- the same attention as pbs_attn_fwd in PBS mode, with the own segment

@@ -72,6 +72,16 @@ def test_errors_before_any_launch():
     assert attn(None, None, fake, None) == P.PBS_E_ARG          # counts without idx
     assert attn(fake, None, None, None) == P.PBS_E_ARG          # permutation in dense mode
     assert attn(fake, fake + 4, fake, fake) == P.PBS_E_ALIGN
+    pq = lambda perm, q, qp: _call("pbs_permute_queries", S, perm, q, qp, None)
+    assert pq(None, fake, fake + 256) == P.PBS_E_ARG
+    assert pq(fake, fake, fake) == P.PBS_E_ARG                  # in place is rejected
+    assert pq(fake, fake + 8, fake + 256) == P.PBS_E_ALIGN
+    aq = lambda perm, counts, minpos=None: _call(
+        "pbs_attn_fwd_permuted_queries", S, fake, fake, fake, perm, minpos, counts, fake, 0.1,
+        fake, None, None)
+    assert aq(None, fake) == P.PBS_E_ARG                         # the permutation is required
+    assert aq(fake, None) == P.PBS_E_ARG                         # lists are required
+    assert aq(fake, fake, minpos=fake + 4) == P.PBS_E_ALIGN
     hyb = lambda kp, k, counts, lse=None: _call(
         "pbs_attn_fwd_hybrid", S, fake, kp, fake, k, fake, counts, fake, 0.1, fake, lse, None)
     assert hyb(fake, fake, None) == P.PBS_E_ARG                  # lists are required

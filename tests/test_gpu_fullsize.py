@@ -8,6 +8,8 @@ times (the same entry points, shapes and parameters), on outputs the oracle can 
   * attention with the oracle's permutation and lists: sampled query blocks (the first and last
     block of every segment and every 16th block) of a few query heads, max-abs 2e-2 / mean-abs
     2e-3, through pbs_attn_fwd and through pbs_attn_fwd_hybrid;
+  * the query-permutation variant: query gather and selection bit-exact, attention on sampled
+    permuted query blocks;
   * the whole GPU pipeline end to end: the same sampled blocks against the whole oracle pipeline.
 
 Each workload is generated once per module (seconds) and the oracle stages cost tens of seconds
@@ -128,6 +130,43 @@ def test_full_attention_sampled(full):
         gl = np.stack([lhg[b, g, i * w.block:(i + 1) * w.block] for b, g, i in samples])
         check_attn(got, oo, f"{full['name']} hybrid attention param {param}")
         assert np.abs(gl - ol).max() < 1e-3
+
+
+def test_full_permuted_queries_sampled(full):
+    """The query-permutation variant at full size, in the launch configuration bench.py times:
+    the query gather bit-exact on every row, the selection on the permuted queries bit-exact
+    given the oracle's float32 block probabilities, and the attention (rows written back at
+    their original positions) on sampled permuted query blocks."""
+    w, ref, inp, g = full["w"], full["ref"], full["inp"], full["g"]
+    say(full["name"], "permuted queries")
+    perm = ref["perm"]
+    qp_ref = oracle.permute_queries(inp["q"], perm)
+    qp = torch.empty_like(g["q"])
+    P.pbs_permute_queries(full["sh"], dev(perm), g["q"], qp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(qp), qp_ref)
+    mode = oracle.KEEP if w.mode == "keep" else oracle.COVERAGE
+    Pq = oracle.block_probabilities(qp_ref, ref["k_perm"], block=w.block, segment=w.segment,
+                                    scale=full["scale"])
+    rc, ri = oracle.select_blocks(Pq, block=w.block, segment=w.segment, mode=mode, param=w.params[0])
+    counts, idx = run_select(full["sh"], None, None, None, full["scale"],
+                             P.PBS_SELECT_KEEP_RATIO if w.mode == "keep" else P.PBS_SELECT_COVERAGE,
+                             w.params[0], blk_scores=dev(Pq), flags=P.PBS_FLAG_SCORES_IN)
+    assert lists_equal(counts.cpu().numpy(), idx.cpu().numpy(), rc, ri)
+    B, H, N = perm.shape
+    minpos = perm.reshape(B, H, N // w.block, w.block).min(-1).astype(np.int32)
+    o = torch.empty_like(g["q"])
+    P.pbs_attn_fwd_permuted_queries(full["sh"], qp, dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
+                                    dev(perm), dev(minpos), counts, idx, full["scale"], o, None)
+    torch.cuda.synchronize()
+    G = w.heads_q // w.heads_kv
+    samples = _sample_blocks(w, sorted({0, w.heads_q - 1}))
+    oo, _ = oracle.attention_permuted_queries(qp_ref, inp["k"], inp["v"], block=w.block,
+                                              segment=w.segment, scale=full["scale"], perm=perm,
+                                              counts=rc, idx=ri, qblocks=samples)
+    og = o.float().cpu().numpy()
+    got = np.stack([og[b, gg, perm[b, gg // G, i * w.block:(i + 1) * w.block]] for b, gg, i in samples])
+    check_attn(got, oo, f"{full['name']} permuted-query attention ({len(samples)} blocks)")
 
 
 def test_full_end_to_end_sampled(full):

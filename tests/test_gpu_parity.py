@@ -171,6 +171,58 @@ def test_hybrid_own_segment_natural(case):
     assert np.abs(lse.cpu().numpy() - ref["lse"]).max() < 1e-3
 
 
+def test_permuted_queries(case):
+    """The query-permutation variant: queries gathered with their KV head's permutation
+    (bit-exact against the oracle), selection on the permuted queries (bit-exact given the
+    oracle's float32 block probabilities), attention with rows written back at their original
+    positions against the oracle (sciencestack.ai page, Lemma 3.2 / Theorem 3.3)."""
+    say(case["name"], "permuted queries")
+    ref, w, sh, g, inp = case["ref"], case["w"], case["sh"], case["g"], case["inp"]
+    perm = ref["perm"]
+    qp_ref = oracle.permute_queries(inp["q"], perm)
+    qp = torch.empty_like(g["q"])
+    P.pbs_permute_queries(sh, dev(perm), g["q"], qp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(qp), qp_ref)
+    mode = oracle.KEEP if w.mode == "keep" else oracle.COVERAGE
+    Pq = oracle.block_probabilities(qp_ref, ref["k_perm"], block=w.block, segment=w.segment,
+                                    scale=case["scale"])
+    rc, ri = oracle.select_blocks(Pq, block=w.block, segment=w.segment, mode=mode, param=w.params[0])
+    counts, idx = run_select(sh, None, None, None, case["scale"], case["cmode"], w.params[0],
+                             blk_scores=dev(Pq), flags=P.PBS_FLAG_SCORES_IN)
+    assert lists_equal(counts.cpu().numpy(), idx.cpu().numpy(), rc, ri)
+    oo, ol = oracle.attention_permuted_queries(qp_ref, inp["k"], inp["v"], block=w.block,
+                                               segment=w.segment, scale=case["scale"], perm=perm,
+                                               counts=rc, idx=ri)
+    B, H, N = perm.shape
+    minpos = perm.reshape(B, H, N // w.block, w.block).min(-1).astype(np.int32)
+    for mp in (dev(minpos), None):
+        o = torch.empty_like(g["q"])
+        lse = torch.empty(g["q"].shape[:3], dtype=torch.float32, device="cuda")
+        P.pbs_attn_fwd_permuted_queries(sh, qp, dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
+                                        dev(perm), mp, counts, idx, case["scale"], o, lse)
+        torch.cuda.synchronize()
+        check_attn(o.float().cpu().numpy(), oo, f"{case['name']} permuted-query attention")
+        assert np.abs(lse.cpu().numpy() - ol).max() < 1e-3
+
+
+def test_permuted_queries_keep_one_is_dense(case):
+    """Theorem 3.3 on the GPU: permuted queries and keys with every candidate kept, rows put
+    back in original order, equal plain causal attention."""
+    say(case["name"], "permuted queries, keep 1")
+    ref, w, sh, g, inp = case["ref"], case["w"], case["sh"], case["g"], case["inp"]
+    perm = ref["perm"]
+    qp = torch.empty_like(g["q"])
+    P.pbs_permute_queries(sh, dev(perm), g["q"], qp)
+    counts, idx = run_select(sh, qp, dev_bf16(ref["k_perm"]), None, case["scale"],
+                             P.PBS_SELECT_KEEP_RATIO, 1.0)
+    o = torch.empty_like(g["q"])
+    P.pbs_attn_fwd_permuted_queries(sh, qp, dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
+                                    dev(perm), None, counts, idx, case["scale"], o, None)
+    torch.cuda.synchronize()
+    check_attn(o.float().cpu().numpy(), ref["dense_o"], f"{case['name']} permuted queries keep 1")
+
+
 def test_dense_causal(case):
     say(case["name"], "pbs_attn_fwd dense")
     ref, sh = case["ref"], case["sh"]

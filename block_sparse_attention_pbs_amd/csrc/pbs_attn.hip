@@ -65,7 +65,13 @@ struct AttnArgs {
   int tile_off[4];
 };
 
-constexpr int kStageKeys = 64;  // keys per LDS stage
+#ifndef PBS_ATTN_STAGE_KEYS
+#define PBS_ATTN_STAGE_KEYS 32
+#endif
+#ifndef PBS_ATTN_MIN_WAVES
+#define PBS_ATTN_MIN_WAVES 3
+#endif
+constexpr int kStageKeys = PBS_ATTN_STAGE_KEYS;  // keys per LDS stage
 constexpr int kOffWindow = 1792; // off-diagonal list entries held in LDS at a time
 constexpr int kOwnMax = 256;     // own-segment blocks (S / Bs <= 16384 / 64)
 
@@ -83,8 +89,10 @@ struct Cfg {
   static constexpr int VPAD = 4;           // spare 16-byte chunks per V row
   static constexpr int KTILE = SK * (D + 8 * KPAD);   // bf16 elements of a K stage in LDS
   static constexpr int VTILE = SK * (D + 8 * VPAD);   // bf16 elements of a V stage in LDS
-  static constexpr int NLDK = SK * (CPR + KPAD) / 64; // 1 KiB direct loads per K stage
-  static constexpr int NLDV = SK * (CPR + VPAD) / 64; // 1 KiB direct loads per V stage
+  static constexpr int KCH = SK * (CPR + KPAD);      // 16-byte chunks of a K stage in LDS
+  static constexpr int VCH = SK * (CPR + VPAD);      // 16-byte chunks of a V stage in LDS
+  static constexpr int NLDK = (KCH + 63) / 64;       // direct loads (64 lanes) per K stage
+  static constexpr int NLDV = (VCH + 63) / 64;       // direct loads (64 lanes) per V stage
 };
 
 // LDS row layouts.  K rows: stride = 16 B mod 256 B, so the 16 lanes of a K fragment read
@@ -236,17 +244,20 @@ __device__ __forceinline__ void issue_stage(const AttnArgs& a, const Rsrc& rr, S
   for (int n = w; n < C::NLDK; n += C::NW) {
     const int P = n * 64 + lane;
     const int r = P / (C::CPR + C::KPAD), pc = P - r * (C::CPR + C::KPAD);
-    load_lds16(rk, Kst + n * 512, static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2),
-               base);
+    // a partial last load (KCH not a multiple of 64) runs with the tail lanes switched off
+    if (C::KCH % 64 == 0 || P < C::KCH)
+      load_lds16(rk, Kst + n * 512,
+                 static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2), base);
   }
 #pragma unroll
   for (int n = w; n < C::NLDV; n += C::NW) {
     const int P = n * 64 + lane;
     const int r = P / (C::CPR + C::VPAD), pc = P - r * (C::CPR + C::VPAD);
-    load_lds16(rv, Vst + n * 512, static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2),
-               base);
+    if (C::VCH % 64 == 0 || P < C::VCH)
+      load_lds16(rv, Vst + n * 512,
+                 static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2), base);
   }
-  if (st.masked && (a.mode == 1 || a.mode == 4) && w == 0)
+  if (st.masked && (a.mode == 1 || a.mode == 4) && w == 0 && lane < C::SK)
     load_lds4(rp, Pst, static_cast<uint32_t>(lane * 4), static_cast<uint32_t>(st.key0) * 4);
 }
 
@@ -462,7 +473,7 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
 }
 
 template <int D, int BS, int MODE>
-__global__ __launch_bounds__(BS * 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(AttnArgs a) {
   using C = Cfg<D, BS>;
   // One LDS array laid out [K stage 0][K stage 1][V stage 0][V stage 1].
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::KTILE + 2 * C::VTILE];

@@ -17,9 +17,10 @@
 //    pooled keys from pbs_permute).  HBM-bound, one workgroup per (head, block).
 //  * select: one workgroup per (query block, up to 4 query heads of one KV head), 256 threads per
 //    head.  Logits are plain fp32 dot products (n <= 8192 candidates x d), the softmax uses
-//    per-row reductions, the ranking is a bitonic sort of next_pow2(n) 64-bit keys in LDS, the
-//    coverage prefix is one strictly sequential fp32 sum (so it is bit-identical to any other
-//    sequential fp32 sum of the same values), and the kept blocks are compacted in ascending
+//    per-row reductions.  Keep ratio: the top-k set comes from a radix select over the ranking
+//    keys (no sort).  Coverage: the ranking is a bitonic sort of next_pow2(n) 64-bit keys in LDS
+//    and the coverage prefix is one strictly sequential fp32 sum (so it is bit-identical to any
+//    other sequential fp32 sum of the same values).  The kept blocks are compacted in ascending
 //    order with a per-row prefix scan.
 #include <cmath>
 
@@ -83,6 +84,7 @@ struct SelArgs {
 };
 
 constexpr int kSub = 256;   // threads per row (one row = one query head of the workgroup)
+static_assert(kSub == 256, "the radix select keeps one 8-bit histogram bin per thread of a row");
 
 // Sum / max over the kSub threads of one row (sub = the row's index in the workgroup).  Every thread
 // of the workgroup calls these together.
@@ -223,18 +225,86 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
     __syncthreads();
   }
 
-  // Sort keys: (descending P, ascending block); with keep_first, block 0 gets key 0, below every
-  // real key (whose top word, the complemented orderable value, is never 0).
-  for (int p = st; p < n2; p += kSub)
-    keys[p] = (p < n) ? ((a.keep_first && p == 0) ? 0ull : desc_sort_key(Ps[p], static_cast<uint32_t>(p)))
-                      : ~0ull;
-  bitonic_sort_row(keys, n2, st);
+  // Rank keys: (descending P, ascending block) as one ascending 64-bit key whose top word is the
+  // complemented orderable value of P and whose low word is the block; with keep_first, block 0
+  // gets key 0, below every real key (whose top word is never 0).
+  if (a.mode == 0) {
+    // Keep ratio: the kk lowest keys, found without sorting.  A radix select over the top words
+    // (4 passes of 8 bits, per-row histograms in LDS) finds the kk-th lowest top word H and how
+    // many keys with top word H belong to the kept set; those are the lowest blocks among the keys
+    // equal to H (the low word is the block), taken by an exclusive scan in block order.  The kept
+    // set is exactly the first kk of the full ranking.
+    uint32_t* hi = reinterpret_cast<uint32_t*>(keys);
+    for (int p = st; p < n; p += kSub)
+      hi[p] = (a.keep_first && p == 0) ? 0u
+                                       : static_cast<uint32_t>(desc_sort_key(Ps[p], 0u) >> 32);
+    const int kk = max(1, min(static_cast<int>(floor(a.param * static_cast<double>(n))), n));
+    int32_t* hist = scan + sub * kSub;      // 256 bins per row (kSub == 256)
+    uint32_t prefix = 0, pmask = 0;
+    int need = kk;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hist[st] = 0;
+      __syncthreads();
+      for (int p = st; p < n; p += kSub) {
+        const uint32_t x = hi[p];
+        if ((x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (st < 64) {   // the row's first wave finds the digit where the running count reaches need
+        const int c0 = hist[4 * st], c1 = hist[4 * st + 1], c2 = hist[4 * st + 2], c3 = hist[4 * st + 3];
+        const int mine = c0 + c1 + c2 + c3;
+        int incl = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o);
+          if (st >= o) incl += y;
+        }
+        const int excl = incl - mine;
+        if (excl < need && need <= incl) {   // exactly one lane
+          int dgt = 4 * st, below = excl;
+          if (below + c0 < need) { below += c0; ++dgt;
+            if (below + c1 < need) { below += c1; ++dgt;
+              if (below + c2 < need) { below += c2; ++dgt; } } }
+          red[sub * 4] = __int_as_float(dgt);
+          red[sub * 4 + 1] = __int_as_float(need - below);
+        }
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(__float_as_int(red[sub * 4])) << shift;
+      pmask |= 0xffu << shift;
+      need = __float_as_int(red[sub * 4 + 1]);
+      __syncthreads();
+    }
+    // keep every key below H and the first `need` keys equal to H in block order
+    const uint32_t H = prefix;
+    const int per = (n + kSub - 1) / kSub;
+    const int lo = min(st * per, n), hi_end = min(lo + per, n);
+    int eq = 0;
+    for (int j = lo; j < hi_end; ++j) eq += (hi[j] == H);
+    hist[st] = eq;
+    __syncthreads();
+    for (int off = 1; off < kSub; off <<= 1) {
+      const int vv = (st >= off) ? hist[st - off] : 0;
+      __syncthreads();
+      hist[st] += vv;
+      __syncthreads();
+    }
+    int rank = hist[st] - eq;
+    for (int j = lo; j < hi_end; ++j) {
+      const uint32_t x = hi[j];
+      flag[j] = (x < H || (x == H && rank++ < need)) ? 1 : 0;
+    }
+    if (st == 0) kept[sub] = kk;
+    __syncthreads();
+  } else {
+    for (int p = st; p < n2; p += kSub)
+      keys[p] = (p < n) ? ((a.keep_first && p == 0) ? 0ull : desc_sort_key(Ps[p], static_cast<uint32_t>(p)))
+                        : ~0ull;
+    bitonic_sort_row(keys, n2, st);
+  }
 
   if (a.mode == 0) {
-    if (st == 0) {
-      int kk = static_cast<int>(floor(a.param * static_cast<double>(n)));
-      kept[sub] = max(1, min(kk, n));
-    }
+    // flags are set
   } else if (st < 64) {
     // Shortest prefix of the ranking whose running float32 sum reaches tau: the sum is strictly
     // sequential (one rounding per element, in ranking order); the first wave of the row gathers
@@ -259,11 +329,14 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
     }
     if (st == 0) kept[sub] = kk;
   }
-  for (int j = st; j < n; j += kSub) flag[j] = 0;
-  __syncthreads();
+  if (a.mode != 0) {
+    for (int j = st; j < n; j += kSub) flag[j] = 0;
+    __syncthreads();   // also publishes kept[sub] from the coverage scan
+    const int kc = kept[sub];
+    for (int m = st; m < kc; m += kSub) flag[static_cast<int>(keys[m] & 0xffffffffull)] = 1;
+    __syncthreads();
+  }
   const int kk = kept[sub];
-  for (int m = st; m < kk; m += kSub) flag[static_cast<int>(keys[m] & 0xffffffffull)] = 1;
-  __syncthreads();
 
   // ascending compaction: thread st of the row owns candidates [st*per, (st+1)*per)
   const int per = (n + kSub - 1) / kSub;

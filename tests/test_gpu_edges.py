@@ -130,6 +130,37 @@ def test_select_widest_rows():
             assert np.array_equal(ix[0, 0, i, :kk], np.sort(order[:kk]))
 
 
+def test_select_keep_ratio_ties_and_specials():
+    """Keep-ratio selection on rows full of ties that straddle the kept count, signed zeros,
+    tiny values and NaN (ranked after every number), with and without the first block forced
+    first: bit-exact against the oracle's ranking rules, on rows up to 8191 candidates."""
+    say("select ties and specials")
+    B, Hq, N, d, Bs, S = 1, 2, 8192 * 64, 64, 64, 64
+    nb = N // Bs
+    rng = np.random.default_rng(12)
+    vals = np.array([0.0, -0.0, 1e-30, 0.25, 0.25, 0.25, 0.125, np.nan, 3.0, 2.0 ** -20], np.float32)
+    rows = [nb - 1, 4097, 960, 129, 2]
+    Pm = np.zeros((B, Hq, nb, nb), np.float32)
+    for g in range(Hq):
+        for i in rows:
+            Pm[0, g, i, :i] = rng.choice(vals, size=i)
+    sh = shape(B, Hq, 1, N, d, Bs, S)
+    for param in (0.1, 0.3, 0.5, 1.0):
+        for keep_first in (False, True):
+            flags = P.PBS_FLAG_SCORES_IN | (P.PBS_FLAG_KEEP_FIRST if keep_first else 0)
+            counts, idx = run_select(sh, None, None, None, 0.125, P.PBS_SELECT_KEEP_RATIO, param,
+                                     blk_scores=dev(Pm), flags=flags)
+            c, ix = counts.cpu().numpy(), idx.cpu().numpy()
+            for g in range(Hq):
+                for i in rows:
+                    order = oracle.descending_order(Pm[0, g, i, :i])
+                    if keep_first:
+                        order = np.concatenate([[0], order[order != 0]])
+                    kk = oracle.keep_count(i, param)
+                    assert c[0, g, i] == kk, (param, keep_first, g, i)
+                    assert np.array_equal(ix[0, g, i, :kk], np.sort(order[:kk])), (param, keep_first, g, i)
+
+
 def test_permute_largest_segment():
     """The largest supported segment (16384 keys sorted in one workgroup)."""
     say("permute S=16384")

@@ -7,14 +7,20 @@
 // keys of one segment that it may see (causal), and every key's probabilities are averaged over
 // the rows.
 //
-// Two passes, both on v_mfma_f32_32x32x16_bf16 with S^T = K Q^T (a lane owns one scoring row):
-//  1. stats:  per (segment, row) the softmax max m (log2 units) and sum l, streaming the
-//             segment's keys through LDS;
-//  2. reduce: per key, sum over all rows of exp2(z - m) / l.  A wave owns 32 keys for the
-//             whole pass (its K fragments stay in registers); the rows stream through LDS in
-//             chunks of 32; each lane accumulates its 16 keys over its rows in fp32 and a final
-//             butterfly over the 32 lanes of each half-wave (wavefront reduction) gives the
-//             per-key sum, scaled by 1/R.
+// Three kernels, the matrix work on v_mfma_f32_32x32x16_bf16 with S^T = K Q^T (a lane owns one
+// scoring row in the first, one key column in the last):
+//  1. stats:   per (segment, chunk of keys, row) the softmax max m (log2 units) and sum l over
+//              the chunk, streaming its keys through LDS.  Segments are split into chunks of at
+//              most 1024 keys so that enough workgroups run to hide the loads' latency;
+//  2. combine: per (segment, row) the chunks' (m, l) merged into one log2-normaliser
+//              L = m + log2(l);
+//  3. reduce:  per key, the sum over all rows of exp2(z - L).  A wave owns 32 keys for the whole
+//              pass (its K fragments stay in registers); the rows stream through LDS in chunks
+//              of 32; each lane accumulates its 16 keys over its rows in fp32 and a final
+//              butterfly over the 32 lanes of each half-wave (wavefront reduction) gives the
+//              per-key sum, scaled by 1/R.
+// A key can be after a scoring row only in the last Bs positions of the sequence, so only tiles
+// that reach them apply the causal test.
 #include "pbs_device.h"
 #include "pbs_internal.h"
 
@@ -25,8 +31,10 @@ struct ScoreArgs {
   const uint16_t* q;
   const uint16_t* k;
   float* scores;
-  float2* stats;  // [B, Hkv, nseg, R] (m, l)
+  float2* part;   // [B, Hkv, nseg, nchunk, R] (m, l) of each key chunk
+  float* lse2;    // [B, Hkv, nseg, R] log2-normaliser of each (segment, row)
   int Hq, Hkv, G, N, S, nseg, R, Bs;
+  int chunk, nchunk;  // keys per chunk, chunks per segment
   float c;        // scale * log2(e)
 };
 
@@ -45,7 +53,7 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kStatKeys * STR];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, c32 = lane & 31;
-  const int sigma = blockIdx.x;
+  const int sigma = blockIdx.x / a.nchunk, ch = blockIdx.x - sigma * a.nchunk;
   const int bh = blockIdx.z;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int r = blockIdx.y * 128 + w * 32 + c32;
@@ -60,9 +68,10 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
   }
   const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;
-  const int s0 = sigma * a.S;
+  const int kbeg = sigma * a.S + ch * a.chunk;
+  const int first_row = a.N - a.Bs;   // every scoring row is >= first_row
   float m = -INFINITY, l = 0.f;
-  for (int k0 = s0; k0 < s0 + a.S; k0 += kStatKeys) {
+  for (int k0 = kbeg; k0 < kbeg + a.chunk; k0 += kStatKeys) {
     __syncthreads();
     {
       const uint16_t* kb = a.k + (kv_head + k0) * D;
@@ -75,6 +84,7 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
     }
     __syncthreads();
     if (!active) continue;
+    const bool causal = k0 + kStatKeys - 1 > first_row;   // uniform: a key may follow a row
 #pragma unroll
     for (int kt = 0; kt < kStatKeys / 32; ++kt) {
       f32x16 s;
@@ -85,19 +95,21 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
       for (int ks = 0; ks < NKS; ++ks)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(krow + ks * 16),
                                                      qf[ks], s, 0, 0, 0);
+      if (causal) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + kt * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+          if (key > t) s[e] = -INFINITY;
+        }
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + kt * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
-        const float z = (key <= t) ? s[e] * a.c : -INFINITY;
-        s[e] = z;
-        mx = fmaxf(mx, z);
-      }
-      const float m_new = fmaxf(m, mx);
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      const float m_new = fmaxf(m, mx * a.c);   // a.c > 0: the max commutes with the scaling
       if (m_new == -INFINITY) continue;
       float acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc += fast_exp2(s[e] - m_new);
+      for (int e = 0; e < 16; ++e) acc += fast_exp2(fmaf(s[e], a.c, -m_new));
       l = l * fast_exp2(m - m_new) + acc;
       m = m_new;
     }
@@ -109,7 +121,26 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
   const float mt = fmaxf(m, m2);
   const float lt = (mt == -INFINITY) ? 0.f
                                      : l * fast_exp2(m - mt) + l2 * fast_exp2(m2 - mt);
-  if (hl == 0) a.stats[(static_cast<size_t>(bh) * a.nseg + sigma) * a.R + r] = make_float2(mt, lt);
+  if (hl == 0)
+    a.part[((static_cast<size_t>(bh) * a.nseg + sigma) * a.nchunk + ch) * a.R + r] = make_float2(mt, lt);
+}
+
+// Per (segment, row): the chunks' (m, l) merged into L = m + log2(l).  Every row sees at least one
+// key of every segment (itself, or the whole segment when it lies before the row).
+__global__ __launch_bounds__(256) void score_combine_kernel(ScoreArgs a) {
+  const int local = blockIdx.x * 256 + threadIdx.x;       // sigma * R + r within one KV head
+  if (local >= a.nseg * a.R) return;
+  const int sigma = local / a.R, r = local - sigma * a.R;
+  const size_t seg = static_cast<size_t>(blockIdx.y) * a.nseg + sigma;   // bh * nseg + sigma
+  const float2* p = a.part + seg * a.nchunk * a.R + r;
+  float m = -INFINITY;
+  for (int c = 0; c < a.nchunk; ++c) m = fmaxf(m, p[static_cast<size_t>(c) * a.R].x);
+  float l = 0.f;
+  for (int c = 0; c < a.nchunk; ++c) {
+    const float2 v = p[static_cast<size_t>(c) * a.R];
+    if (v.x != -INFINITY) l += v.y * fast_exp2(v.x - m);
+  }
+  a.lse2[seg * a.R + r] = (l > 0.f) ? m + __log2f(l) : INFINITY;
 }
 
 template <int D>
@@ -137,7 +168,8 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
   float acc[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-  const float2* st_seg = a.stats + (static_cast<size_t>(bh) * a.nseg + sigma) * a.R;
+  const float* st_seg = a.lse2 + (static_cast<size_t>(bh) * a.nseg + sigma) * a.R;
+  const bool causal = active && key0 + 31 > a.N - a.Bs;   // uniform: a key may follow a row
   for (int rc = 0; rc < a.R; rc += 32) {
     __syncthreads();
     {
@@ -162,14 +194,18 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], *reinterpret_cast<const bf16x8*>(qrow + ks * 16),
                                                    s, 0, 0, 0);
     // lane column = scoring row rc + c32; lane value e = key key0 + (e/4)*8 + hl*4 + e%4
-    int gl, tt;
-    score_row(a, rc + c32, gl, tt);
-    const float2 st = st_seg[rc + c32];
-    const float inv_l = 1.f / st.y;
+    const float nl = -st_seg[rc + c32];
+    if (causal) {
+      int gl, tt;
+      score_row(a, rc + c32, gl, tt);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = key0 + (e >> 2) * 8 + hl * 4 + (e & 3);
-      if (key <= tt) acc[e] += fast_exp2(s[e] * a.c - st.x) * inv_l;
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + (e >> 2) * 8 + hl * 4 + (e & 3);
+        if (key <= tt) acc[e] += fast_exp2(fmaf(s[e], a.c, nl));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += fast_exp2(fmaf(s[e], a.c, nl));
     }
   }
   if (!active) return;
@@ -190,8 +226,11 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
 
 template <int D>
 hipError_t launch_score_t(const Dims& d, const ScoreArgs& a, hipStream_t stream) {
-  dim3 g1(d.nseg, (a.R + 127) / 128, d.B * d.Hkv);
+  dim3 g1(d.nseg * a.nchunk, (a.R + 127) / 128, d.B * d.Hkv);
   hipError_t e = launch(score_stats_kernel<D>, g1, dim3(256), 0, stream, a);
+  if (e != hipSuccess) return e;
+  dim3 gc((d.nseg * a.R + 255) / 256, d.B * d.Hkv);
+  e = launch(score_combine_kernel, gc, dim3(256), 0, stream, a);
   if (e != hipSuccess) return e;
   dim3 g2((d.N + 127) / 128, d.B * d.Hkv);
   return launch(score_reduce_kernel<D>, g2, dim3(256), 0, stream, a);
@@ -199,16 +238,33 @@ hipError_t launch_score_t(const Dims& d, const ScoreArgs& a, hipStream_t stream)
 
 }  // namespace
 
+// Keys per stats chunk: the segment split into at most 1024-key pieces (S and the chunk are
+// multiples of the 64-key tile).
+static int score_chunk(const Dims& d) {
+  int c = d.S;
+  while (c > 1024 && c % 2 == 0 && (c / 2) % kStatKeys == 0) c /= 2;
+  return c;
+}
+
 size_t score_workspace_bytes(const Dims& d) {
-  return static_cast<size_t>(d.B) * d.Hkv * d.nseg * d.G * d.Bs * sizeof(float2);
+  const size_t rows = static_cast<size_t>(d.B) * d.Hkv * d.nseg * d.G * d.Bs;
+  const size_t nchunk = static_cast<size_t>(d.S / score_chunk(d));
+  const size_t part = (rows * nchunk * sizeof(float2) + 255) & ~static_cast<size_t>(255);
+  return part + rows * sizeof(float);
 }
 
 hipError_t launch_score(const Dims& d, const uint16_t* q, const uint16_t* k, float scale,
                         float* scores, void* ws, hipStream_t stream) {
   ScoreArgs a;
-  a.q = q; a.k = k; a.scores = scores; a.stats = static_cast<float2*>(ws);
+  a.q = q; a.k = k; a.scores = scores;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.N = d.N; a.S = d.S; a.nseg = d.nseg;
   a.R = d.G * d.Bs; a.Bs = d.Bs;
+  a.chunk = score_chunk(d);
+  a.nchunk = d.S / a.chunk;
+  const size_t rows = static_cast<size_t>(d.B) * d.Hkv * d.nseg * a.R;
+  const size_t part = (rows * a.nchunk * sizeof(float2) + 255) & ~static_cast<size_t>(255);
+  a.part = static_cast<float2*>(ws);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + part);
   a.c = scale * kLog2e;
   return d.d == 128 ? launch_score_t<128>(d, a, stream) : launch_score_t<64>(d, a, stream);
 }

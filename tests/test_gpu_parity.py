@@ -6,7 +6,7 @@ relative 1e-4; attention within max-abs 2e-2 and mean-abs 2e-3 of the float64 or
 
 Cases are small enough for the oracle to finish in seconds and still span several blocks and
 segments, ragged segment counts (S = 3 Bs), both head dims and block sizes, GQA groups of 4 and 7,
-and both selection rules."""
+both selection rules, and a batch of 3."""
 import zlib
 
 import numpy as np
@@ -23,20 +23,22 @@ pytestmark = pytest.mark.gpu
 
 SCORE_RTOL = 1e-4
 
-# name -> (Hq, Hkv, N, d, Bs, S, mode, param)
+# name -> (Hq, Hkv, N, d, Bs, S, mode, param[, batch])
 CASES = {
     "toy_1k": (1, 1, 1024, 64, 64, 256, "keep", 0.5),
     "gqa4_2k_keep": (8, 2, 2048, 128, 128, 512, "keep", 0.3),
     "gqa7_1536_ragged": (14, 2, 1536, 128, 128, 384, "keep", 0.25),
     "d64_bs128_cov": (4, 2, 1024, 64, 128, 256, "coverage", 0.9),
     "d128_bs64_cov": (4, 1, 1152, 128, 64, 192, "coverage", 0.8),
+    "batch3_gqa2_keep": (4, 2, 1024, 128, 128, 256, "keep", 0.4, 3),
 }
 
 
 def _inputs(name):
-    Hq, Hkv, N, d, Bs, S, mode, param = CASES[name]
-    w = pbs_synth.WORKLOADS["gqa_8k"].scaled(name=name, heads_q=Hq, heads_kv=Hkv, seq_len=N,
-                                             head_dim=d, block=Bs, segment=S, mode=mode,
+    Hq, Hkv, N, d, Bs, S, mode, param = CASES[name][:8]
+    batch = CASES[name][8] if len(CASES[name]) > 8 else 1
+    w = pbs_synth.WORKLOADS["gqa_8k"].scaled(name=name, batch=batch, heads_q=Hq, heads_kv=Hkv,
+                                             seq_len=N, head_dim=d, block=Bs, segment=S, mode=mode,
                                              params=(param,), seed=zlib.crc32(name.encode()) % 100000)
     return w, pbs_synth.make_inputs(w)
 

@@ -239,7 +239,7 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": src.numel() * 2, "launches": 5}))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); the path "
               "would shard by KV-head groups with no exchange, which is not built here.",
               file=sys.stderr)
         sys.exit(2)

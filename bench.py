@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -33,10 +34,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_gqa_128k_traffic.txt")
 
 
 def attn_source_hash() -> str:
+    """Hash of the attention kernel's code (comments and layout stripped) and its compile flags:
+    the counters in the traffic summary stay valid while this is unchanged."""
+    from block_sparse_attention_pbs_amd import build as pbs_build
     h = hashlib.sha256()
     for rel in ATTN_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    h.update(repr((pbs_build.common_flags(), pbs_build.EXTRA_FLAGS.get("pbs_attn.hip"))).encode())
     return h.hexdigest()[:16]
 
 

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libpbs.so")
 SOURCES = ["pbs_api.cpp", "pbs_score.hip", "pbs_permute.hip", "pbs_select.hip", "pbs_attn.hip"]
 # Per-source extra flags.  The attention kernel keeps its MFMA accumulators in VGPRs: its scores
 # feed VALU work directly (no v_accvgpr_read per score), and the whole kernel then fits the
-# 256-register budget of two waves per SIMD.
+# 168-register budget of three waves per SIMD.
 EXTRA_FLAGS = {"pbs_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 

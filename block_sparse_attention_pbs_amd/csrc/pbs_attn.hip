@@ -11,14 +11,14 @@
 // Design (CDNA4, wave64):
 //  * one workgroup of Bs/32 waves per (query block, query head); wave w owns 32 query rows and
 //    sees every key of every visited block, so no cross-wave reduction is needed;
-//  * keys stream through LDS in stages of 64 keys (half a 128-key block), double-buffered and
-//    filled by asynchronous direct buffer->LDS loads (buffer_load_dwordx4 ... lds, bounds-
-//    checked) one stage ahead of the compute.  A workgroup needs ~75 KiB of LDS, so two
-//    workgroups share a CU: while one waits for its next stage the other computes;
+//  * keys stream through LDS in stages of 32 keys, double-buffered and filled by asynchronous
+//    direct buffer->LDS loads (buffer_load_dwordx4 ... lds, bounds-checked) one stage ahead of
+//    the compute.  A workgroup needs ~42 KiB of LDS and at most 168 VGPRs per lane, so three
+//    workgroups share a CU (three waves per SIMD): while one waits or runs its softmax, the
+//    others keep the matrix cores busy;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 (A = K rows from
 //    LDS, B = the wave's Q rows held in registers), so each lane owns one query row and the
-//    softmax statistics need one cross-half exchange per stage.  The two 32-key halves of a
-//    stage accumulate in two independent MFMA chains, and the accumulators live in VGPRs (built
+//    softmax statistics need one cross-half exchange.  The accumulators live in VGPRs (built
 //    with the VGPR form of the MFMAs), so scores feed the softmax without register moves;
 //  * the output is accumulated transposed, O^T += V^T P^T: P leaves the score accumulators as the
 //    bf16 B operand without touching LDS (the key order inside a 16-key step is a relabelling
@@ -144,7 +144,7 @@ __device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* lds_ptr) {
                                        (__attribute__((address_space(3))) i16x4*)(lds_ptr)));
 }
 
-// The key blocks one query block visits, in order, each split into stages of 64 keys; uniform
+// The key blocks one query block visits, in order, each split into stages of 32 keys; uniform
 // across the workgroup (every value it returns is scalar).  The visit list lives in LDS as 16-bit
 // entries (block index, bit 15 = needs the causal mask): the query block's off-diagonal list, a
 // window of kOffWindow entries at a time, and the visible own-segment blocks, compacted once.
@@ -218,7 +218,7 @@ struct StageIter {
 };
 
 struct Stage {
-  int key0;     // first key of the stage in the head's key order (block * Bs + half * 64)
+  int key0;     // first key of the stage in the head's key order (block * Bs + stage * 32)
   bool masked;
   bool orig;    // read from the original keys and values (mode 3 own segment)
 };
@@ -309,10 +309,10 @@ struct RowState {
   float mseen;    // exact row max (max-only pass)
 };
 
-// One stage (64 keys) for one wave.  S^T = K Q^T for the two 32-key halves as two independent MFMA
-// chains (for a masked stage, masked keys enter as -inf through the accumulators' initial values);
-// then, half by half, exp2 against the fixed reference and O^T += V^T P^T, so that the exp2 work of
-// one half can overlap the matrix work of the other.  There is no running max: before a pass each
+// One stage (32 keys, one 32-key sub-tile per kStageKeys / 32) for one wave.  S^T = K Q^T as one
+// MFMA chain per sub-tile (for a masked stage, masked keys enter as -inf through the accumulators'
+// initial values); then exp2 against the fixed reference and O^T += V^T P^T.  The other waves of
+// the SIMD keep the matrix cores busy while this one runs its exp2 work.  There is no running max: before a pass each
 // row's reference is set to its max over the pass's first stage (0 for a row that sees no key of
 // it; the MAXONLY form of this function computes that max), and a row sum outside [2^-60, 2^64]
 // after the pass sends the workgroup through the exact-max fallback.

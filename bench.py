@@ -218,6 +218,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-qperm", action="store_true",
                     help="skip timing the query-permutation variant")
+    ap.add_argument("--no-gemm", action="store_true",
+                    help="skip the hipBLASLt bf16 GEMM reference measurement")
     ap.add_argument("--no-hybrid", action="store_true",
                     help="skip timing pbs_attn_fwd_hybrid (own segment from the original K/V)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -418,6 +420,32 @@ def main():
                  "max_abs_diff_vs_main_output": float((o_q.float() - bf.o.float()).abs().max().item())}
         del qp, c2, i2, o_q
 
+    # Reference: what the vendor GEMM library reaches on this GPU with a large bf16 GEMM
+    # (torch.matmul -> hipBLASLt), i.e. the practical matrix-core ceiling at the clock the chip
+    # holds under load.  Measured outside the timed steps; not part of the path.
+    gemm = None
+    if not args.no_gemm:
+        n = 8192
+        ga = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        gb = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        gc = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(ga, gb, out=gc)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 30
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(ga, gb, out=gc)
+        e1.record()
+        e1.synchronize()
+        g_tflops = 2.0 * n ** 3 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+        gemm = {"shape": f"{n}x{n}x{n} bf16 (torch.matmul, hipBLASLt)",
+                "tflops": round(g_tflops, 1),
+                "frac_of_peak": round(g_tflops / PEAK_BF16_TFLOPS, 4),
+                "attention_over_gemm": round(eff_tflops / g_tflops, 4)}
+        del ga, gb, gc
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -472,6 +500,7 @@ def main():
             "traffic": traffic,
             "work_per_launch": f"{computed} computed blocks x {flop_per_block / 1e6:.3f} MFLOP",
         },
+        "library_gemm_reference": gemm,
         "hybrid_own_segment_natural": hybrid,
         "permuted_queries": qperm,
         "cpu_baseline": cpu,

@@ -44,7 +44,8 @@ def attn_source_hash() -> str:
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
-    h.update(repr((pbs_build.common_flags(), pbs_build.EXTRA_FLAGS.get("pbs_attn.hip"))).encode())
+    flags = [f for f in pbs_build.common_flags() if not f.startswith("-I")]   # no paths
+    h.update(repr((flags, pbs_build.EXTRA_FLAGS.get("pbs_attn.hip"))).encode())
     return h.hexdigest()[:16]
 
 

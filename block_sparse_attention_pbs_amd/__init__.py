@@ -28,6 +28,8 @@ PBS_E_WORKSPACE = -4
 PBS_E_LAUNCH = -5
 PBS_SELECT_KEEP_RATIO = 0
 PBS_SELECT_COVERAGE = 1
+PBS_LAYOUT_BHND = 0
+PBS_LAYOUT_BNHD = 1
 PBS_FLAG_SCORES_IN = 1
 PBS_FLAG_KEEP_FIRST = 2
 
@@ -50,7 +52,7 @@ class pbs_shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
                 ("heads_kv", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
-                ("segment", ctypes.c_int32)]
+                ("segment", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -112,14 +114,21 @@ def _check(code: int):
         raise PbsError(code, lib().pbs_strerror(code).decode())
 
 
-def make_shape(batch, heads_q, heads_kv, seq_len, head_dim, block, segment) -> pbs_shape:
-    return pbs_shape(batch, heads_q, heads_kv, seq_len, head_dim, block, segment)
+def make_shape(batch, heads_q, heads_kv, seq_len, head_dim, block, segment,
+               layout: int = 0) -> pbs_shape:
+    return pbs_shape(batch, heads_q, heads_kv, seq_len, head_dim, block, segment, layout)
 
 
-def shape_of(q: torch.Tensor, k: torch.Tensor, block: int, segment: int) -> pbs_shape:
-    """Shape from Q [B,Hq,N,d] and K [B,Hkv,N,d]."""
+def shape_of(q: torch.Tensor, k: torch.Tensor, block: int, segment: int,
+             layout: int = None) -> pbs_shape:
+    """Shape from Q and K: [B,Hq,N,d] / [B,Hkv,N,d] (PBS_LAYOUT_BHND, the default) or
+    [B,N,Hq,d] / [B,N,Hkv,d] (PBS_LAYOUT_BNHD)."""
+    layout = PBS_LAYOUT_BHND if layout is None else layout
+    if layout == PBS_LAYOUT_BNHD:
+        B, N, Hq, d = q.shape
+        return pbs_shape(B, Hq, k.shape[2], N, d, block, segment, layout)
     B, Hq, N, d = q.shape
-    return pbs_shape(B, Hq, k.shape[1], N, d, block, segment)
+    return pbs_shape(B, Hq, k.shape[1], N, d, block, segment, layout)
 
 
 def pbs_workspace_bytes(shape: pbs_shape) -> int:
@@ -198,27 +207,29 @@ class Buffers:
         self.shape = shape
         self.scores = torch.empty((B, Hkv, N), dtype=torch.float32, **e)
         self.perm = torch.empty((B, Hkv, N), dtype=torch.int32, **e)
-        self.k_perm = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, **e)
-        self.v_perm = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, **e)
+        kv = (B, N, Hkv, d) if shape.layout == PBS_LAYOUT_BNHD else (B, Hkv, N, d)
+        self.k_perm = torch.empty(kv, dtype=torch.bfloat16, **e)
+        self.v_perm = torch.empty(kv, dtype=torch.bfloat16, **e)
         self.k_pool = torch.empty((B, Hkv, nb, d), dtype=torch.float32, **e)
         self.blk_minpos = torch.empty((B, Hkv, nb), dtype=torch.int32, **e)
         self.counts = torch.empty((B, Hq, nb), dtype=torch.int32, **e)
         self.idx = torch.empty((B, Hq, nb, mo), dtype=torch.int32, **e)
         self.blk_scores = torch.empty((B, Hq, nb, nb), dtype=torch.float32, **e) if with_scores else None
-        self.o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, **e)
+        self.o = torch.empty((B, N, Hq, d) if shape.layout == PBS_LAYOUT_BNHD else (B, Hq, N, d),
+                             dtype=torch.bfloat16, **e)
         self.lse = torch.empty((B, Hq, N), dtype=torch.float32, **e)
         self.workspace = torch.empty(max(pbs_workspace_bytes(shape), 16), dtype=torch.uint8, **e)
 
 
 def prefill(q, k, v, *, block: int, segment: int, keep: Optional[float] = None,
             coverage: Optional[float] = None, scale: Optional[float] = None,
-            buffers: Optional[Buffers] = None, stream=None) -> Buffers:
+            buffers: Optional[Buffers] = None, stream=None, layout: int = None) -> Buffers:
     """The whole PBS-Attn prefill: pbs_score -> pbs_permute -> pbs_block_select ->
     pbs_attn_fwd on one stream.  Exactly one of ``keep`` / ``coverage``.  Returns the buffers
-    (``.o`` is the output in original token order)."""
+    (``.o`` is the output in original token order, in the layout of q)."""
     if (keep is None) == (coverage is None):
         raise PbsError(PBS_E_ARG, "give exactly one of keep / coverage")
-    shape = shape_of(q, k, block, segment)
+    shape = shape_of(q, k, block, segment, layout)
     if scale is None:
         scale = default_scale(q.shape[-1])
     bf = buffers or Buffers(shape, q.device)
@@ -234,9 +245,9 @@ def prefill(q, k, v, *, block: int, segment: int, keep: Optional[float] = None,
 
 
 def dense_causal(q, k, v, *, block: int = 128, scale: Optional[float] = None, o=None, lse=None,
-                 stream=None):
+                 stream=None, layout: int = None):
     """Plain causal attention with the same kernel (dense mode of pbs_attn_fwd)."""
-    shape = shape_of(q, k, block, block)   # dense mode does not use segments
+    shape = shape_of(q, k, block, block, layout)   # dense mode does not use segments
     if scale is None:
         scale = default_scale(q.shape[-1])
     if o is None:

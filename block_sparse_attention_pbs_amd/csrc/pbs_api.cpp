@@ -23,6 +23,11 @@ int check_shape(const pbs_shape* s, Dims* d) {
   if (s->segment <= 0 || s->segment % s->block || s->segment > 16384) return PBS_E_SHAPE;
   if (s->seq_len % s->segment) return PBS_E_SHAPE;
   if (s->seq_len / s->block > 8192) return PBS_E_SHAPE;
+  if (s->layout != PBS_LAYOUT_BHND && s->layout != PBS_LAYOUT_BNHD) return PBS_E_SHAPE;
+  // K/V rows are addressed with 32-bit byte offsets from the start of a head
+  if (s->layout == PBS_LAYOUT_BNHD &&
+      static_cast<uint64_t>(s->seq_len) * s->heads_kv * s->head_dim * 2 >= (1ull << 32))
+    return PBS_E_SHAPE;
   d->B = s->batch;
   d->Hq = s->heads_q;
   d->Hkv = s->heads_kv;
@@ -35,6 +40,7 @@ int check_shape(const pbs_shape* s, Dims* d) {
   d->bps = s->segment / s->block;
   d->nseg = s->seq_len / s->segment;
   d->max_off = d->nseg > 0 ? (d->nseg - 1) * d->bps : 0;
+  d->layout = s->layout;
   return PBS_OK;
 }
 

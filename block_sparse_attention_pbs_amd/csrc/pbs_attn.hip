@@ -59,6 +59,8 @@ struct AttnArgs {
                  // queries (output rows written back at their original positions)
   int xcd_map;   // 1: total work items divisible by 8, use the XCD-grouped order
   float c;       // scale * log2(e)
+  RowMap qm, km; // row addressing of q / o and of every key and value tensor (either layout)
+  int kv_rs;     // elements between consecutive rows of one K/V head (km.stride())
   // Element offsets of the K/V stage tiles in LDS.  Passed at run time on purpose: the compiler
   // then keeps one (tile base + lane) address per tile and folds every in-tile offset into the
   // DS instruction, instead of materialising one register per (stage, offset) pair.
@@ -236,7 +238,7 @@ __device__ __forceinline__ void issue_stage(const AttnArgs& a, const Rsrc& rr, S
                                             uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
                                             int lane) {
   using C = Cfg<D, BS>;
-  const uint32_t base = static_cast<uint32_t>(st.key0) * D * 2;
+  const uint32_t base = static_cast<uint32_t>(st.key0) * static_cast<uint32_t>(a.kv_rs) * 2;
   const u32x4 rk = st.orig ? rr.k2 : rr.k;
   const u32x4 rv = st.orig ? rr.v2 : rr.v;
   const u32x4 rp = rr.p;
@@ -247,7 +249,7 @@ __device__ __forceinline__ void issue_stage(const AttnArgs& a, const Rsrc& rr, S
     // a partial last load (KCH not a multiple of 64) runs with the tail lanes switched off
     if (C::KCH % 64 == 0 || P < C::KCH)
       load_lds16(rk, Kst + n * 512,
-                 static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2), base);
+                 static_cast<uint32_t>((r * a.kv_rs + (pc < C::CPR ? pc : 0) * 8) * 2), base);
   }
 #pragma unroll
   for (int n = w; n < C::NLDV; n += C::NW) {
@@ -255,7 +257,7 @@ __device__ __forceinline__ void issue_stage(const AttnArgs& a, const Rsrc& rr, S
     const int r = P / (C::CPR + C::VPAD), pc = P - r * (C::CPR + C::VPAD);
     if (C::VCH % 64 == 0 || P < C::VCH)
       load_lds16(rv, Vst + n * 512,
-                 static_cast<uint32_t>((r * D + (pc < C::CPR ? pc : 0) * 8) * 2), base);
+                 static_cast<uint32_t>((r * a.kv_rs + (pc < C::CPR ? pc : 0) * 8) * 2), base);
   }
   if (st.masked && (a.mode == 1 || a.mode == 4) && w == 0 && lane < C::SK)
     load_lds4(rp, Pst, static_cast<uint32_t>(lane * 4), static_cast<uint32_t>(st.key0) * 4);
@@ -506,19 +508,22 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
     g = (hb - b * a.Hkv) * a.G + rem % a.G;
   }
   const int h = g / a.G;
-  const size_t q_head = (static_cast<size_t>(b) * a.Hq + g) * a.N;
-  const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;
+  const size_t q_head = (static_cast<size_t>(b) * a.Hq + g) * a.N;     // lse is [B, Hq, N]
+  const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;   // perm is [B, Hkv, N]
   // This lane's query row (both halves share it): slot ts of the query tensor; its original
   // position t drives the causal test and the output row.  Queries are in natural order except
   // in mode 4, where slot ts holds the token at perm[ts] and the row is written back there.
   const int ts = i * BS + w * 32 + c32;
   const int t = (MODE == 4) ? min(max(a.perm[kv_head + ts], 0), a.N - 1) : ts;
-  const uint32_t head_bytes = static_cast<uint32_t>(a.N) * D * 2;
+  // one K/V head: rows 0 .. N-1, a.kv_rs elements apart (< 2^32 bytes, checked on the host)
+  const size_t kv0 = a.km.off(b, h, 0);
+  const uint32_t head_bytes =
+      static_cast<uint32_t>((static_cast<size_t>(a.N - 1) * a.kv_rs + D) * 2);
   Rsrc rr;
-  rr.k = make_rsrc(a.k + kv_head * D, head_bytes);
-  rr.v = make_rsrc(a.v + kv_head * D, head_bytes);
-  rr.k2 = make_rsrc(MODE == 3 ? a.k2 + kv_head * D : nullptr, MODE == 3 ? head_bytes : 0u);
-  rr.v2 = make_rsrc(MODE == 3 ? a.v2 + kv_head * D : nullptr, MODE == 3 ? head_bytes : 0u);
+  rr.k = make_rsrc(a.k + kv0, head_bytes);
+  rr.v = make_rsrc(a.v + kv0, head_bytes);
+  rr.k2 = make_rsrc(MODE == 3 ? a.k2 + kv0 : nullptr, MODE == 3 ? head_bytes : 0u);
+  rr.v2 = make_rsrc(MODE == 3 ? a.v2 + kv0 : nullptr, MODE == 3 ? head_bytes : 0u);
   rr.p =
       make_rsrc(a.perm ? a.perm + kv_head : nullptr, a.perm ? static_cast<uint32_t>(a.N) * 4 : 0u);
 
@@ -592,7 +597,7 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
   // Q fragments (B operand of S^T = K Q^T): lane holds q[t][ks*16 + hl*8 .. +8]
   bf16x8 qf[C::NKS];
   {
-    const uint16_t* qrow = a.q + (q_head + ts) * D + hl * 8;
+    const uint16_t* qrow = a.q + a.qm.off(b, g, ts) + hl * 8;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
   }
@@ -618,7 +623,7 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
 
   const float l = pair_sum(rs.lsum);   // the two halves of the row
   const float inv_l = (l > 0.f) ? 1.f / l : 0.f;
-  uint16_t* orow = a.o + (q_head + t) * D;
+  uint16_t* orow = a.o + a.qm.off(b, g, t);
 #pragma unroll
   for (int mt = 0; mt < C::NMT; ++mt) {
 #pragma unroll
@@ -661,6 +666,9 @@ hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, cons
   const long long total = static_cast<long long>(d.B) * d.Hq * d.nb;
   a.xcd_map = (total % 8 == 0) ? 1 : 0;
   a.c = scale * kLog2e;
+  a.qm = q_rows(d);
+  a.km = kv_rows(d);
+  a.kv_rs = a.km.stride();
   const int ktile = kStageKeys * (d.d + 8), vtile = kStageKeys * (d.d + 32);
   a.tile_off[0] = 0;
   a.tile_off[1] = ktile;

@@ -15,7 +15,21 @@ struct Dims {
   int bps;      // S / Bs
   int nseg;     // N / S
   int max_off;  // (nseg - 1) * bps
+  int layout;   // 0: bf16 tensors [B, H, N, d]; 1: [B, N, H, d]
 };
+
+// Addressing of a bf16 [B, H, N, d] tensor in either layout: the element offset of row n of head
+// h of batch b, and the element distance between two consecutive rows of one head.
+struct RowMap {
+  int layout, H, N, d;
+  __host__ __device__ size_t off(int b, int h, int n) const {
+    return layout == 0 ? ((static_cast<size_t>(b) * H + h) * N + n) * d
+                       : ((static_cast<size_t>(b) * N + n) * H + h) * d;
+  }
+  __host__ __device__ int stride() const { return layout == 0 ? d : H * d; }
+};
+inline RowMap q_rows(const Dims& d) { return RowMap{d.layout, d.Hq, d.N, d.d}; }
+inline RowMap kv_rows(const Dims& d) { return RowMap{d.layout, d.Hkv, d.N, d.d}; }
 
 // Kernel launch through hipLaunchKernel so that the status of this very launch is returned
 // (every kernel takes one argument struct).

@@ -47,7 +47,8 @@ struct GatherArgs {
   uint16_t* v_perm;
   float* k_pool;
   int32_t* minpos;
-  int N, nb;
+  int N, nb, Hkv;
+  RowMap km;      // row addressing of k, v, k_perm and v_perm (either layout)
 };
 
 template <int D, int BS>
@@ -60,20 +61,22 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int c = tid % CH, rg = tid / CH;
   const int j = blockIdx.x;
   const int bh = blockIdx.y;
-  const size_t head = static_cast<size_t>(bh) * a.N;
+  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+  const size_t head = static_cast<size_t>(bh) * a.N;   // perm is [B, Hkv, N]
   float sum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sum[e] = 0.f;
   int mn = 0x7fffffff;
 #pragma unroll 4
   for (int r = rg; r < BS; r += RP) {
-    const size_t p = head + static_cast<size_t>(j) * BS + r;
-    const int src = a.perm[p];
+    const int pos = j * BS + r;
+    const int src = a.perm[head + pos];
     mn = min(mn, src);
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(a.k + (head + src) * D + c * 8);
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v + (head + src) * D + c * 8);
-    *reinterpret_cast<u32x4*>(a.k_perm + p * D + c * 8) = kv;
-    *reinterpret_cast<u32x4*>(a.v_perm + p * D + c * 8) = vv;
+    const size_t so = a.km.off(b, h, src) + c * 8, po = a.km.off(b, h, pos) + c * 8;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(a.k + so);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v + so);
+    *reinterpret_cast<u32x4*>(a.k_perm + po) = kv;
+    *reinterpret_cast<u32x4*>(a.v_perm + po) = vv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       sum[2 * e] += __uint_as_float(kv[e] << 16);
@@ -112,6 +115,7 @@ struct QGatherArgs {
   const int32_t* perm;
   uint16_t* q_perm;
   int N, Hq, Hkv, G;
+  RowMap qm;      // row addressing of q and q_perm (either layout)
 };
 
 // Queries moved with their tokens (the query-permutation variant): row p of query head g takes
@@ -124,15 +128,14 @@ __global__ __launch_bounds__(256) void qgather_kernel(QGatherArgs a) {
   constexpr int ROWS = 64;
   const int bg = blockIdx.y;                       // b * Hq + g
   const int b = bg / a.Hq, g = bg - b * a.Hq;
-  const size_t qhead = static_cast<size_t>(bg) * a.N;
   const size_t phead = (static_cast<size_t>(b) * a.Hkv + g / a.G) * a.N;
   const int c = threadIdx.x % CH;
   for (int r = threadIdx.x / CH; r < ROWS; r += 256 / CH) {
     const int p = blockIdx.x * ROWS + r;
     if (p >= a.N) break;
     const int src = min(max(a.perm[phead + p], 0), a.N - 1);
-    const u32x4 x = *reinterpret_cast<const u32x4*>(a.q + (qhead + src) * D + c * 8);
-    *reinterpret_cast<u32x4*>(a.q_perm + (qhead + p) * D + c * 8) = x;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(a.q + a.qm.off(b, g, src) + c * 8);
+    *reinterpret_cast<u32x4*>(a.q_perm + a.qm.off(b, g, p) + c * 8) = x;
   }
 }
 
@@ -143,6 +146,7 @@ hipError_t launch_permute_queries(const Dims& d, const int32_t* perm, const uint
   QGatherArgs qa;
   qa.q = q; qa.perm = perm; qa.q_perm = q_perm;
   qa.N = d.N; qa.Hq = d.Hq; qa.Hkv = d.Hkv; qa.G = d.G;
+  qa.qm = q_rows(d);
   const dim3 grid((d.N + 63) / 64, d.B * d.Hq);
   if (d.d == 128) return launch(qgather_kernel<128>, grid, dim3(256), 0, stream, qa);
   return launch(qgather_kernel<64>, grid, dim3(256), 0, stream, qa);
@@ -166,7 +170,8 @@ hipError_t launch_permute(const Dims& d, const float* scores, const uint16_t* k,
   if (e != hipSuccess) return e;
   GatherArgs ga;
   ga.k = k; ga.v = v; ga.perm = perm; ga.k_perm = k_perm; ga.v_perm = v_perm;
-  ga.k_pool = k_pool; ga.minpos = blk_minpos; ga.N = d.N; ga.nb = d.nb;
+  ga.k_pool = k_pool; ga.minpos = blk_minpos; ga.N = d.N; ga.nb = d.nb; ga.Hkv = d.Hkv;
+  ga.km = kv_rows(d);
   if (d.d == 128 && d.Bs == 128) return launch_gather_t<128, 128>(d, ga, stream);
   if (d.d == 128 && d.Bs == 64) return launch_gather_t<128, 64>(d, ga, stream);
   if (d.d == 64 && d.Bs == 128) return launch_gather_t<64, 128>(d, ga, stream);

@@ -36,6 +36,7 @@ struct ScoreArgs {
   int Hq, Hkv, G, N, S, nseg, R, Bs;
   int chunk, nchunk;  // keys per chunk, chunks per segment
   float c;        // scale * log2(e)
+  RowMap qm, km;  // row addressing of q and k (either layout)
 };
 
 // Scoring row r of a KV group -> (query head offset inside the group, query position).
@@ -63,23 +64,23 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
   if (active) {
     score_row(a, r, g_local, t);
     const int g = h * a.G + g_local;
-    const uint16_t* qrow = a.q + ((static_cast<size_t>(b) * a.Hq + g) * a.N + t) * D + hl * 8;
+    const uint16_t* qrow = a.q + a.qm.off(b, g, t) + hl * 8;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
   }
-  const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;
+  const size_t krs = static_cast<size_t>(a.km.stride());
   const int kbeg = sigma * a.S + ch * a.chunk;
   const int first_row = a.N - a.Bs;   // every scoring row is >= first_row
   float m = -INFINITY, l = 0.f;
   for (int k0 = kbeg; k0 < kbeg + a.chunk; k0 += kStatKeys) {
     __syncthreads();
     {
-      const uint16_t* kb = a.k + (kv_head + k0) * D;
+      const uint16_t* kb = a.k + a.km.off(b, h, k0);
       constexpr int CH = D / 8;
       for (int c = tid; c < kStatKeys * CH; c += 256) {
         const int rr = c / CH, col = (c % CH) * 8;
         *reinterpret_cast<u32x4*>(&Ks[rr * STR + col]) =
-            *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(rr) * D + col);
+            *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(rr) * krs + col);
       }
     }
     __syncthreads();
@@ -156,12 +157,11 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
   const int key0 = (blockIdx.x * 4 + w) * 32;
   const bool active = key0 < a.N;  // wave-uniform
   const int sigma = active ? key0 / a.S : 0;
-  const size_t kv_head = (static_cast<size_t>(b) * a.Hkv + h) * a.N;
   // Every wave of the workgroup lies in one segment only if 128 | S; the stats rows are read
   // per wave, so waves of different segments are fine.
   bf16x8 kf[NKS];
   if (active) {
-    const uint16_t* krow = a.k + (kv_head + key0 + c32) * D + hl * 8;
+    const uint16_t* krow = a.k + a.km.off(b, h, key0 + c32) + hl * 8;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(krow + ks * 16);
   }
@@ -178,8 +178,7 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
         const int rr = c / CH, col = (c % CH) * 8;
         int gl, tt;
         score_row(a, rc + rr, gl, tt);
-        const uint16_t* src =
-            a.q + ((static_cast<size_t>(b) * a.Hq + h * a.G + gl) * a.N + tt) * D + col;
+        const uint16_t* src = a.q + a.qm.off(b, h * a.G + gl, tt) + col;
         *reinterpret_cast<u32x4*>(&Qs[rr * STR + col]) = *reinterpret_cast<const u32x4*>(src);
       }
     }
@@ -218,7 +217,7 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
     acc[e] = v;
   }
   if (c32 == 0) {
-    float* out = a.scores + kv_head + key0;
+    float* out = a.scores + static_cast<size_t>(bh) * a.N + key0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) out[(e >> 2) * 8 + hl * 4 + (e & 3)] = acc[e] * inv_r;
   }
@@ -266,6 +265,8 @@ hipError_t launch_score(const Dims& d, const uint16_t* q, const uint16_t* k, flo
   a.part = static_cast<float2*>(ws);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + part);
   a.c = scale * kLog2e;
+  a.qm = q_rows(d);
+  a.km = kv_rows(d);
   return d.d == 128 ? launch_score_t<128>(d, a, stream) : launch_score_t<64>(d, a, stream);
 }
 

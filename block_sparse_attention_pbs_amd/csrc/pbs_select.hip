@@ -33,7 +33,8 @@ namespace {
 struct PoolArgs {
   const uint16_t* x;
   float* out;
-  int N, nb;
+  int N, nb, H;
+  RowMap xm;      // row addressing of x (either layout)
 };
 
 template <int D, int BS>
@@ -44,14 +45,15 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   const int tid = threadIdx.x;
   const int c = tid % CH, rg = tid / CH;
   const int j = blockIdx.x;
-  const size_t head = static_cast<size_t>(blockIdx.y) * a.N;
+  const int b = blockIdx.y / a.H, h = blockIdx.y - b * a.H;
+  const size_t rs = static_cast<size_t>(a.xm.stride());
+  const uint16_t* x0 = a.x + a.xm.off(b, h, j * BS) + c * 8;
   float sum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sum[e] = 0.f;
 #pragma unroll 4
   for (int r = rg; r < BS; r += RP) {
-    const u32x4 xv =
-        *reinterpret_cast<const u32x4*>(a.x + (head + static_cast<size_t>(j) * BS + r) * D + c * 8);
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(x0 + static_cast<size_t>(r) * rs);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       sum[2 * e] += __uint_as_float(xv[e] << 16);
@@ -363,7 +365,8 @@ template <int D, int BS>
 hipError_t launch_pool_t(const uint16_t* x, float* out, int heads, const Dims& d,
                          hipStream_t stream) {
   PoolArgs pa;
-  pa.x = x; pa.out = out; pa.N = d.N; pa.nb = d.nb;
+  pa.x = x; pa.out = out; pa.N = d.N; pa.nb = d.nb; pa.H = heads;
+  pa.xm = RowMap{d.layout, heads, d.N, d.d};
   return launch(pool_kernel<D, BS>, dim3(d.nb, d.B * heads), dim3(256), 0, stream, pa);
 }
 

@@ -12,13 +12,19 @@
  *                     segment (token-level causal mask through the stored positions)
  *
  * Conventions shared by every call
- *  - Tensors are DEVICE pointers owned by the caller, contiguous, batch-major "BHND":
- *    Q/O [B, Hq, N, d], K/V [B, Hkv, N, d]; bf16 is passed as uint16_t bit patterns.
- *    Every pointer must be 16-byte aligned (PBS_E_ALIGN otherwise).
+ *  - Tensors are DEVICE pointers owned by the caller, contiguous; bf16 is passed as uint16_t
+ *    bit patterns.  The bf16 activations -- q, k, v, o and the permuted copies k_perm, v_perm,
+ *    q_perm -- are laid out as pbs_shape.layout says: PBS_LAYOUT_BHND (0, the default of a
+ *    zero-initialised shape) Q/O [B, Hq, N, d], K/V [B, Hkv, N, d]; or PBS_LAYOUT_BNHD (1, the
+ *    token-major layout of FlashAttention-style callers) Q/O [B, N, Hq, d], K/V [B, N, Hkv, d].
+ *    Every other tensor (scores, perm, k_pool, blk_minpos, blk_scores, counts, idx, lse) is
+ *    head-major as documented at its call.  Every pointer must be 16-byte aligned
+ *    (PBS_E_ALIGN otherwise).
  *  - Query head g reads KV head g / (Hq / Hkv) (grouped-query attention).
  *  - Block size Bs (the pages' B) and segment size S (the pages' S) come in pbs_shape.
  *    Required: Hq % Hkv == 0, d in {64, 128}, Bs in {64, 128}, S % Bs == 0, N % S == 0,
- *    S <= 16384, N / Bs <= 8192 (PBS_E_SHAPE otherwise).  batch == 0 or seq_len == 0 is an
+ *    S <= 16384, N / Bs <= 8192, and for PBS_LAYOUT_BNHD N * Hkv * d * 2 < 2^32 bytes
+ *    (PBS_E_SHAPE otherwise).  batch == 0 or seq_len == 0 is an
  *    empty problem: once the shape and the scalar arguments are valid the call returns PBS_OK
  *    without launching anything or inspecting the pointers.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).  The
@@ -47,7 +53,11 @@ typedef struct pbs_shape {
   int32_t head_dim;  /* d, 64 or 128                                     */
   int32_t block;     /* Bs, attention block size, 64 or 128              */
   int32_t segment;   /* S, permutation segment size, multiple of Bs      */
+  int32_t layout;    /* PBS_LAYOUT_BHND or PBS_LAYOUT_BNHD (bf16 tensors) */
 } pbs_shape;
+
+#define PBS_LAYOUT_BHND 0 /* [B, H, N, d]: each head's rows contiguous                  */
+#define PBS_LAYOUT_BNHD 1 /* [B, N, H, d]: each token's heads contiguous (row stride H*d) */
 
 typedef enum pbs_status {
   PBS_OK = 0,

@@ -35,10 +35,30 @@ def test_shape_rules():
            P.make_shape(1, 32, 8, 1024, 96, 128, 256),    # d
            P.make_shape(1, 32, 8, 1024, 128, 32, 256),    # Bs
            P.make_shape(1, 32, 8, 65536, 128, 128, 32768),  # S too large
-           P.make_shape(1, 32, 8, 8192 * 64 * 2, 128, 64, 64)]  # too many blocks
+           P.make_shape(1, 32, 8, 8192 * 64 * 2, 128, 64, 64),  # too many blocks
+           P.make_shape(1, 32, 8, 1024, 128, 128, 256, 2),      # unknown layout
+           P.make_shape(1, 32, 8, 1024, 128, 128, 256, -1),     # unknown layout
+           # token-major K/V head wider than 32-bit byte offsets: N * Hkv * d * 2 = 2^32
+           P.make_shape(1, 64, 16, 8192 * 128, 128, 128, 8192, P.PBS_LAYOUT_BNHD)]
     for s in bad:
         assert P.pbs_max_offdiag(s) == -1
         assert P.pbs_workspace_bytes(s) == 0
+    # the same sizes are fine head-major, and token-major just below the limit
+    assert P.pbs_max_offdiag(P.make_shape(1, 64, 16, 8192 * 128, 128, 128, 8192)) > 0
+    assert P.pbs_max_offdiag(P.make_shape(1, 60, 15, 8192 * 128, 128, 128, 8192,
+                                          P.PBS_LAYOUT_BNHD)) > 0
+    assert P.pbs_max_offdiag(P.make_shape(1, 32, 8, 131072, 128, 128, 8192,
+                                          P.PBS_LAYOUT_BNHD)) == 15 * 64
+
+
+def test_shape_of_both_layouts():
+    import torch
+    q = torch.empty((2, 32, 4096, 128), dtype=torch.bfloat16)
+    k = torch.empty((2, 8, 4096, 128), dtype=torch.bfloat16)
+    s = P.shape_of(q, k, 128, 1024)
+    assert (s.batch, s.heads_q, s.heads_kv, s.seq_len, s.head_dim, s.layout) == (2, 32, 8, 4096, 128, 0)
+    s = P.shape_of(q.transpose(1, 2), k.transpose(1, 2), 128, 1024, P.PBS_LAYOUT_BNHD)
+    assert (s.batch, s.heads_q, s.heads_kv, s.seq_len, s.head_dim, s.layout) == (2, 32, 8, 4096, 128, 1)
 
 
 def _call(fn, *args):

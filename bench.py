@@ -219,6 +219,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-qperm", action="store_true",
                     help="skip timing the query-permutation variant")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the prefill")
     ap.add_argument("--no-gemm", action="store_true",
                     help="skip the hipBLASLt bf16 GEMM reference measurement")
     ap.add_argument("--no-hybrid", action="store_true",
@@ -311,6 +313,39 @@ def main():
     stage /= args.steps
     pbs_ms = float(stage.sum())
     print(f"[bench] {w.name}: PBS prefill {pbs_ms:.3f} ms (wall {wall_ms:.3f} ms/step)", file=sys.stderr, flush=True)
+
+    # The same four calls recorded once in a HIP graph and replayed (the library only enqueues
+    # kernels: no allocation, memset or synchronisation inside a call), timed the same way; the
+    # replayed output must equal the eager one bit for bit.
+    graph = None
+    if not args.no_graph:
+        o_eager = bf.o.clone()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            P.prefill(q, k, v, block=w.block, segment=w.segment, scale=scale, buffers=bf,
+                      **({"keep": param} if mode == P.PBS_SELECT_KEEP_RATIO else {"coverage": param}))
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            P.prefill(q, k, v, block=w.block, segment=w.segment, scale=scale, buffers=bf,
+                      **({"keep": param} if mode == P.PBS_SELECT_KEEP_RATIO else {"coverage": param}))
+        torch.cuda.synchronize()
+        bf.o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(bf.o.view(torch.int16), o_eager.view(torch.int16)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tot = 0.0
+        for _ in range(args.steps):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            tot += e0.elapsed_time(e1)
+        graph = {"prefill_ms": round(tot / args.steps, 4), "output_bit_identical_to_eager": same}
+        del g, o_eager
 
     # Algorithmic work of the attention launch: 4*Bs^2*d flops per computed key block.
     B, Hq, Hkv, N, d, Bs, S = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment
@@ -501,6 +536,7 @@ def main():
             "traffic": traffic,
             "work_per_launch": f"{computed} computed blocks x {flop_per_block / 1e6:.3f} MFLOP",
         },
+        "hip_graph_replay": graph,
         "library_gemm_reference": gemm,
         "hybrid_own_segment_natural": hybrid,
         "permuted_queries": qperm,

@@ -519,6 +519,46 @@ def prefill(q, k, v, *, block: int, segment: int, scale: float, mode: str, param
                 idx=idx, o=o, lse=lse)
 
 
+def prefill_varlen(q, k, v, cu_seqlens, *, block: int, segment: int, scale: float, mode: str,
+                   param: float):
+    """Several sequences packed along N (``q [1, Hq, T, d]``, ``k, v [1, Hkv, T, d]``, sequence
+    s holding tokens ``cu_seqlens[s] .. cu_seqlens[s+1]-1``, every length a multiple of
+    ``segment``): the method applied to each sequence on its own, the results placed back at
+    the sequences' positions.  Positions (``perm``) and block indices (``idx``) are absolute in
+    the packed sequence; ``P`` is block-diagonal (no block is a candidate of another
+    sequence's query).  The pages treat one sequence at a time; a packed batch is read as that,
+    sequence by sequence."""
+    cu = [int(x) for x in cu_seqlens]
+    T = q.shape[2]
+    if q.shape[0] != 1 or cu[0] != 0 or cu[-1] != T or any(b <= a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must run 0 < ... < T over one packed batch row")
+    if any((b - a) % segment for a, b in zip(cu, cu[1:])):
+        raise ValueError("every sequence length must be a multiple of the segment size")
+    Hq, Hkv = q.shape[1], k.shape[1]
+    nbT = T // block
+    width = max((T // segment - 1) * (segment // block), 1)
+    out = dict(scores=np.zeros((1, Hkv, T), np.float32), perm=np.zeros((1, Hkv, T), np.int64),
+               k_perm=np.zeros_like(k), v_perm=np.zeros_like(v),
+               P=np.zeros((1, Hq, nbT, nbT), np.float32), counts=np.zeros((1, Hq, nbT), np.int32),
+               idx=np.full((1, Hq, nbT, width), -1, np.int32),
+               o=np.zeros(q.shape, np.float64), lse=np.zeros((1, Hq, T), np.float64))
+    for a, b in zip(cu, cu[1:]):
+        r = prefill(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], block=block, segment=segment,
+                    scale=scale, mode=mode, param=param)
+        i0, i1 = a // block, b // block
+        out["scores"][:, :, a:b] = r["scores"]
+        out["perm"][:, :, a:b] = r["perm"] + a
+        out["k_perm"][:, :, a:b] = r["k_perm"]
+        out["v_perm"][:, :, a:b] = r["v_perm"]
+        out["P"][:, :, i0:i1, i0:i1] = r["P"]
+        out["counts"][:, :, i0:i1] = r["counts"]
+        w = r["idx"].shape[-1]
+        out["idx"][:, :, i0:i1, :w] = np.where(r["idx"] >= 0, r["idx"] + i0, -1)
+        out["o"][:, :, a:b] = r["o"]
+        out["lse"][:, :, a:b] = r["lse"]
+    return out
+
+
 def default_scale(head_dim: int) -> float:
     """float32(1/sqrt(d)) widened: the conventional softmax temperature (the pages print
     none)."""

@@ -509,6 +509,75 @@ def pin_segment0_rows_are_dense(O):
     assert np.abs(out["o"][:, :, 8:] - od[:, :, 8:]).max() > 1e-3
 
 
+# ----------------------------------------------------------------------------- packed sequences
+
+def _pack(x):
+    """[B, H, N, d] -> [1, H, B*N, d] (the sequences one after another along N)."""
+    B, H, N, d = x.shape
+    return np.ascontiguousarray(x.transpose(1, 0, 2, 3).reshape(1, H, B * N, d))
+
+
+def pin_varlen_equal_lengths_is_batch(O):
+    """Three sequences of one length packed along N give the batch-of-three result, with
+    positions and block indices shifted by each sequence's start and P block-diagonal."""
+    q, k, v = _tiny(111, B=3, N=32)
+    ref = O.prefill(q, k, v, block=4, segment=8, scale=0.4, mode=O.KEEP, param=0.5)
+    out = O.prefill_varlen(_pack(q), _pack(k), _pack(v), [0, 32, 64, 96], block=4, segment=8,
+                           scale=0.4, mode=O.KEEP, param=0.5)
+    for b in range(3):
+        a, i0 = 32 * b, 8 * b
+        assert np.array_equal(out["scores"][0, :, a:a + 32], ref["scores"][b])
+        assert np.array_equal(out["perm"][0, :, a:a + 32], ref["perm"][b] + a)
+        assert np.array_equal(out["k_perm"][0, :, a:a + 32], ref["k_perm"][b])
+        assert np.array_equal(out["counts"][0, :, i0:i0 + 8], ref["counts"][b])
+        w = ref["idx"].shape[-1]
+        want = np.where(ref["idx"][b] >= 0, ref["idx"][b] + i0, -1)
+        assert np.array_equal(out["idx"][0, :, i0:i0 + 8, :w], want)
+        assert (out["idx"][0, :, i0:i0 + 8, w:] == -1).all()
+        assert np.array_equal(out["P"][0, :, i0:i0 + 8, i0:i0 + 8], ref["P"][b])
+        P_rest = out["P"][0, :, i0:i0 + 8].copy()
+        P_rest[:, :, i0:i0 + 8] = 0
+        assert (P_rest == 0).all()
+        assert np.array_equal(out["o"][0, :, a:a + 32], ref["o"][b])
+        assert np.array_equal(out["lse"][0, :, a:a + 32], ref["lse"][b])
+
+
+def pin_varlen_keep_one_is_dense_per_sequence(O):
+    """Unequal lengths at keep ratio 1: every sequence equals dense causal attention over its
+    own tokens only."""
+    lens = [16, 32, 8, 24]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v = _tiny(121, N=int(cu[-1]))
+    out = O.prefill_varlen(q, k, v, cu, block=4, segment=8, scale=0.4, mode=O.KEEP, param=1.0)
+    for a, b in zip(cu[:-1], cu[1:]):
+        od, lsed = O.dense_causal(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], block=4, scale=0.4)
+        assert np.abs(out["o"][:, :, a:b] - od).max() < 1e-12
+        assert np.abs(out["lse"][:, :, a:b] - lsed).max() < 1e-12
+
+
+def pin_varlen_sequences_independent(O):
+    """Changing one sequence's tokens changes nothing in the others, and no block list points
+    into another sequence."""
+    lens = [16, 24, 16]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v = _tiny(131, N=int(cu[-1]))
+    out = O.prefill_varlen(q, k, v, cu, block=4, segment=8, scale=0.4, mode=O.KEEP, param=0.5)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[:, :, 16:40], k2[:, :, 16:40], v2[:, :, 16:40] = _tiny(132, N=24)
+    out2 = O.prefill_varlen(q2, k2, v2, cu, block=4, segment=8, scale=0.4, mode=O.KEEP, param=0.5)
+    for sl in (slice(0, 16), slice(40, 56)):
+        assert np.array_equal(out["o"][:, :, sl], out2["o"][:, :, sl])
+        assert np.array_equal(out["perm"][:, :, sl], out2["perm"][:, :, sl])
+    assert not np.array_equal(out["o"][:, :, 16:40], out2["o"][:, :, 16:40])
+    for s_, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        i0, i1 = a // 4, b // 4
+        c = out["counts"][0, :, i0:i1]
+        ix = out["idx"][0, :, i0:i1]
+        live = np.arange(ix.shape[-1])[None, None, :] < c[..., None]
+        assert ((ix >= i0) | ~live).all() and ((ix < i1) | ~live).all()
+        assert (out["perm"][0, :, a:b] >= a).all() and (out["perm"][0, :, a:b] < b).all()
+
+
 # ----------------------------------------------------------------------------- density, coverage
 
 def _bf_coverage(Q, K, vis, scale, t):

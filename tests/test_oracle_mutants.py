@@ -49,6 +49,10 @@ MUTANTS = {
                                   "o[b, g, slots], lse[b, g, slots] = ob, lb                 # the inverse"),
     "qperm_heads_modulo": ("return apply_permutation(q, np.repeat(perm, Hq // Hkv, axis=1))",
                            "return apply_permutation(q, np.tile(perm, (1, Hq // Hkv, 1)))"),
+    "varlen_idx_not_shifted": ('out["idx"][:, :, i0:i1, :w] = np.where(r["idx"] >= 0, r["idx"] + i0, -1)',
+                               'out["idx"][:, :, i0:i1, :w] = r["idx"]'),
+    "varlen_perm_not_shifted": ('out["perm"][:, :, a:b] = r["perm"] + a', 'out["perm"][:, :, a:b] = r["perm"]'),
+    "varlen_P_rows_only": ('out["P"][:, :, i0:i1, i0:i1] = r["P"]', 'out["P"][:, :, i0:i1, :i1 - i0] = r["P"]'),
     "density_perm_max_position": ("perm[b, h, j * block:(j + 1) * block].min() <= last",
                                   "perm[b, h, j * block:(j + 1) * block].max() <= last"),
 }

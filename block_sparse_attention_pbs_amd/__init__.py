@@ -35,7 +35,8 @@ PBS_FLAG_KEEP_FIRST = 2
 
 ENTRY_POINTS = ("pbs_workspace_bytes", "pbs_max_offdiag", "pbs_strerror", "pbs_score",
                 "pbs_permute", "pbs_block_select", "pbs_attn_fwd", "pbs_attn_fwd_hybrid",
-                "pbs_permute_queries", "pbs_attn_fwd_permuted_queries")
+                "pbs_permute_queries", "pbs_attn_fwd_permuted_queries", "pbs_score_varlen",
+                "pbs_block_select_varlen")
 
 
 class PbsError(RuntimeError):
@@ -84,8 +85,14 @@ def lib():
     L.pbs_permute_queries.argtypes = [S, _P, _P, _P, _P]
     L.pbs_attn_fwd_permuted_queries.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                                 _P, _P, _P]
+    L.pbs_score_varlen.argtypes = [S, _P, ctypes.c_int32, _P, _P, ctypes.c_float, _P, _P,
+                                   ctypes.c_size_t, _P]
+    L.pbs_block_select_varlen.argtypes = [S, _P, ctypes.c_int32, _P, _P, _P, ctypes.c_float,
+                                          ctypes.c_int, ctypes.c_double, _P, ctypes.c_int, _P, _P,
+                                          _P, ctypes.c_size_t, _P]
     for name in ("pbs_score", "pbs_permute", "pbs_block_select", "pbs_attn_fwd",
-                 "pbs_attn_fwd_hybrid", "pbs_permute_queries", "pbs_attn_fwd_permuted_queries"):
+                 "pbs_attn_fwd_hybrid", "pbs_permute_queries", "pbs_attn_fwd_permuted_queries",
+                 "pbs_score_varlen", "pbs_block_select_varlen"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -166,6 +173,26 @@ def pbs_block_select(shape, q, k_perm, k_pool, scale, mode, param, blk_scores, f
                                   _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def pbs_score_varlen(shape, cu_seqlens, n_seqs, q, k, scale, scores, workspace,
+                     workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().pbs_score_varlen(ctypes.byref(shape), _ptr(cu_seqlens), n_seqs, _ptr(q), _ptr(k),
+                                  scale, _ptr(scores), _ptr(workspace), workspace_bytes,
+                                  _stream(stream)))
+
+
+def pbs_block_select_varlen(shape, cu_seqlens, n_seqs, q, k_perm, k_pool, scale, mode, param,
+                            blk_scores, flags, counts, idx, workspace, workspace_bytes=None,
+                            stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().pbs_block_select_varlen(ctypes.byref(shape), _ptr(cu_seqlens), n_seqs, _ptr(q),
+                                         _ptr(k_perm), _ptr(k_pool), scale, mode, param,
+                                         _ptr(blk_scores), flags, _ptr(counts), _ptr(idx),
+                                         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 def pbs_attn_fwd(shape, q, k, v, perm, blk_minpos, counts, idx, scale, o, lse=None, stream=None):
     _check(lib().pbs_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm),
                               _ptr(blk_minpos), _ptr(counts), _ptr(idx), scale, _ptr(o), _ptr(lse),
@@ -239,6 +266,31 @@ def prefill(q, k, v, *, block: int, segment: int, keep: Optional[float] = None,
                 stream=stream)
     pbs_block_select(shape, q, bf.k_perm, bf.k_pool, scale, mode, param, bf.blk_scores, 0,
                      bf.counts, bf.idx, bf.workspace, stream=stream)
+    pbs_attn_fwd(shape, q, bf.k_perm, bf.v_perm, bf.perm, bf.blk_minpos, bf.counts, bf.idx, scale,
+                 bf.o, bf.lse, stream=stream)
+    return bf
+
+
+def prefill_varlen(q, k, v, cu_seqlens, *, block: int, segment: int,
+                   keep: Optional[float] = None, coverage: Optional[float] = None,
+                   scale: Optional[float] = None, buffers: Optional[Buffers] = None, stream=None,
+                   layout: int = None) -> Buffers:
+    """PBS-Attn prefill of several sequences packed along N (batch 1): ``cu_seqlens`` is a
+    device int32 tensor of the n+1 sequence starts, every length a multiple of ``segment``.
+    pbs_score_varlen -> pbs_permute -> pbs_block_select_varlen -> pbs_attn_fwd on one stream."""
+    if (keep is None) == (coverage is None):
+        raise PbsError(PBS_E_ARG, "give exactly one of keep / coverage")
+    shape = shape_of(q, k, block, segment, layout)
+    n_seqs = int(cu_seqlens.numel()) - 1
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    bf = buffers or Buffers(shape, q.device)
+    mode, param = (PBS_SELECT_KEEP_RATIO, keep) if keep is not None else (PBS_SELECT_COVERAGE, coverage)
+    pbs_score_varlen(shape, cu_seqlens, n_seqs, q, k, scale, bf.scores, bf.workspace, stream=stream)
+    pbs_permute(shape, bf.scores, k, v, bf.perm, bf.k_perm, bf.v_perm, bf.k_pool, bf.blk_minpos,
+                stream=stream)
+    pbs_block_select_varlen(shape, cu_seqlens, n_seqs, q, bf.k_perm, bf.k_pool, scale, mode, param,
+                            bf.blk_scores, 0, bf.counts, bf.idx, bf.workspace, stream=stream)
     pbs_attn_fwd(shape, q, bf.k_perm, bf.v_perm, bf.perm, bf.blk_minpos, bf.counts, bf.idx, scale,
                  bf.o, bf.lse, stream=stream)
     return bf

@@ -92,18 +92,82 @@ const char* pbs_strerror(int status) {
   }
 }
 
-int pbs_score(const pbs_shape* shape, const uint16_t* q, const uint16_t* k, float scale,
-              float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Packed sequences: one batch row, 1 <= n_seqs <= N / S sequences, boundaries on the device.
+int check_varlen(const Dims& d, const int32_t* cu_seqlens, int32_t n_seqs) {
+  if (d.B != 1 && !empty(d)) return PBS_E_SHAPE;
+  if (!cu_seqlens) return PBS_E_ARG;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return PBS_E_ALIGN;
+  if (n_seqs < 1 || (!empty(d) && n_seqs > d.nseg)) return PBS_E_ARG;
+  return PBS_OK;
+}
+
+int score_impl(const pbs_shape* shape, const int32_t* cu, int32_t nseq, const uint16_t* q,
+               const uint16_t* k, float scale, float* scores, void* workspace,
+               size_t workspace_bytes, void* stream) {
   Dims d;
   int st = check_shape(shape, &d);
   if (st != PBS_OK) return st;
+  if (cu && (st = check_varlen(d, cu, nseq)) != PBS_OK) return st;
   if (!finite_positive(scale)) return PBS_E_ARG;
   if (empty(d)) return PBS_OK;
   const void* const req[] = {q, k, scores, workspace};
   if ((st = check_required(req)) != PBS_OK) return st;
   if (workspace_bytes < pbs::score_workspace_bytes(d)) return PBS_E_WORKSPACE;
-  return status_of(pbs::launch_score(d, q, k, scale, scores, workspace,
+  return status_of(pbs::launch_score(d, q, k, scale, scores, workspace, cu, cu ? nseq : 0,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int select_impl(const pbs_shape* shape, const int32_t* cu, int32_t nseq, const uint16_t* q,
+                const uint16_t* k_perm, const float* k_pool, float scale, int mode, double param,
+                float* blk_scores, int flags, int32_t* counts, int32_t* idx, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  Dims d;
+  int st = check_shape(shape, &d);
+  if (st != PBS_OK) return st;
+  if (cu && (st = check_varlen(d, cu, nseq)) != PBS_OK) return st;
+  if (mode != PBS_SELECT_KEEP_RATIO && mode != PBS_SELECT_COVERAGE) return PBS_E_ARG;
+  if (!(param > 0.0 && param <= 1.0)) return PBS_E_ARG;
+  if (flags & ~(PBS_FLAG_SCORES_IN | PBS_FLAG_KEEP_FIRST)) return PBS_E_ARG;
+  const bool scores_in = (flags & PBS_FLAG_SCORES_IN) != 0;
+  if (!scores_in && !finite_positive(scale)) return PBS_E_ARG;
+  if (empty(d)) return PBS_OK;
+  const void* const req[] = {counts, idx, workspace};
+  if ((st = check_required(req)) != PBS_OK) return st;
+  if (scores_in) {
+    if (!blk_scores) return PBS_E_ARG;
+  } else {
+    if (!q || (!k_perm && !k_pool)) return PBS_E_ARG;
+  }
+  if ((st = check_optional(q)) != PBS_OK) return st;
+  if ((st = check_optional(k_perm)) != PBS_OK) return st;
+  if ((st = check_optional(k_pool)) != PBS_OK) return st;
+  if ((st = check_optional(blk_scores)) != PBS_OK) return st;
+  if (workspace_bytes < pbs::select_workspace_bytes(d)) return PBS_E_WORKSPACE;
+  const bool keep_first = (flags & PBS_FLAG_KEEP_FIRST) != 0;
+  return status_of(pbs::launch_block_select(d, q, k_perm, k_pool, scale, mode, param, blk_scores,
+                                            scores_in, keep_first, counts, idx, workspace, cu,
+                                            cu ? nseq : 0, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pbs_score(const pbs_shape* shape, const uint16_t* q, const uint16_t* k, float scale,
+              float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  return score_impl(shape, nullptr, 0, q, k, scale, scores, workspace, workspace_bytes, stream);
+}
+
+int pbs_score_varlen(const pbs_shape* shape, const int32_t* cu_seqlens, int32_t n_seqs,
+                     const uint16_t* q, const uint16_t* k, float scale, float* scores,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return PBS_E_ARG;
+  return score_impl(shape, cu_seqlens, n_seqs, q, k, scale, scores, workspace, workspace_bytes,
+                    stream);
 }
 
 int pbs_permute(const pbs_shape* shape, const float* scores, const uint16_t* k,
@@ -138,31 +202,18 @@ int pbs_block_select(const pbs_shape* shape, const uint16_t* q, const uint16_t* 
                      const float* k_pool, float scale, int mode, double param,
                      float* blk_scores, int flags, int32_t* counts, int32_t* idx,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  Dims d;
-  int st = check_shape(shape, &d);
-  if (st != PBS_OK) return st;
-  if (mode != PBS_SELECT_KEEP_RATIO && mode != PBS_SELECT_COVERAGE) return PBS_E_ARG;
-  if (!(param > 0.0 && param <= 1.0)) return PBS_E_ARG;
-  if (flags & ~(PBS_FLAG_SCORES_IN | PBS_FLAG_KEEP_FIRST)) return PBS_E_ARG;
-  const bool scores_in = (flags & PBS_FLAG_SCORES_IN) != 0;
-  if (!scores_in && !finite_positive(scale)) return PBS_E_ARG;
-  if (empty(d)) return PBS_OK;
-  const void* const req[] = {counts, idx, workspace};
-  if ((st = check_required(req)) != PBS_OK) return st;
-  if (scores_in) {
-    if (!blk_scores) return PBS_E_ARG;
-  } else {
-    if (!q || (!k_perm && !k_pool)) return PBS_E_ARG;
-  }
-  if ((st = check_optional(q)) != PBS_OK) return st;
-  if ((st = check_optional(k_perm)) != PBS_OK) return st;
-  if ((st = check_optional(k_pool)) != PBS_OK) return st;
-  if ((st = check_optional(blk_scores)) != PBS_OK) return st;
-  if (workspace_bytes < pbs::select_workspace_bytes(d)) return PBS_E_WORKSPACE;
-  const bool keep_first = (flags & PBS_FLAG_KEEP_FIRST) != 0;
-  return status_of(pbs::launch_block_select(d, q, k_perm, k_pool, scale, mode, param, blk_scores,
-                                            scores_in, keep_first, counts, idx, workspace,
-                                            static_cast<hipStream_t>(stream)));
+  return select_impl(shape, nullptr, 0, q, k_perm, k_pool, scale, mode, param, blk_scores, flags,
+                     counts, idx, workspace, workspace_bytes, stream);
+}
+
+int pbs_block_select_varlen(const pbs_shape* shape, const int32_t* cu_seqlens, int32_t n_seqs,
+                            const uint16_t* q, const uint16_t* k_perm, const float* k_pool,
+                            float scale, int mode, double param, float* blk_scores, int flags,
+                            int32_t* counts, int32_t* idx, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return PBS_E_ARG;
+  return select_impl(shape, cu_seqlens, n_seqs, q, k_perm, k_pool, scale, mode, param,
+                     blk_scores, flags, counts, idx, workspace, workspace_bytes, stream);
 }
 
 int pbs_attn_fwd(const pbs_shape* shape, const uint16_t* q, const uint16_t* k,

@@ -88,4 +88,25 @@ __device__ __forceinline__ void bitonic_sort_lds(uint64_t* keys, int n2) {
   __syncthreads();
 }
 
+// Sequence of token p in a packed batch row of T tokens: [lo, hi) with lo <= p < hi.  `cu` holds
+// the n + 1 sequence starts (cu[0] = 0, cu[n] = T); without it the whole row is one sequence.  A
+// binary search over cu (every lane of a wave looks up the same p, so the loads are uniform);
+// malformed boundaries are clamped so that every derived index stays inside the row.
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int T, int p, int& lo,
+                                           int& hi) {
+  if (cu == nullptr) {
+    lo = 0;
+    hi = T;
+    return;
+  }
+  int a = 0, b = n;   // the last s in [0, n) with cu[s] <= p
+  while (b - a > 1) {
+    const int m = (a + b) >> 1;
+    if (cu[m] <= p) a = m;
+    else b = m;
+  }
+  lo = min(max(cu[a], 0), p);
+  hi = max(min(cu[a + 1], T), p + 1);
+}
+
 }  // namespace pbs

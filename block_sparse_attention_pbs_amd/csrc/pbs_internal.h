@@ -43,8 +43,10 @@ inline hipError_t launch(void (*kernel)(Args), dim3 grid, dim3 block, size_t shm
 
 // Workspace of pbs_score: per (batch, KV head, segment, scoring row) softmax max and sum.
 size_t score_workspace_bytes(const Dims& d);
+// cu / nseq: packed sequences (nseq + 1 starts along N) or null / 0 for one sequence per row.
 hipError_t launch_score(const Dims& d, const uint16_t* q, const uint16_t* k, float scale,
-                        float* scores, void* ws, hipStream_t stream);
+                        float* scores, void* ws, const int32_t* cu, int nseq,
+                        hipStream_t stream);
 
 hipError_t launch_permute(const Dims& d, const float* scores, const uint16_t* k,
                           const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
@@ -59,7 +61,8 @@ size_t select_workspace_bytes(const Dims& d);
 hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t* k_perm,
                                const float* k_pool, float scale, int mode, double param,
                                float* blk_scores, bool scores_in, bool keep_first, int32_t* counts,
-                               int32_t* idx, void* ws, hipStream_t stream);
+                               int32_t* idx, void* ws, const int32_t* cu, int nseq,
+                               hipStream_t stream);
 
 // mode: 0 dense causal, 1 PBS with a permutation, 2 PBS in the identity order, 3 PBS with
 // permuted off-diagonal blocks and the own segment read from k_orig/v_orig in natural order,

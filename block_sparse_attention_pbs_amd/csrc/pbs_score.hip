@@ -37,12 +37,23 @@ struct ScoreArgs {
   int chunk, nchunk;  // keys per chunk, chunks per segment
   float c;        // scale * log2(e)
   RowMap qm, km;  // row addressing of q and k (either layout)
+  const int32_t* cu;  // packed sequences: nseq + 1 starts along N, or null (one sequence)
+  int nseq;
 };
 
-// Scoring row r of a KV group -> (query head offset inside the group, query position).
-__device__ __forceinline__ void score_row(const ScoreArgs& a, int r, int& g_local, int& t) {
+// End of the sequence that holds segment sigma (N without packed sequences).
+__device__ __forceinline__ int seq_end(const ScoreArgs& a, int sigma) {
+  int lo, hi;
+  seq_bounds(a.cu, a.nseq, a.N, sigma * a.S, lo, hi);
+  return hi;
+}
+
+// Scoring row r of a KV group -> (query head offset inside the group, query position): the last
+// Bs positions of the sequence, which ends at `end`.
+__device__ __forceinline__ void score_row(const ScoreArgs& a, int r, int end, int& g_local,
+                                          int& t) {
   g_local = r / a.Bs;
-  t = a.N - a.Bs + (r - g_local * a.Bs);
+  t = min(max(end - a.Bs + (r - g_local * a.Bs), 0), a.N - 1);
 }
 
 constexpr int kStatKeys = 64;  // keys per LDS tile in the stats pass
@@ -59,10 +70,11 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int r = blockIdx.y * 128 + w * 32 + c32;
   const bool active = (blockIdx.y * 128 + w * 32) < a.R;  // wave-uniform (R % 32 == 0)
+  const int end = seq_end(a, sigma);
   int g_local = 0, t = 0;
   bf16x8 qf[NKS];
   if (active) {
-    score_row(a, r, g_local, t);
+    score_row(a, r, end, g_local, t);
     const int g = h * a.G + g_local;
     const uint16_t* qrow = a.q + a.qm.off(b, g, t) + hl * 8;
 #pragma unroll
@@ -70,7 +82,7 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
   }
   const size_t krs = static_cast<size_t>(a.km.stride());
   const int kbeg = sigma * a.S + ch * a.chunk;
-  const int first_row = a.N - a.Bs;   // every scoring row is >= first_row
+  const int first_row = end - a.Bs;   // every scoring row is >= first_row
   float m = -INFINITY, l = 0.f;
   for (int k0 = kbeg; k0 < kbeg + a.chunk; k0 += kStatKeys) {
     __syncthreads();
@@ -154,11 +166,14 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
   const int hl = lane >> 5, c32 = lane & 31;
   const int bh = blockIdx.y;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const int key0 = (blockIdx.x * 4 + w) * 32;
-  const bool active = key0 < a.N;  // wave-uniform
-  const int sigma = active ? key0 / a.S : 0;
-  // Every wave of the workgroup lies in one segment only if 128 | S; the stats rows are read
-  // per wave, so waves of different segments are fine.
+  // One workgroup covers up to 128 keys of ONE segment (every wave reads the same scoring rows,
+  // which belong to the segment's sequence); a segment takes ceil(S / 128) workgroups and waves
+  // past its end idle.
+  const int wps = (a.S + 127) / 128;
+  const int sigma = blockIdx.x / wps;
+  const int off = ((blockIdx.x - sigma * wps) * 4 + w) * 32;
+  const bool active = off < a.S;  // wave-uniform
+  const int key0 = sigma * a.S + (active ? off : 0);
   bf16x8 kf[NKS];
   if (active) {
     const uint16_t* krow = a.k + a.km.off(b, h, key0 + c32) + hl * 8;
@@ -169,7 +184,8 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   const float* st_seg = a.lse2 + (static_cast<size_t>(bh) * a.nseg + sigma) * a.R;
-  const bool causal = active && key0 + 31 > a.N - a.Bs;   // uniform: a key may follow a row
+  const int end = seq_end(a, sigma);
+  const bool causal = active && key0 + 31 > end - a.Bs;   // uniform: a key may follow a row
   for (int rc = 0; rc < a.R; rc += 32) {
     __syncthreads();
     {
@@ -177,7 +193,7 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
       for (int c = tid; c < 32 * CH; c += 256) {
         const int rr = c / CH, col = (c % CH) * 8;
         int gl, tt;
-        score_row(a, rc + rr, gl, tt);
+        score_row(a, rc + rr, end, gl, tt);
         const uint16_t* src = a.q + a.qm.off(b, h * a.G + gl, tt) + col;
         *reinterpret_cast<u32x4*>(&Qs[rr * STR + col]) = *reinterpret_cast<const u32x4*>(src);
       }
@@ -196,7 +212,7 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
     const float nl = -st_seg[rc + c32];
     if (causal) {
       int gl, tt;
-      score_row(a, rc + c32, gl, tt);
+      score_row(a, rc + c32, end, gl, tt);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = key0 + (e >> 2) * 8 + hl * 4 + (e & 3);
@@ -231,7 +247,7 @@ hipError_t launch_score_t(const Dims& d, const ScoreArgs& a, hipStream_t stream)
   dim3 gc((d.nseg * a.R + 255) / 256, d.B * d.Hkv);
   e = launch(score_combine_kernel, gc, dim3(256), 0, stream, a);
   if (e != hipSuccess) return e;
-  dim3 g2((d.N + 127) / 128, d.B * d.Hkv);
+  dim3 g2(d.nseg * ((d.S + 127) / 128), d.B * d.Hkv);
   return launch(score_reduce_kernel<D>, g2, dim3(256), 0, stream, a);
 }
 
@@ -253,9 +269,11 @@ size_t score_workspace_bytes(const Dims& d) {
 }
 
 hipError_t launch_score(const Dims& d, const uint16_t* q, const uint16_t* k, float scale,
-                        float* scores, void* ws, hipStream_t stream) {
+                        float* scores, void* ws, const int32_t* cu, int nseq,
+                        hipStream_t stream) {
   ScoreArgs a;
   a.q = q; a.k = k; a.scores = scores;
+  a.cu = cu; a.nseq = nseq;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.N = d.N; a.S = d.S; a.nseg = d.nseg;
   a.R = d.G * d.Bs; a.Bs = d.Bs;
   a.chunk = score_chunk(d);

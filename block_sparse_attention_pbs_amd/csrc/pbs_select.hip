@@ -81,6 +81,8 @@ struct SelArgs {
   int p_in;            // read P instead of computing it
   int keep_first;      // rank key block 0 ahead of every other candidate
   double param;
+  const int32_t* cu;   // packed sequences: nseq + 1 starts along N, or null (one sequence)
+  int nseq, N, bs;
   float tau_f;         // least float f with (double)f >= param (coverage)
   float scale;
 };
@@ -143,7 +145,12 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const int b = blockIdx.y / groups;
   const int g = (blockIdx.y - b * groups) * a.hpw + sub;   // this row's query head
   const int h = g / a.G;
-  const int n = (i / a.bps) * a.bps;          // candidates: blocks of earlier segments
+  // candidates: the blocks of earlier segments of the query block's own sequence
+  const int seg_first = (i / a.bps) * a.bps;
+  int seq_lo, seq_hi;
+  seq_bounds(a.cu, a.nseq, a.N, i * a.bs, seq_lo, seq_hi);
+  const int first = min(seq_lo / a.bs, seg_first);   // the sequence's first block
+  const int n = seg_first - first;                    // candidates first .. seg_first - 1
   int n2 = 1;
   while (n2 < n) n2 <<= 1;
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem) + static_cast<size_t>(sub) * a.n2max;
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   }
 
   if (a.p_in) {
-    for (int j = st; j < n; j += kSub) Ps[j] = prow[j];
+    for (int j = st; j < n; j += kSub) Ps[j] = prow[first + j];
     __syncthreads();
   } else {
     // Logits of all hpw rows: TPC threads per candidate, each with an 8-wide slice of the head
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
         qv[r][4] = x1.x; qv[r][5] = x1.y; qv[r][6] = x1.z; qv[r][7] = x1.w;
       }
     }
-    const float* kb = a.kbar + (static_cast<size_t>(b) * a.Hkv + h) * a.nb * D;
+    const float* kb = a.kbar + ((static_cast<size_t>(b) * a.Hkv + h) * a.nb + first) * D;
     float* Pall = reinterpret_cast<float*>(reinterpret_cast<uint64_t*>(smem) + static_cast<size_t>(a.hpw) * a.n2max);
 #pragma unroll 2
     for (int j0 = 0; j0 < n; j0 += cpi) {
@@ -220,10 +227,11 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
     for (int j = st; j < n; j += kSub) {
       const float p = Ps[j] * inv;
       Ps[j] = p;
-      if (prow) prow[j] = p;
+      if (prow) prow[first + j] = p;
     }
     if (prow)
-      for (int j = n + st; j < a.nb; j += kSub) prow[j] = 0.f;
+      for (int j = st; j < a.nb; j += kSub)
+        if (j < first || j >= seg_first) prow[j] = 0.f;
     __syncthreads();
   }
 
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   int pos = sc[st] - cnt;
   int32_t* out = a.idx + row * a.max_off;
   for (int j = lo; j < hi; ++j)
-    if (flag[j]) out[pos++] = j;
+    if (flag[j]) out[pos++] = first + j;
   if (st == 0) a.counts[row] = kk;
 }
 
@@ -391,7 +399,8 @@ size_t select_workspace_bytes(const Dims& d) {
 hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t* k_perm,
                                const float* k_pool, float scale, int mode, double param,
                                float* blk_scores, bool scores_in, bool keep_first, int32_t* counts,
-                               int32_t* idx, void* ws, hipStream_t stream) {
+                               int32_t* idx, void* ws, const int32_t* cu, int nseq,
+                               hipStream_t stream) {
   float* qbar = static_cast<float*>(ws);
   float* kbar_ws = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                             align256(static_cast<size_t>(d.B) * d.Hq * d.nb * d.d * sizeof(float)));
@@ -420,6 +429,7 @@ hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t*
   sa.hpw = hpw;
   sa.mode = mode; sa.p_in = scores_in ? 1 : 0; sa.param = param; sa.scale = scale;
   sa.keep_first = keep_first ? 1 : 0;
+  sa.cu = cu; sa.nseq = nseq; sa.N = d.N; sa.bs = d.Bs;
   sa.tau_f = static_cast<float>(param);
   if (static_cast<double>(sa.tau_f) < param) sa.tau_f = std::nextafter(sa.tau_f, INFINITY);
   const size_t shmem = hpw * per_row;

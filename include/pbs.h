@@ -259,6 +259,37 @@ int pbs_attn_fwd_hybrid(const pbs_shape* shape, const uint16_t* q, const uint16_
                         const int32_t* counts, const int32_t* idx, float scale, uint16_t* o,
                         float* lse, void* stream);
 
+/*
+ * pbs_score_varlen / pbs_block_select_varlen -- several sequences packed along N.
+ * Passage: the pages define the method on one sequence (gist.science summary, Methodik 2-4;
+ * sciencestack.ai page, Fig. 1 caption); a packed batch applies it to every sequence on its
+ * own: each sequence's segments are scored by that sequence's last Bs query rows, and a query
+ * block's candidates are the blocks of earlier segments of its own sequence only.
+ *
+ *   shape       batch = 1; seq_len = T, the packed length; q/k/v hold the sequences one after
+ *               another along N (in either layout: PBS_LAYOUT_BNHD with batch 1 is the
+ *               FlashAttention varlen layout [T, H, d])
+ *   cu_seqlens  DEVICE int32 [n_seqs + 1], 4-byte aligned: sequence s holds tokens
+ *               cu_seqlens[s] .. cu_seqlens[s+1] - 1, with 0 = cu_seqlens[0] < ... <
+ *               cu_seqlens[n_seqs] = T and every length a multiple of S.  The values are not
+ *               read on the host; boundaries that break these rules give unspecified results,
+ *               but every memory access stays inside the tensors.
+ *   n_seqs      1 <= n_seqs <= T / S (PBS_E_ARG otherwise); batch != 1 -> PBS_E_SHAPE
+ * Every other argument, output and error is as in pbs_score / pbs_block_select; positions and
+ * block indices are absolute in the packed row.  pbs_permute, pbs_attn_fwd,
+ * pbs_attn_fwd_hybrid, pbs_permute_queries and pbs_attn_fwd_permuted_queries take the packed
+ * row unchanged: segments never straddle two sequences and the block lists never leave the
+ * query's sequence.  (The dense mode of pbs_attn_fwd treats the packed row as one sequence.)
+ */
+int pbs_score_varlen(const pbs_shape* shape, const int32_t* cu_seqlens, int32_t n_seqs,
+                     const uint16_t* q, const uint16_t* k, float scale, float* scores,
+                     void* workspace, size_t workspace_bytes, void* stream);
+int pbs_block_select_varlen(const pbs_shape* shape, const int32_t* cu_seqlens, int32_t n_seqs,
+                            const uint16_t* q, const uint16_t* k_perm, const float* k_pool,
+                            float scale, int mode, double param, float* blk_scores, int flags,
+                            int32_t* counts, int32_t* idx, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

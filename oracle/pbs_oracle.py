@@ -537,7 +537,7 @@ def prefill_varlen(q, k, v, cu_seqlens, *, block: int, segment: int, scale: floa
     Hq, Hkv = q.shape[1], k.shape[1]
     nbT = T // block
     width = max((T // segment - 1) * (segment // block), 1)
-    out = dict(scores=np.zeros((1, Hkv, T), np.float32), perm=np.zeros((1, Hkv, T), np.int64),
+    out = dict(scores=np.zeros((1, Hkv, T), np.float32), perm=np.zeros((1, Hkv, T), np.int32),
                k_perm=np.zeros_like(k), v_perm=np.zeros_like(v),
                P=np.zeros((1, Hq, nbT, nbT), np.float32), counts=np.zeros((1, Hq, nbT), np.int32),
                idx=np.full((1, Hq, nbT, width), -1, np.int32),

@@ -110,6 +110,32 @@ def test_errors_before_any_launch():
     assert hyb(fake, fake, fake, lse=fake + 4) == P.PBS_E_ALIGN
 
 
+def test_varlen_errors_before_any_launch():
+    s = P.make_shape(1, 4, 2, 1024, 128, 128, 256)   # 4 segments
+    S = ctypes.byref(s)
+    fake = 0x10000
+    sv = lambda cu, n, ws=1 << 30, shape=S: _call(
+        "pbs_score_varlen", shape, cu, n, fake, fake, 0.1, fake, fake, ws, None)
+    assert sv(fake, 2, shape=ctypes.byref(P.make_shape(2, 4, 2, 1024, 128, 128, 256))) == P.PBS_E_SHAPE
+    assert sv(None, 2) == P.PBS_E_ARG
+    assert sv(fake + 2, 2) == P.PBS_E_ALIGN
+    assert sv(fake, 0) == P.PBS_E_ARG
+    assert sv(fake, 5) == P.PBS_E_ARG                  # more sequences than segments
+    assert sv(fake + 4, 4, ws=16) == P.PBS_E_WORKSPACE   # 4-byte aligned boundaries accepted
+    sl = lambda cu, n, mode=0, ws=1 << 30: _call(
+        "pbs_block_select_varlen", S, cu, n, fake, fake, None, 0.1, mode, 0.5, None, 0, fake, fake,
+        fake, ws, None)
+    assert sl(None, 1) == P.PBS_E_ARG
+    assert sl(fake + 1, 1) == P.PBS_E_ALIGN
+    assert sl(fake, 9) == P.PBS_E_ARG
+    assert sl(fake, 1, mode=3) == P.PBS_E_ARG
+    assert sl(fake, 1, ws=16) == P.PBS_E_WORKSPACE
+    # an empty packed row is a no-op
+    e = P.make_shape(1, 4, 2, 0, 128, 128, 256)
+    assert _call("pbs_score_varlen", ctypes.byref(e), fake, 1, None, None, 0.1, None, None, 0,
+                 None) == P.PBS_OK
+
+
 def test_empty_problem_is_ok_without_pointers():
     s = P.make_shape(0, 4, 2, 1024, 128, 128, 256)
     assert _call("pbs_attn_fwd", ctypes.byref(s), None, None, None, None, None, None, None, 0.1,

@@ -5,7 +5,8 @@
 // attention scores; Methodik 2: no query sees a later segment): for each KV head, each of the
 // R = G*Bs scoring rows (every query head of the group, rows [N-Bs, N)) takes a softmax over the
 // keys of one segment that it may see (causal), and every key's probabilities are averaged over
-// the rows.
+// the rows.  With several sequences packed along N, each sequence is scored on its own: the rows
+// are the last Bs of the sequence that holds the segment.
 //
 // Three kernels, the matrix work on v_mfma_f32_32x32x16_bf16 with S^T = K Q^T (a lane owns one
 // scoring row in the first, one key column in the last):

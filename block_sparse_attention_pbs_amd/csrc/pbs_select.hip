@@ -10,7 +10,9 @@
 // coverage tau keeps the shortest prefix whose sequential float32 sum reaches tau.  Optionally key
 // block 0 (the block of the first tokens, where the attention sink lands) is ranked ahead of
 // every other candidate; the pages name a first-token mask in the authors' code without defining
-// it (codewithpapers.app record), and this is its plainest reading.
+// it (codewithpapers.app record), and this is its plainest reading.  With several sequences
+// packed along N, the candidates are the earlier-segment blocks of the query block's own
+// sequence (block 0 above is then the sequence's first block).
 //
 // Kernels:
 //  * pool: float32 mean of every block of Bs rows (queries; keys too when the caller has no

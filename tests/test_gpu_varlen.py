@@ -204,3 +204,55 @@ def test_varlen_token_major_bit_identical(case):
     assert lists_equal(head.counts.cpu().numpy(), head.idx.cpu().numpy(),
                        tm.counts.cpu().numpy(), tm.idx.cpu().numpy())
     assert torch.equal(head.o.view(torch.int16), tok(tm.o).view(torch.int16))
+
+
+def test_varlen_hybrid_given_oracle_lists(case):
+    """pbs_attn_fwd_hybrid on the packed row: the own segment from the original keys in natural
+    order (a segment never leaves its sequence), the kept blocks from the permuted copies."""
+    ref, sh = case["ref"], case["sh"]
+    g = case["g"]
+    o = torch.empty_like(g["q"])
+    P.pbs_attn_fwd_hybrid(sh, g["q"], dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]), g["k"],
+                          g["v"], dev(ref["counts"]), dev(ref["idx"]), case["scale"], o, None)
+    torch.cuda.synchronize()
+    check_attn(o.float().cpu().numpy(), ref["o"], f"{case['name']} varlen hybrid attention")
+
+
+def test_varlen_permuted_queries(case):
+    """The query-permutation variant on the packed row: queries moved with their KV head's
+    permutation, selection (varlen) on them given the oracle's probabilities of the moved queries,
+    attention with rows written back at their original positions, against the oracle."""
+    ref, w, sh, g, inp = case["ref"], case["w"], case["sh"], case["g"], case["inp"]
+    perm = ref["perm"]
+    qp_ref = oracle.permute_queries(inp["q"], perm)
+    qp = torch.empty_like(g["q"])
+    P.pbs_permute_queries(sh, dev(perm), g["q"], qp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(qp), qp_ref)
+    # the oracle's probabilities of the moved queries, sequence by sequence (block-diagonal)
+    omode = oracle.KEEP if w.mode == "keep" else oracle.COVERAGE
+    nb = w.seq_len // w.block
+    Pq = np.zeros((1, w.heads_q, nb, nb), np.float32)
+    width = ref["idx"].shape[-1]
+    rc = np.zeros((1, w.heads_q, nb), np.int32)
+    ri = np.full((1, w.heads_q, nb, width), -1, np.int32)
+    cu = case["cu"]
+    for a, b in zip(cu[:-1], cu[1:]):
+        i0, i1 = a // w.block, b // w.block
+        Ps = oracle.block_probabilities(qp_ref[:, :, a:b], ref["k_perm"][:, :, a:b],
+                                        block=w.block, segment=w.segment, scale=case["scale"])
+        c_s, x_s = oracle.select_blocks(Ps, block=w.block, segment=w.segment, mode=omode,
+                                        param=w.params[0])
+        Pq[:, :, i0:i1, i0:i1] = Ps
+        rc[:, :, i0:i1] = c_s
+        ri[:, :, i0:i1, :x_s.shape[-1]] = np.where(x_s >= 0, x_s + i0, -1)
+    counts, idx = _select(case, None, None, None, blk_scores=dev(Pq), flags=P.PBS_FLAG_SCORES_IN)
+    assert lists_equal(counts.cpu().numpy(), idx.cpu().numpy(), rc, ri)
+    oo, _ = oracle.attention_permuted_queries(qp_ref, inp["k"], inp["v"], block=w.block,
+                                              segment=w.segment, scale=case["scale"], perm=perm,
+                                              counts=rc, idx=ri)
+    o = torch.empty_like(g["q"])
+    P.pbs_attn_fwd_permuted_queries(sh, qp, dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
+                                    dev(perm), None, counts, idx, case["scale"], o, None)
+    torch.cuda.synchronize()
+    check_attn(o.float().cpu().numpy(), oo, f"{case['name']} varlen permuted-query attention")

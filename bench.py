@@ -208,6 +208,102 @@ def density_main(args):
         torch.cuda.empty_cache()
 
 
+def sweep_main(args):
+    """Latency and speedup against dense causal over keep ratios (the 28/4-head 64K sweep
+    workload, or --workload) or over sequence lengths (the 128K workload's structure at
+    16K..256K, keep 0.1): one JSON line with one point per setting."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_pbs_amd as P
+    import pbs_synth
+
+    dev = torch.device("cuda:0")
+    if args.sweep == "keep":
+        base = pbs_synth.WORKLOADS[args.workload if args.workload != "gqa_128k" else "gqa28_64k_sweep"]
+        points = [(base, r) for r in base.params]
+    elif args.sweep == "length":
+        base = pbs_synth.WORKLOADS["gqa_128k"]
+        points = [(base.scaled(name=f"gqa_{n // 1024}k", seq_len=n), 0.1)
+                  for n in (16384, 32768, 65536, 131072, 262144)]
+    else:
+        raise SystemExit(f"bench.py: unknown sweep {args.sweep!r} (keep or length)")
+    res = []
+    inputs = {}
+    for w, keep in points:
+        if w.name not in inputs:
+            inputs.clear()
+            inp = pbs_synth.make_inputs(w)
+            inputs[w.name] = [torch.from_numpy(inp[x].view(np.int16)).view(torch.bfloat16).to(dev)
+                              for x in ("q", "k", "v")]
+            del inp
+        q, k, v = inputs[w.name]
+        sh = P.shape_of(q, k, w.block, w.segment)
+        bf = P.Buffers(sh, dev)
+        scale = P.default_scale(w.head_dim)
+        stream = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+        def step():
+            ev[0].record(stream)
+            P.pbs_score(sh, q, k, scale, bf.scores, bf.workspace, stream=stream)
+            P.pbs_permute(sh, bf.scores, k, v, bf.perm, bf.k_perm, bf.v_perm, bf.k_pool,
+                          bf.blk_minpos, stream=stream)
+            P.pbs_block_select(sh, q, bf.k_perm, bf.k_pool, scale, P.PBS_SELECT_KEEP_RATIO, keep,
+                               None, 0, bf.counts, bf.idx, bf.workspace, stream=stream)
+            ev[1].record(stream)
+            P.pbs_attn_fwd(sh, q, bf.k_perm, bf.v_perm, bf.perm, bf.blk_minpos, bf.counts, bf.idx,
+                           scale, bf.o, bf.lse, stream=stream)
+            ev[2].record(stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        pre = att = 0.0
+        for _ in range(args.steps):
+            step()
+            ev[2].synchronize()
+            pre += ev[0].elapsed_time(ev[1])
+            att += ev[1].elapsed_time(ev[2])
+        pre /= args.steps
+        att /= args.steps
+        B, Hq, Hkv, N, d, Bs, S = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment
+        nb, bps, G = N // Bs, S // Bs, Hq // Hkv
+        counts = bf.counts.cpu().numpy().astype(np.int64)
+        minpos = bf.blk_minpos.cpu().numpy()
+        last_row = (np.arange(nb) + 1) * Bs - 1
+        ondiag = sum(int((minpos[:, :, (i // bps) * bps:(i // bps) * bps + bps] <= last_row[i]).sum()) * G
+                     for i in range(nb))
+        computed = int(counts.sum()) + ondiag
+        flop_per_block = 4.0 * Bs * Bs * d
+        od = torch.empty_like(q)
+        for _ in range(max(1, args.warmup)):
+            P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale, od, None, stream=stream)
+        torch.cuda.synchronize()
+        dense = 0.0
+        for _ in range(max(1, args.steps // 2)):
+            ev[0].record(stream)
+            P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale, od, None, stream=stream)
+            ev[1].record(stream)
+            ev[1].synchronize()
+            dense += ev[0].elapsed_time(ev[1])
+        dense /= max(1, args.steps // 2)
+        diff_dense = float((od.float() - bf.o.float()).abs().max().item()) if keep >= 1.0 else None
+        dense_blocks = B * Hq * nb * (nb + 1) // 2
+        res.append({"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} block={Bs} segment={S}",
+                    "keep": keep, "prefill_ms": round(pre + att, 4), "attention_ms": round(att, 4),
+                    "score_permute_select_ms": round(pre, 4), "dense_causal_ms": round(dense, 4),
+                    "speedup_vs_dense": round(dense / (pre + att), 3),
+                    "computed_block_frac": round(computed / dense_blocks, 4),
+                    "effective_tflops_computed_blocks": round(computed * flop_per_block / (att * 1e-3) / 1e12, 1),
+                    "dense_tflops": round(dense_blocks * flop_per_block / (dense * 1e-3) / 1e12, 1),
+                    "keep1_max_abs_diff_vs_dense": diff_dense})
+        print(f"[bench] sweep point {res[-1]}", file=sys.stderr, flush=True)
+        del bf, od
+    print(json.dumps({"sweep": args.sweep, "steps": args.steps, "warmup": args.warmup,
+                      "data": "synthetic (seeded planted-salient-key Q/K/V, no trained weights)",
+                      "points": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,11 +327,20 @@ def main():
     ap.add_argument("--density", default=None,
                     help="comma-separated workloads: block density vs attention coverage, permuted vs "
                          "natural order (one JSON line per workload instead of the bench line)")
+    ap.add_argument("--sweep", default=None, choices=["keep", "length"],
+                    help="latency and speedup vs dense over keep ratios (64K, 28/4 heads) or over "
+                         "sequence lengths 16K..256K (one JSON line instead of the bench line)")
     ap.add_argument("--taus", default="0.5,0.7,0.8,0.9,0.95,0.98,0.99,0.995")
     ap.add_argument("--coverage-target", type=float, default=0.975)
     ap.add_argument("--k-boost", type=float, default=None,
                     help="density mode: override the planted salient-key boost (attention concentration)")
     args = ap.parse_args()
+    if args.sweep:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            sys.exit(2)
+        sweep_main(args)
+        return
     if args.density:
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)

@@ -57,7 +57,9 @@ struct AttnArgs {
   int mode;      // 0 dense causal, 1 permuted PBS, 2 identity-order PBS, 3 permuted off-diagonal
                  // blocks with the own segment in natural order, 4 permuted PBS with permuted
                  // queries (output rows written back at their original positions)
-  int xcd_map;   // 1: total work items divisible by 8, use the XCD-grouped order
+  int xcd_map;   // 0: launch order; 1: each XCD runs whole KV heads; 2: each KV head is split
+                 // over xcd_split XCDs, query blocks dealt round-robin among them
+  int xcd_split;
   float c;       // scale * log2(e)
   RowMap qm, km; // row addressing of q / o and of every key and value tensor (either layout)
   int kv_rs;     // elements between consecutive rows of one K/V head (km.stride())
@@ -499,8 +501,18 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
   {
     const int total = gridDim.x;
     const int L = blockIdx.x;
-    const int item = a.xcd_map ? (L & 7) * (total >> 3) + (L >> 3) : L;
     const int per_head = a.G * a.nb;
+    // The hardware deals workgroups round-robin over the 8 XCDs (workgroup L to XCD L % 8), so
+    // L % 8 picks the XCD and L / 8 the position in that XCD's sequence.  Every XCD walks its
+    // items heaviest query block first, keeps to one KV head at a time (its K/V stay in that
+    // XCD's L2) and gets the same mix of heavy and light blocks.
+    int item = L;
+    if (a.xcd_map == 1) {          // B*Hkv a multiple of 8: whole KV heads per XCD
+      item = (L & 7) * (total >> 3) + (L >> 3);
+    } else if (a.xcd_map == 2) {   // 8 a multiple of B*Hkv: xcd_split XCDs share a KV head
+      const int x = L & 7, r = a.xcd_split;
+      item = (x / r) * per_head + (L >> 3) * r + x % r;
+    }
     const int hb = item / per_head;            // b * Hkv + h
     const int rem = item - hb * per_head;
     i = a.nb - 1 - rem / a.G;
@@ -664,7 +676,15 @@ hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, cons
   a.max_off = d.max_off > 0 ? d.max_off : 1;
   a.mode = mode;
   const long long total = static_cast<long long>(d.B) * d.Hq * d.nb;
-  a.xcd_map = (total % 8 == 0) ? 1 : 0;
+  const int heads = d.B * d.Hkv;
+  a.xcd_split = 1;
+  a.xcd_map = 0;
+  if (total % 8 == 0 && heads % 8 == 0) {
+    a.xcd_map = 1;
+  } else if (total % 8 == 0 && 8 % heads == 0) {
+    a.xcd_map = 2;                  // per_head * heads = total, so per_head % (8 / heads) == 0
+    a.xcd_split = 8 / heads;
+  }
   a.c = scale * kLog2e;
   a.qm = q_rows(d);
   a.km = kv_rows(d);

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
   const int bh = blockIdx.z;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int r = blockIdx.y * 128 + w * 32 + c32;
-  const bool active = (blockIdx.y * 128 + w * 32) < a.R;  // wave-uniform (R % 32 == 0)
+  const bool active = static_cast<int>(blockIdx.y) * 128 + w * 32 < a.R;  // wave-uniform (R % 32 == 0)
   const int end = seq_end(a, sigma);
   int g_local = 0, t = 0;
   bf16x8 qf[NKS];
@@ -162,7 +162,6 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
   constexpr int STR = D + 8;
   constexpr int NKS = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[32 * STR];
-  __shared__ float2 St[32];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, c32 = lane & 31;
   const int bh = blockIdx.y;

@@ -21,7 +21,9 @@
 //              butterfly over the 32 lanes of each half-wave (wavefront reduction) gives the
 //              per-key sum, scaled by 1/R.
 // A key can be after a scoring row only in the last Bs positions of the sequence, so only tiles
-// that reach them apply the causal test.
+// that reach them apply the causal test.  Both passes run eight waves per workgroup: a stats
+// workgroup streams each K tile once for 256 scoring rows, a reduce workgroup stages each chunk
+// of rows once for 256 keys.
 #include "pbs_device.h"
 #include "pbs_internal.h"
 
@@ -58,9 +60,17 @@ __device__ __forceinline__ void score_row(const ScoreArgs& a, int r, int end, in
 }
 
 constexpr int kStatKeys = 64;  // keys per LDS tile in the stats pass
+#ifndef PBS_SCORE_STAT_WAVES
+#define PBS_SCORE_STAT_WAVES 8
+#endif
+#ifndef PBS_SCORE_RED_WAVES
+#define PBS_SCORE_RED_WAVES 8
+#endif
+constexpr int kStatWaves = PBS_SCORE_STAT_WAVES;  // waves (32 scoring rows each) per stats workgroup
+constexpr int kRedWaves = PBS_SCORE_RED_WAVES;    // waves (32 keys each) per reduce workgroup
 
 template <int D>
-__global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(64 * kStatWaves) void score_stats_kernel(ScoreArgs a) {
   constexpr int STR = D + 8;
   constexpr int NKS = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kStatKeys * STR];
@@ -69,8 +79,8 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
   const int sigma = blockIdx.x / a.nchunk, ch = blockIdx.x - sigma * a.nchunk;
   const int bh = blockIdx.z;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const int r = blockIdx.y * 128 + w * 32 + c32;
-  const bool active = static_cast<int>(blockIdx.y) * 128 + w * 32 < a.R;  // wave-uniform (R % 32 == 0)
+  const int r = blockIdx.y * (32 * kStatWaves) + w * 32 + c32;
+  const bool active = static_cast<int>(blockIdx.y) * (32 * kStatWaves) + w * 32 < a.R;  // wave-uniform
   const int end = seq_end(a, sigma);
   int g_local = 0, t = 0;
   bf16x8 qf[NKS];
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(256) void score_stats_kernel(ScoreArgs a) {
     {
       const uint16_t* kb = a.k + a.km.off(b, h, k0);
       constexpr int CH = D / 8;
-      for (int c = tid; c < kStatKeys * CH; c += 256) {
+      for (int c = tid; c < kStatKeys * CH; c += 64 * kStatWaves) {
         const int rr = c / CH, col = (c % CH) * 8;
         *reinterpret_cast<u32x4*>(&Ks[rr * STR + col]) =
             *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(rr) * krs + col);
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(256) void score_combine_kernel(ScoreArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(64 * kRedWaves) void score_reduce_kernel(ScoreArgs a) {
   constexpr int STR = D + 8;
   constexpr int NKS = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[32 * STR];
@@ -166,12 +176,12 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
   const int hl = lane >> 5, c32 = lane & 31;
   const int bh = blockIdx.y;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
-  // One workgroup covers up to 128 keys of ONE segment (every wave reads the same scoring rows,
-  // which belong to the segment's sequence); a segment takes ceil(S / 128) workgroups and waves
-  // past its end idle.
-  const int wps = (a.S + 127) / 128;
+  // One workgroup covers up to 32 * kRedWaves keys of ONE segment (every wave reads the same
+  // scoring rows, which belong to the segment's sequence); a segment takes
+  // ceil(S / (32 * kRedWaves)) workgroups and waves past its end idle.
+  const int wps = (a.S + 32 * kRedWaves - 1) / (32 * kRedWaves);
   const int sigma = blockIdx.x / wps;
-  const int off = ((blockIdx.x - sigma * wps) * 4 + w) * 32;
+  const int off = ((blockIdx.x - sigma * wps) * kRedWaves + w) * 32;
   const bool active = off < a.S;  // wave-uniform
   const int key0 = sigma * a.S + (active ? off : 0);
   bf16x8 kf[NKS];
@@ -190,7 +200,7 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
     __syncthreads();
     {
       constexpr int CH = D / 8;
-      for (int c = tid; c < 32 * CH; c += 256) {
+      for (int c = tid; c < 32 * CH; c += 64 * kRedWaves) {
         const int rr = c / CH, col = (c % CH) * 8;
         int gl, tt;
         score_row(a, rc + rr, end, gl, tt);
@@ -241,14 +251,14 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(ScoreArgs a) {
 
 template <int D>
 hipError_t launch_score_t(const Dims& d, const ScoreArgs& a, hipStream_t stream) {
-  dim3 g1(d.nseg * a.nchunk, (a.R + 127) / 128, d.B * d.Hkv);
-  hipError_t e = launch(score_stats_kernel<D>, g1, dim3(256), 0, stream, a);
+  dim3 g1(d.nseg * a.nchunk, (a.R + 32 * kStatWaves - 1) / (32 * kStatWaves), d.B * d.Hkv);
+  hipError_t e = launch(score_stats_kernel<D>, g1, dim3(64 * kStatWaves), 0, stream, a);
   if (e != hipSuccess) return e;
   dim3 gc((d.nseg * a.R + 255) / 256, d.B * d.Hkv);
   e = launch(score_combine_kernel, gc, dim3(256), 0, stream, a);
   if (e != hipSuccess) return e;
-  dim3 g2(d.nseg * ((d.S + 127) / 128), d.B * d.Hkv);
-  return launch(score_reduce_kernel<D>, g2, dim3(256), 0, stream, a);
+  dim3 g2(d.nseg * ((d.S + 32 * kRedWaves - 1) / (32 * kRedWaves)), d.B * d.Hkv);
+  return launch(score_reduce_kernel<D>, g2, dim3(64 * kRedWaves), 0, stream, a);
 }
 
 }  // namespace

@@ -4,7 +4,7 @@ two equivalences on the GPU alone: equal lengths give the batched result bit for
 token-major packed layout gives the head-major one bit for bit.
 
 Cases mix sequence lengths, both head dims and block sizes, a segment of 192 tokens (not a
-multiple of the 128-key workgroup of the score reduction) and segments of a single block."""
+multiple of the 256-key workgroup of the score reduction) and segments of a single block."""
 import zlib
 
 import numpy as np

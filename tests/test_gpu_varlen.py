@@ -256,3 +256,27 @@ def test_varlen_permuted_queries(case):
                                     dev(perm), None, counts, idx, case["scale"], o, None)
     torch.cuda.synchronize()
     check_attn(o.float().cpu().numpy(), oo, f"{case['name']} varlen permuted-query attention")
+
+
+def test_varlen_malformed_boundaries_stay_in_bounds():
+    """Boundaries that break the documented rules (out of order, past the row, lengths not a
+    multiple of S) give unspecified selections, but every access stays inside the tensors: the
+    calls complete, the scores are finite and non-negative, and every list entry is a block of an
+    earlier segment."""
+    w = pbs_synth.WORKLOADS["gqa_8k"].scaled(name="varlen_bad", heads_q=4, heads_kv=1,
+                                             seq_len=4096, segment=512, seed=777)
+    inp = pbs_synth.make_inputs(w)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    nb, bps = w.seq_len // w.block, w.segment // w.block
+    for cu in ([0, 700, 300, 9000, 4096], [0, 4096 + 512, 100], [4000, 1, 2, 3, 4096]):
+        out = P.prefill_varlen(q, k, v, dev(np.array(cu, np.int32)), block=w.block,
+                               segment=w.segment, keep=0.3)
+        torch.cuda.synchronize()
+        s = out.scores.cpu().numpy()
+        assert np.isfinite(s).all() and (s >= 0).all()
+        c, ix = out.counts.cpu().numpy(), out.idx.cpu().numpy()
+        seg_first = (np.arange(nb) // bps) * bps
+        live = np.arange(ix.shape[-1])[None, None, None, :] < c[..., None]
+        assert ((ix >= 0) & (ix < seg_first[None, None, :, None]) | ~live).all()
+        assert np.isfinite(out.o.float().cpu().numpy()).all()
+        say(f"malformed boundaries {cu}: completed, finite, lists inside earlier segments")

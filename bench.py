@@ -317,6 +317,8 @@ def main():
                     help="skip timing the query-permutation variant")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the prefill")
+    ap.add_argument("--no-sdpa", action="store_true",
+                    help="skip the torch scaled_dot_product_attention reference")
     ap.add_argument("--no-gemm", action="store_true",
                     help="skip the hipBLASLt bf16 GEMM reference measurement")
     ap.add_argument("--no-hybrid", action="store_true",
@@ -587,6 +589,37 @@ def main():
                 "attention_over_gemm": round(eff_tflops / g_tflops, 4)}
         del ga, gb, gc
 
+    # Reference: PyTorch's own fused causal attention on the same inputs (scaled_dot_product_attention,
+    # flash backend; K/V repeated to the query heads), timed the same way.  Context for the dense
+    # baseline above, not part of the path.
+    sdpa = None
+    if not args.no_sdpa and not args.no_dense:
+        try:
+            from torch.nn.attention import SDPBackend, sdpa_kernel
+            kk = k.repeat_interleave(G, dim=1)
+            vv = v.repeat_interleave(G, dim=1)
+            with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+                ref_o = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, is_causal=True,
+                                                                         scale=scale)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 3
+                e0.record()
+                for _ in range(reps):
+                    torch.nn.functional.scaled_dot_product_attention(q, kk, vv, is_causal=True,
+                                                                     scale=scale)
+                e1.record()
+                e1.synchronize()
+            sdpa_ms = e0.elapsed_time(e1) / reps
+            sdpa = {"what": "torch.nn.functional.scaled_dot_product_attention, flash backend, causal",
+                    "ms": round(sdpa_ms, 3),
+                    "tflops_causal": round(dense_blocks * flop_per_block / (sdpa_ms * 1e-3) / 1e12, 1),
+                    "dense_kernel_speedup_over_it": round(sdpa_ms / dense_ms, 3),
+                    "pbs_prefill_speedup_over_it": round(sdpa_ms / pbs_ms, 3)}
+            del kk, vv, ref_o
+        except Exception as ex:   # backend missing on this build of torch
+            sdpa = {"unavailable": str(ex)[:200]}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -643,6 +676,7 @@ def main():
         },
         "hip_graph_replay": graph,
         "library_gemm_reference": gemm,
+        "torch_sdpa_reference": sdpa,
         "hybrid_own_segment_natural": hybrid,
         "permuted_queries": qperm,
         "cpu_baseline": cpu,

@@ -49,6 +49,25 @@ def attn_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def own_segment_blocks(perm, block: int, segment: int, G: int) -> float:
+    """Block-equivalents of own-segment work the attention kernel does (pbs_attn_fwd): for every
+    query block, the slots of its segment whose original position is at or before the block's
+    last row, walked 32 keys per stage (keys after every row of the block add nothing and are
+    not loaded).  Summed over the G query heads of each KV head."""
+    import numpy as np
+    B, H, N = perm.shape
+    bps = segment // block
+    total = 0.0
+    for b in range(B):
+        for h in range(H):
+            for s0 in range(0, N, segment):
+                pos = np.sort(perm[b, h, s0:s0 + segment].astype(np.int64))
+                last = s0 + (np.arange(bps) + 1) * block - 1
+                vis = np.searchsorted(pos, last, side="right")
+                total += float((np.ceil(vis / 32.0) * 32.0).sum()) / block
+    return total * G
+
+
 def read_traffic(workload: str):
     """HBM bytes per attention launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE,
     scaled by a copy-kernel calibration), valid only if the kernel source is unchanged."""
@@ -269,11 +288,7 @@ def sweep_main(args):
         B, Hq, Hkv, N, d, Bs, S = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment
         nb, bps, G = N // Bs, S // Bs, Hq // Hkv
         counts = bf.counts.cpu().numpy().astype(np.int64)
-        minpos = bf.blk_minpos.cpu().numpy()
-        last_row = (np.arange(nb) + 1) * Bs - 1
-        ondiag = sum(int((minpos[:, :, (i // bps) * bps:(i // bps) * bps + bps] <= last_row[i]).sum()) * G
-                     for i in range(nb))
-        computed = int(counts.sum()) + ondiag
+        computed = int(counts.sum()) + own_segment_blocks(bf.perm.cpu().numpy(), Bs, S, G)
         flop_per_block = 4.0 * Bs * Bs * d
         od = torch.empty_like(q)
         for _ in range(max(1, args.warmup)):
@@ -458,14 +473,9 @@ def main():
     B, Hq, Hkv, N, d, Bs, S = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment
     nb, bps, G = N // Bs, S // Bs, Hq // Hkv
     counts = bf.counts.cpu().numpy().astype(np.int64)
-    minpos = bf.blk_minpos.cpu().numpy()
-    last_row = (np.arange(nb) + 1) * Bs - 1
-    ondiag = 0
-    for i in range(nb):
-        s0 = (i // bps) * bps
-        ondiag_blocks = minpos[:, :, s0:s0 + bps] <= last_row[i]          # [B, Hkv, bps]
-        ondiag += int(ondiag_blocks.sum()) * G
-    computed = int(counts.sum()) + ondiag
+    # kept earlier-segment blocks in full, plus the own segment's visible keys (32-key stages)
+    computed = int(counts.sum()) + own_segment_blocks(bf.perm.cpu().numpy(), Bs, S, G)
+    computed = int(round(computed)) if abs(computed - round(computed)) < 1e-6 else round(computed, 3)
     flop_per_block = 4.0 * Bs * Bs * d
     attn_flops = computed * flop_per_block
     dense_blocks = B * Hq * nb * (nb + 1) // 2

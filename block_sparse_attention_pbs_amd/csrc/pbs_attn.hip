@@ -78,6 +78,8 @@ struct AttnArgs {
 constexpr int kStageKeys = PBS_ATTN_STAGE_KEYS;  // keys per LDS stage
 constexpr int kOffWindow = 1792; // off-diagonal list entries held in LDS at a time
 constexpr int kOwnMax = 256;     // own-segment blocks (S / Bs <= 16384 / 64)
+constexpr int kOwnWin = 2048;    // visible own-segment keys held in LDS at a time (modes 1, 4)
+constexpr int kSegWords = 16384 / 64;   // 64-slot words of the largest segment's visibility bitmap
 
 template <int D, int BS>
 struct Cfg {
@@ -166,6 +168,20 @@ struct StageIter {
   uint16_t* offw;       // LDS window of the off-diagonal list
   const uint16_t* ownl; // LDS list of the visible own-segment blocks
   int ent;              // the next entry's LDS word, read ahead (per lane, all lanes equal)
+  // Modes 1 and 4: the own segment is walked as a stream of its VISIBLE keys -- the slots whose
+  // original position is at or before the query block's last row, in permuted (slot) order -- 32
+  // per stage.  A key after every row of the query block adds exactly zero to every row, so it
+  // is never loaded; the rest still go through the per-key causal test.
+  bool ks_on;
+  int n_ks;             // visible own-segment keys: first those visible to every row of the
+  int n_ks_full;        // block (n_ks_full of them, unmasked stages), then the others
+  int ks;               // next stream stage
+  int kidx;             // stream index of the stage just returned (-1: a contiguous block stage)
+  int kwin;             // first stream index held in the LDS window
+  int kfill, kscan;     // wave 0 only: entries in the window, next bitmap word to expand
+  uint16_t* ownk;       // LDS window: segment slots of visible keys (kOwnWin + 64 entries)
+  const uint64_t* bits; // LDS bitmaps of the segment's slots, 64 per word: seg_words words of
+  int seg_words;        // slots visible to every row, then seg_words words of the other visible ones
 
   // Load off-diagonal entries [w0, w0 + kOffWindow) into LDS (all threads; barrier after).
   __device__ __forceinline__ void fill(int w0, int tid, int nt) {
@@ -177,9 +193,41 @@ struct StageIter {
   __device__ __forceinline__ int read_entry(int k) const {
     return k < n_off ? offw[k - win] : static_cast<int>(ownl[k - n_off]);
   }
-  __device__ __forceinline__ void start(int tid, int nt) {
+  // Wave 0: expand bitmap words from kscan on into the slot window until it holds at least
+  // kOwnWin entries or the bitmap ends (LDS only: the bitmap is built once per workgroup).
+  __device__ __forceinline__ void scan_fill(int lane) {
+    while (kfill < kOwnWin && kscan < 2 * seg_words) {
+      const uint64_t bal = bits[kscan];
+      const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+      const int word = kscan < seg_words ? kscan : kscan - seg_words;
+      if ((bal >> lane) & 1ull) ownk[kfill + before] = static_cast<uint16_t>(word * 64 + lane);
+      kfill += __builtin_popcountll(bal);
+      ++kscan;
+    }
+  }
+  // Make stream indices [k0, k0 + 32) available in the window.  Called by every wave right after
+  // a barrier, so no wave still reads the window; the entries from k0 to the end of the window
+  // (at most 94) move to its front, the scan continues behind them.
+  __device__ __forceinline__ void refill(int k0, int w, int lane) {
+    if (w == 0) {
+      const int keep = kwin + kfill - k0;
+      const int src = k0 - kwin;
+      const uint16_t e0 = lane < keep ? ownk[src + lane] : static_cast<uint16_t>(0);
+      const uint16_t e1 = lane + 64 < keep ? ownk[src + 64 + lane] : static_cast<uint16_t>(0);
+      if (lane < keep) ownk[lane] = e0;
+      if (lane + 64 < keep) ownk[64 + lane] = e1;
+      kfill = max(keep, 0);
+      scan_fill(lane);
+    }
+    kwin = k0;
+    __syncthreads();
+  }
+  __device__ __forceinline__ void start(int tid, int nt, int w, int lane) {
     m = 0;
     half = -1;
+    ks = 0;
+    kidx = -1;
     if (mode != 0) {
       if (win != 0) {  // a long list left a later window in LDS
         __syncthreads();
@@ -187,6 +235,16 @@ struct StageIter {
         __syncthreads();
       }
       if (n_off + n_own > 0) ent = read_entry(0);
+    }
+    if (ks_on && kwin != 0) {  // a long stream left a later window in LDS: scan again from 0
+      __syncthreads();
+      if (w == 0) {
+        kfill = 0;
+        kscan = 0;
+        scan_fill(lane);
+      }
+      kwin = 0;
+      __syncthreads();
     }
   }
   __device__ __forceinline__ bool next_block(int tid, int nt) {
@@ -211,13 +269,25 @@ struct StageIter {
     return true;
   }
   // Advance to the next stage; false when the list is exhausted.
-  __device__ __forceinline__ bool next(int tid, int nt) {
+  __device__ __forceinline__ bool next(int tid, int nt, int w, int lane) {
     if (half >= 0 && half + 1 < halves) {
       ++half;
       return true;
     }
     half = 0;
-    return next_block(tid, nt);
+    if (!ks_on || m < n_off) {
+      kidx = -1;
+      return next_block(tid, nt);
+    }
+    if (ks * 32 >= n_ks) return false;
+    kidx = __builtin_amdgcn_readfirstlane(ks * 32);
+    ks = __builtin_amdgcn_readfirstlane(ks + 1);
+    if (kidx + 32 > kwin + kOwnWin) refill(kidx, w, lane);
+    j = seg_first;
+    masked = kidx + 32 > n_ks_full;   // holds a key that some row of the block must not see
+    orig = false;
+    half = halves - 1;   // one stage per stream step
+    return true;
   }
 };
 
@@ -225,7 +295,29 @@ struct Stage {
   int key0;     // first key of the stage in the head's key order (block * Bs + stage * 32)
   bool masked;
   bool orig;    // read from the original keys and values (mode 3 own segment)
+  // Own-segment key-stream stage (modes 1, 4): the segment slots of its keys and how many are
+  // valid (1..32); slots == nullptr for a contiguous stage.  seg0: first key of the segment.
+  const uint16_t* slots;
+  int cnt, seg0;
 };
+
+// The stage the iterator just returned.
+template <int BS, int SK>
+__device__ __forceinline__ Stage stage_of(const StageIter& it) {
+  Stage st;
+  st.key0 = it.j * BS + it.half * SK;
+  st.masked = it.masked;
+  st.orig = it.orig;
+  st.slots = nullptr;
+  st.cnt = 0;
+  st.seg0 = it.seg_first * BS;
+  if (it.kidx >= 0) {
+    st.slots = it.ownk + (it.kidx - it.kwin);
+    st.cnt = min(32, it.n_ks - it.kidx);
+    st.key0 = st.seg0;
+  }
+  return st;
+}
 
 // Buffer resources of one head: keys, values, key positions, and (mode 3) the original keys
 // and values.
@@ -235,11 +327,53 @@ struct Rsrc {
 
 // Start the asynchronous loads of one stage (K, V and, for masked permuted blocks, the original
 // positions of its keys) into LDS.  A spare chunk of a padded row re-reads chunk 0 of its row.
+// A key-stream stage gathers its rows: row r of the stage is segment slot slots[r] (rows past
+// the valid count repeat the last valid slot and get a position after every row, so they are
+// masked out).
+template <int D, int BS>
+__device__ __forceinline__ void issue_gathered(const AttnArgs& a, const Rsrc& rr, Stage st,
+                                               uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
+                                               int lane) {
+  using C = Cfg<D, BS>;
+  const uint32_t base = static_cast<uint32_t>(st.seg0) * static_cast<uint32_t>(a.kv_rs) * 2;
+#pragma unroll
+  for (int n = w; n < C::NLDK; n += C::NW) {
+    const int P = n * 64 + lane;
+    const int r = P / (C::CPR + C::KPAD), pc = P - r * (C::CPR + C::KPAD);
+    if (C::KCH % 64 == 0 || P < C::KCH) {
+      const int slot = st.slots[min(r, st.cnt - 1)];
+      load_lds16(rr.k, Kst + n * 512,
+                 static_cast<uint32_t>((slot * a.kv_rs + (pc < C::CPR ? pc : 0) * 8) * 2), base);
+    }
+  }
+#pragma unroll
+  for (int n = w; n < C::NLDV; n += C::NW) {
+    const int P = n * 64 + lane;
+    const int r = P / (C::CPR + C::VPAD), pc = P - r * (C::CPR + C::VPAD);
+    if (C::VCH % 64 == 0 || P < C::VCH) {
+      const int slot = st.slots[min(r, st.cnt - 1)];
+      load_lds16(rr.v, Vst + n * 512,
+                 static_cast<uint32_t>((slot * a.kv_rs + (pc < C::CPR ? pc : 0) * 8) * 2), base);
+    }
+  }
+  if (st.masked && w == 0 && lane < C::SK) {
+    if (lane < st.cnt)
+      load_lds4(rr.p, Pst, static_cast<uint32_t>(st.slots[lane]) * 4,
+                static_cast<uint32_t>(st.seg0) * 4);
+    else
+      Pst[lane] = a.N + 1;   // after every row: the padding row is masked
+  }
+}
+
 template <int D, int BS>
 __device__ __forceinline__ void issue_stage(const AttnArgs& a, const Rsrc& rr, Stage st,
                                             uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
                                             int lane) {
   using C = Cfg<D, BS>;
+  if (st.slots != nullptr) {
+    issue_gathered<D, BS>(a, rr, st, Kst, Vst, Pst, w, lane);
+    return;
+  }
   const uint32_t base = static_cast<uint32_t>(st.key0) * static_cast<uint32_t>(a.kv_rs) * 2;
   const u32x4 rk = st.orig ? rr.k2 : rr.k;
   const u32x4 rv = st.orig ? rr.v2 : rr.v;
@@ -418,14 +552,16 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // the current stage landed; the other buffer is no longer read
     const int p = pp.p;
-    const bool more = it.next(tid, C::NT);
-    Stage nxt;
-    nxt.key0 = it.j * BS + it.half * C::SK;
-    nxt.masked = it.masked;
-    nxt.orig = it.orig;
-    if (more)
-      issue_stage<D, BS>(a, rr, nxt, smem + (p ? a.tile_off[0] : a.tile_off[1]),
-                         smem + (p ? a.tile_off[2] : a.tile_off[3]), p ? Ps0 : Ps1, w, lane);
+    const bool more = it.next(tid, C::NT, w, lane);
+    const Stage nxt = stage_of<BS, C::SK>(it);
+    if (more) {
+      uint16_t* Kn = smem + (p ? a.tile_off[0] : a.tile_off[1]);
+      uint16_t* Vn = smem + (p ? a.tile_off[2] : a.tile_off[3]);
+      if constexpr (MASKED && MODE == 1)   // the own segment: always a key stream
+        issue_gathered<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
+      else
+        issue_stage<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
+    }
     attn_stage<D, BS, MODE, MASKED, MAXONLY>(
         a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
         p ? Ps1 : Ps0, pp.cur.key0, lane, t, qf, oacc, rs);
@@ -440,26 +576,24 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
 // the rows' references are first set from the max of the pass's first stage (computed once more,
 // scores only, as soon as that stage has landed).
 template <int D, int BS, int MODE, bool MAXONLY, bool PRIME>
-__device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int n_unmasked,
-                                          int n_masked, const Rsrc& rr,
+__device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int n_unm_stages,
+                                          int n_msk_stages, const Rsrc& rr,
                                           uint16_t* smem, int32_t* Ps0, int32_t* Ps1, int w,
                                           int lane, int t, const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
   using C = Cfg<D, BS>;
   const int tid = threadIdx.x;
-  it.start(tid, C::NT);
-  if (it.next(tid, C::NT)) {
+  it.start(tid, C::NT, w, lane);
+  if (it.next(tid, C::NT, w, lane)) {
     Pipe pp;
-    pp.cur.key0 = it.j * BS + it.half * C::SK;
-    pp.cur.masked = it.masked;
-    pp.cur.orig = it.orig;
+    pp.cur = stage_of<BS, C::SK>(it);
     pp.p = 0;
     issue_stage<D, BS>(a, rr, pp.cur, smem + a.tile_off[0], smem + a.tile_off[2], Ps0, w, lane);
     if constexpr (PRIME) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       RowState first{0.f, 0.f, -INFINITY};
-      if (n_unmasked > 0)
+      if (n_unm_stages > 0)
         attn_stage<D, BS, MODE, false, true>(a, smem + a.tile_off[0], smem + a.tile_off[2], Ps0,
                                              pp.cur.key0, lane, t, qf, oacc, first);
       else
@@ -467,9 +601,9 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
                                             pp.cur.key0, lane, t, qf, oacc, first);
       rs.mref = (first.mseen == -INFINITY) ? 0.f : first.mseen;
     }
-    run_stages<D, BS, MODE, false, MAXONLY>(a, it, n_unmasked * C::HALVES, pp, rr, smem,
+    run_stages<D, BS, MODE, false, MAXONLY>(a, it, n_unm_stages, pp, rr, smem,
                                             Ps0, Ps1, w, lane, t, qf, oacc, rs);
-    run_stages<D, BS, MODE, true, MAXONLY>(a, it, n_masked * C::HALVES, pp, rr, smem, Ps0,
+    run_stages<D, BS, MODE, true, MAXONLY>(a, it, n_msk_stages, pp, rr, smem, Ps0,
                                            Ps1, w, lane, t, qf, oacc, rs);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -485,8 +619,12 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
   __shared__ __attribute__((aligned(16))) int32_t Ps1[C::SK];
   __shared__ uint16_t offw[kOffWindow];
   __shared__ uint16_t ownl[kOwnMax];
+  __shared__ uint16_t ownk[MODE == 1 ? kOwnWin + 64 : 1];
+  __shared__ uint64_t ownbits[MODE == 1 ? 2 * kSegWords : 1];
   __shared__ int own_count;
   __shared__ int qmax_w[C::NW];
+  __shared__ int qmin_w[C::NW];
+  __shared__ int own_full;
   // Visit-list and key-mask rules: mode 4 (permuted queries) walks the permuted keys like mode 1.
   constexpr int LM = (MODE == 4) ? 1 : MODE;
 
@@ -554,6 +692,17 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
   it.masked = false;
   it.orig = false;
   it.ent = 0;
+  it.ks_on = (MODE == 1);
+  it.n_ks = 0;
+  it.n_ks_full = 0;
+  it.ks = 0;
+  it.kidx = -1;
+  it.kwin = 0;
+  it.kfill = 0;
+  it.kscan = 0;
+  it.ownk = ownk;
+  it.bits = ownbits;
+  it.seg_words = (a.bps * BS) / 64;
   if (MODE != 0) {
     const size_t row = (static_cast<size_t>(b) * a.Hq + g) * a.nb + i;
     it.n_off = min(max(a.counts[row], 0), it.seg_first);
@@ -563,47 +712,105 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
     // its smallest original position is after the query block's last row; every visited block
     // is masked per key.  Identity order: blocks up to the diagonal, only the diagonal masked.
     int last_row = i * BS + BS - 1;   // the latest original position among the block's rows
+    int first_row = i * BS;           // the earliest
     if constexpr (MODE == 4) {
-      int mx = t;
+      int mx = t, mn = t;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
-      if (lane == 0) qmax_w[w] = mx;
+      for (int o = 32; o > 0; o >>= 1) {
+        mx = max(mx, __shfl_xor(mx, o));
+        mn = min(mn, __shfl_xor(mn, o));
+      }
+      if (lane == 0) {
+        qmax_w[w] = mx;
+        qmin_w[w] = mn;
+      }
       __syncthreads();
       last_row = qmax_w[0];
+      first_row = qmin_w[0];
 #pragma unroll
-      for (int ww = 1; ww < C::NW; ++ww) last_row = max(last_row, qmax_w[ww]);
-    }
-    if (w == 0) {
-      const int32_t* mp = a.minpos ? a.minpos + kv_head / BS + it.seg_first : nullptr;
-      int n = 0;
-      for (int o0 = 0; o0 < a.bps; o0 += 64) {
-        const int o = o0 + lane;
-        const int jj = it.seg_first + o;
-        bool vis = false;
-        if (o < a.bps) vis = (LM != 1) ? (jj <= i) : (mp == nullptr || mp[o] <= last_row);
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
-        const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
-        if (vis)
-          ownl[n + before] = static_cast<uint16_t>(jj | ((LM == 1 || jj == i) ? 0x8000 : 0));
-        n += __builtin_popcountll(bal);
+      for (int ww = 1; ww < C::NW; ++ww) {
+        last_row = max(last_row, qmax_w[ww]);
+        first_row = min(first_row, qmin_w[ww]);
       }
-      if (lane == 0) own_count = n;
     }
-    __syncthreads();
-    it.n_own = own_count;
+    if constexpr (MODE == 1) {
+      // The own segment as a key stream.  Every wave reads a quarter of the segment's positions
+      // (four independent coalesced loads per step) and stores one 64-slot visibility word per
+      // ballot (visible: position at or before the block's last row); then wave 0 expands the
+      // first words into the LDS window of slots.
+      const int32_t* pseg = a.perm + kv_head + static_cast<size_t>(it.seg_first) * BS;
+      if (tid == 0) {
+        own_count = 0;
+        own_full = 0;
+      }
+      __syncthreads();
+      int n = 0, nf = 0;
+      for (int c = w * 4; c < it.seg_words; c += C::NW * 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int word = c + q;
+          const int pos = word < it.seg_words ? pseg[word * 64 + lane] : 0x7fffffff;
+          const uint64_t full = __builtin_amdgcn_ballot_w64(pos < first_row);
+          const uint64_t part = __builtin_amdgcn_ballot_w64(pos >= first_row && pos <= last_row);
+          if (word < it.seg_words && lane == 0) {
+            ownbits[word] = full;
+            ownbits[it.seg_words + word] = part;
+          }
+          nf += __builtin_popcountll(full);
+          n += __builtin_popcountll(full) + __builtin_popcountll(part);
+        }
+      }
+      if (lane == 0) {
+        atomicAdd(&own_count, n);
+        atomicAdd(&own_full, nf);
+      }
+      __syncthreads();
+      it.n_ks = own_count;
+      it.n_ks_full = own_full;
+      if (w == 0) it.scan_fill(lane);
+      __syncthreads();
+    } else {
+      // Own-segment blocks, compacted by wave 0.  Permuted queries (mode 4): a permuted block is
+      // skipped when its smallest original position is after every row of the block, every
+      // visited block is masked per key.  Identity order: the blocks up to the diagonal, only
+      // the diagonal masked.
+      if (w == 0) {
+        const int32_t* mp = a.minpos ? a.minpos + kv_head / BS + it.seg_first : nullptr;
+        int n = 0;
+        for (int o0 = 0; o0 < a.bps; o0 += 64) {
+          const int o = o0 + lane;
+          const int jj = it.seg_first + o;
+          bool vis = false;
+          if (o < a.bps) vis = (LM == 1) ? (mp == nullptr || mp[o] <= last_row) : (jj <= i);
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
+          const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+          if (vis)
+            ownl[n + before] = static_cast<uint16_t>(jj | ((LM == 1 || jj == i) ? 0x8000 : 0));
+          n += __builtin_popcountll(bal);
+        }
+        if (lane == 0) own_count = n;
+      }
+      __syncthreads();
+      it.n_own = own_count;
+    }
   }
-  // Unmasked entries come first in every visit list, masked ones last.
+  // Unmasked stages come first in every visit list, masked ones last.
   int n_unm, n_msk;
   if (MODE == 0) {
-    n_unm = i;
-    n_msk = 1;
+    n_unm = i * C::HALVES;
+    n_msk = C::HALVES;
+  } else if (MODE == 1) {
+    // the own segment's key stream: whole stages of keys every row sees run unmasked
+    n_unm = it.n_off * C::HALVES + it.n_ks_full / 32;
+    n_msk = (it.n_ks + 31) / 32 - it.n_ks_full / 32;
   } else if (LM == 1) {
-    n_unm = it.n_off;
-    n_msk = it.n_own;
+    n_unm = it.n_off * C::HALVES;
+    n_msk = it.n_own * C::HALVES;
   } else {
-    n_msk = it.n_own > 0 ? 1 : 0;   // the diagonal block closes the identity-order list
-    n_unm = it.n_off + it.n_own - n_msk;
+    const int nm = it.n_own > 0 ? 1 : 0;   // the diagonal block closes the identity-order list
+    n_unm = (it.n_off + it.n_own - nm) * C::HALVES;
+    n_msk = nm * C::HALVES;
   }
 
   // Q fragments (B operand of S^T = K Q^T): lane holds q[t][ks*16 + hl*8 .. +8]

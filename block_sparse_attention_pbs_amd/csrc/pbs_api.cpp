@@ -28,6 +28,10 @@ int check_shape(const pbs_shape* s, Dims* d) {
   if (s->layout == PBS_LAYOUT_BNHD &&
       static_cast<uint64_t>(s->seq_len) * s->heads_kv * s->head_dim * 2 >= (1ull << 32))
     return PBS_E_SHAPE;
+  // ... and one token's K/V row (all KV heads) is under 2^24 bytes (24-bit multiplies)
+  if (s->layout == PBS_LAYOUT_BNHD &&
+      static_cast<uint64_t>(s->heads_kv) * s->head_dim * 2 >= (1ull << 24))
+    return PBS_E_SHAPE;
   d->B = s->batch;
   d->Hq = s->heads_q;
   d->Hkv = s->heads_kv;

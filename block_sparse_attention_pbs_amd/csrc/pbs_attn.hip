@@ -99,6 +99,18 @@ struct Cfg {
   static constexpr int VCH = SK * (CPR + VPAD);      // 16-byte chunks of a V stage in LDS
   static constexpr int NLDK = (KCH + 63) / 64;       // direct loads (64 lanes) per K stage
   static constexpr int NLDV = (VCH + 63) / 64;       // direct loads (64 lanes) per V stage
+  // Key-stream (gathered) loads: every load starts on a row, so lane l always fetches chunk
+  // l % ROW of row l / ROW of that load's rows; the lanes past the last whole row run into the
+  // next row (the next load writes the same bytes there) and, after the last load, into spare
+  // rows behind the tile.
+  static constexpr int KROW = CPR + KPAD, VROW = CPR + VPAD;    // 16-byte chunks per LDS row
+  static constexpr int RK = 64 / KROW, RV = 64 / VROW;          // whole rows per load
+  static constexpr int NGK = (SK + RK - 1) / RK, NGV = (SK + RV - 1) / RV;   // loads per stage
+  static constexpr int KSLK = NGK * RK + (64 % KROW ? 1 : 0) - SK;   // spare rows behind a tile
+  static constexpr int VSLK = NGV * RV + (64 % VROW ? 1 : 0) - SK;
+  static constexpr int KTILE_A = KTILE + KSLK * (D + 8 * KPAD);      // LDS elements per K stage
+  static constexpr int VTILE_A = VTILE + VSLK * (D + 8 * VPAD);      // LDS elements per V stage
+  static constexpr int GPAD = 64;   // slot-window entries a stage may read past its 32
 };
 
 // LDS row layouts.  K rows: stride = 16 B mod 256 B, so the 16 lanes of a K fragment read
@@ -135,6 +147,15 @@ __device__ __forceinline__ void load_lds16(u32x4 r, const void* lds, uint32_t vo
                :
                : "s"(lds_addr(lds)), "v"(voff), "s"(r), "s"(soff)
                : "memory", "m0");
+}
+// The same load, free to move past the compiler's own LDS reads: for key-stream stages, whose
+// loads only ever target the buffer no wave reads before the next wait + barrier.
+__device__ __forceinline__ void load_lds16_free(u32x4 r, const void* lds, uint32_t voff,
+                                                uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr(lds)), "v"(voff), "s"(r), "s"(soff)
+               : "m0");
 }
 __device__ __forceinline__ void load_lds4(u32x4 r, const void* lds, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
@@ -179,7 +200,7 @@ struct StageIter {
   int kidx;             // stream index of the stage just returned (-1: a contiguous block stage)
   int kwin;             // first stream index held in the LDS window
   int kfill, kscan;     // wave 0 only: entries in the window, next bitmap word to expand
-  uint16_t* ownk;       // LDS window: segment slots of visible keys (kOwnWin + 64 entries)
+  uint16_t* ownk;       // LDS window: segment slots of visible keys (kOwnWin + 128 entries)
   const uint64_t* bits; // LDS bitmaps of the segment's slots, 64 per word: seg_words words of
   int seg_words;        // slots visible to every row, then seg_words words of the other visible ones
 
@@ -205,6 +226,9 @@ struct StageIter {
       kfill += __builtin_popcountll(bal);
       ++kscan;
     }
+    // the stream has ended inside the window: the entries behind it name slot 0, so the rows
+    // of a last partial stage (masked out) and the spare rows read a key of the segment
+    if (kscan >= 2 * seg_words) ownk[kfill + lane] = 0;
   }
   // Make stream indices [k0, k0 + 32) available in the window.  Called by every wave right after
   // a barrier, so no wave still reads the window; the entries from k0 to the end of the window
@@ -328,33 +352,39 @@ struct Rsrc {
 // Start the asynchronous loads of one stage (K, V and, for masked permuted blocks, the original
 // positions of its keys) into LDS.  A spare chunk of a padded row re-reads chunk 0 of its row.
 // A key-stream stage gathers its rows: row r of the stage is segment slot slots[r] (rows past
-// the valid count repeat the last valid slot and get a position after every row, so they are
-// masked out).
+// the valid count read slot 0, the window's padding, and get a position after every row, so
+// they are masked out).
 template <int D, int BS>
 __device__ __forceinline__ void issue_gathered(const AttnArgs& a, const Rsrc& rr, Stage st,
                                                uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
                                                int lane) {
   using C = Cfg<D, BS>;
   const uint32_t base = static_cast<uint32_t>(st.seg0) * static_cast<uint32_t>(a.kv_rs) * 2;
+  const uint32_t rowb = static_cast<uint32_t>(a.kv_rs) * 2;   // < 2^24: checked on the host
+  // Straight-line code (no lane masks, no branches).  Every slot is read from the window before
+  // the first load is issued: the loads are asm with side effects, which the compiler never
+  // moves an LDS read across, so reading the slots in between would wait out one LDS round
+  // trip per load.  A wave with fewer loads than the others repeats the last one (the same
+  // bytes to the same place).
+  constexpr int UK = (C::NGK + C::NW - 1) / C::NW, UV = (C::NGV + C::NW - 1) / C::NW;
+  const int rk = lane / C::KROW, ck = lane - rk * C::KROW;
+  const int rv = lane / C::VROW, cv = lane - rv * C::VROW;
+  uint32_t sk[UK], sv[UV];
 #pragma unroll
-  for (int n = w; n < C::NLDK; n += C::NW) {
-    const int P = n * 64 + lane;
-    const int r = P / (C::CPR + C::KPAD), pc = P - r * (C::CPR + C::KPAD);
-    if (C::KCH % 64 == 0 || P < C::KCH) {
-      const int slot = st.slots[min(r, st.cnt - 1)];
-      load_lds16(rr.k, Kst + n * 512,
-                 static_cast<uint32_t>((slot * a.kv_rs + (pc < C::CPR ? pc : 0) * 8) * 2), base);
-    }
+  for (int u = 0; u < UK; ++u) sk[u] = st.slots[rk + min(w + u * C::NW, C::NGK - 1) * C::RK];
+#pragma unroll
+  for (int u = 0; u < UV; ++u) sv[u] = st.slots[rv + min(w + u * C::NW, C::NGV - 1) * C::RV];
+  const uint32_t cok = static_cast<uint32_t>(ck < C::CPR ? ck : 0) * 16;
+  const uint32_t cov = static_cast<uint32_t>(cv < C::CPR ? cv : 0) * 16;
+#pragma unroll
+  for (int u = 0; u < UK; ++u) {
+    const int j = min(w + u * C::NW, C::NGK - 1);
+    load_lds16_free(rr.k, Kst + j * C::RK * C::KROW * 8, __umul24(sk[u], rowb) + cok, base);
   }
 #pragma unroll
-  for (int n = w; n < C::NLDV; n += C::NW) {
-    const int P = n * 64 + lane;
-    const int r = P / (C::CPR + C::VPAD), pc = P - r * (C::CPR + C::VPAD);
-    if (C::VCH % 64 == 0 || P < C::VCH) {
-      const int slot = st.slots[min(r, st.cnt - 1)];
-      load_lds16(rr.v, Vst + n * 512,
-                 static_cast<uint32_t>((slot * a.kv_rs + (pc < C::CPR ? pc : 0) * 8) * 2), base);
-    }
+  for (int u = 0; u < UV; ++u) {
+    const int j = min(w + u * C::NW, C::NGV - 1);
+    load_lds16_free(rr.v, Vst + j * C::RV * C::VROW * 8, __umul24(sv[u], rowb) + cov, base);
   }
   if (st.masked && w == 0 && lane < C::SK) {
     if (lane < st.cnt)
@@ -540,7 +570,7 @@ struct Pipe {
 // both lands the current stage and frees the other buffer.  Buffers are picked by parity through
 // uniform offsets, so the loop body is one straight copy of the stage code and the accumulators
 // stay in place from one iteration to the next.
-template <int D, int BS, int MODE, bool MASKED, bool MAXONLY>
+template <int D, int BS, int MODE, bool MASKED, bool MAXONLY, bool STREAM>
 __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int count, Pipe& pp,
                                            const Rsrc& rr, uint16_t* smem,
                                            int32_t* Ps0, int32_t* Ps1, int w, int lane, int t,
@@ -554,13 +584,14 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
     const int p = pp.p;
     const bool more = it.next(tid, C::NT, w, lane);
     const Stage nxt = stage_of<BS, C::SK>(it);
-    if (more) {
-      uint16_t* Kn = smem + (p ? a.tile_off[0] : a.tile_off[1]);
-      uint16_t* Vn = smem + (p ? a.tile_off[2] : a.tile_off[3]);
-      if constexpr (MASKED && MODE == 1)   // the own segment: always a key stream
-        issue_gathered<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
-      else
-        issue_stage<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
+    uint16_t* Kn = smem + (p ? a.tile_off[0] : a.tile_off[1]);
+    uint16_t* Vn = smem + (p ? a.tile_off[2] : a.tile_off[3]);
+    if constexpr (STREAM) {
+      // Key stream: no branch around the loads.  Past the end of the stream the iterator still
+      // names the current stage, which is then loaded again into the free buffer.
+      issue_gathered<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
+    } else if (more) {
+      issue_stage<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
     }
     attn_stage<D, BS, MODE, MASKED, MAXONLY>(
         a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
@@ -576,8 +607,8 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
 // the rows' references are first set from the max of the pass's first stage (computed once more,
 // scores only, as soon as that stage has landed).
 template <int D, int BS, int MODE, bool MAXONLY, bool PRIME>
-__device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int n_unm_stages,
-                                          int n_msk_stages, const Rsrc& rr,
+__device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int n_blk_stages,
+                                          int n_unm_stages, int n_msk_stages, const Rsrc& rr,
                                           uint16_t* smem, int32_t* Ps0, int32_t* Ps1, int w,
                                           int lane, int t, const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
@@ -601,10 +632,16 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
                                             pp.cur.key0, lane, t, qf, oacc, first);
       rs.mref = (first.mseen == -INFINITY) ? 0.f : first.mseen;
     }
-    run_stages<D, BS, MODE, false, MAXONLY>(a, it, n_unm_stages, pp, rr, smem,
-                                            Ps0, Ps1, w, lane, t, qf, oacc, rs);
-    run_stages<D, BS, MODE, true, MAXONLY>(a, it, n_msk_stages, pp, rr, smem, Ps0,
-                                           Ps1, w, lane, t, qf, oacc, rs);
+    // n_blk_stages contiguous stages (key blocks), then, in mode 1, the rest of the unmasked
+    // stages and all masked ones are the own segment's key stream
+    constexpr bool KS = (MODE == 1);
+    run_stages<D, BS, MODE, false, MAXONLY, false>(a, it, KS ? n_blk_stages : n_unm_stages, pp,
+                                                   rr, smem, Ps0, Ps1, w, lane, t, qf, oacc, rs);
+    if constexpr (KS)
+      run_stages<D, BS, MODE, false, MAXONLY, true>(a, it, n_unm_stages - n_blk_stages, pp, rr,
+                                                    smem, Ps0, Ps1, w, lane, t, qf, oacc, rs);
+    run_stages<D, BS, MODE, true, MAXONLY, KS>(a, it, n_msk_stages, pp, rr, smem, Ps0, Ps1, w,
+                                               lane, t, qf, oacc, rs);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // every wave is done with both buffers before another pass refills them
@@ -614,12 +651,12 @@ template <int D, int BS, int MODE>
 __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(AttnArgs a) {
   using C = Cfg<D, BS>;
   // One LDS array laid out [K stage 0][K stage 1][V stage 0][V stage 1].
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::KTILE + 2 * C::VTILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::KTILE_A + 2 * C::VTILE_A];
   __shared__ __attribute__((aligned(16))) int32_t Ps0[C::SK];
   __shared__ __attribute__((aligned(16))) int32_t Ps1[C::SK];
   __shared__ uint16_t offw[kOffWindow];
   __shared__ uint16_t ownl[kOwnMax];
-  __shared__ uint16_t ownk[MODE == 1 ? kOwnWin + 64 : 1];
+  __shared__ uint16_t ownk[MODE == 1 ? kOwnWin + 128 : 1];
   __shared__ uint64_t ownbits[MODE == 1 ? 2 * kSegWords : 1];
   __shared__ int own_count;
   __shared__ int qmax_w[C::NW];
@@ -797,12 +834,14 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
   }
   // Unmasked stages come first in every visit list, masked ones last.
   int n_unm, n_msk;
+  int n_blk = 0;   // mode 1: the off-diagonal stages before the key stream
   if (MODE == 0) {
     n_unm = i * C::HALVES;
     n_msk = C::HALVES;
   } else if (MODE == 1) {
     // the own segment's key stream: whole stages of keys every row sees run unmasked
-    n_unm = it.n_off * C::HALVES + it.n_ks_full / 32;
+    n_blk = it.n_off * C::HALVES;
+    n_unm = n_blk + it.n_ks_full / 32;
     n_msk = (it.n_ks + 31) / 32 - it.n_ks_full / 32;
   } else if (LM == 1) {
     n_unm = it.n_off * C::HALVES;
@@ -824,19 +863,19 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
 #pragma unroll
   for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
   RowState rs{-INFINITY, 0.f, -INFINITY};
-  attn_pass<D, BS, MODE, false, true>(a, it, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
+  attn_pass<D, BS, MODE, false, true>(a, it, n_blk, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
                                 oacc, rs);
   // A row whose sum left [2^-60, 2^64] (scores far above or below its reference) is recomputed:
   // first its exact maximum, then the pass against that maximum.
   const float l0 = pair_sum(rs.lsum);
   if (__syncthreads_or(!(l0 >= 0x1p-60f && l0 <= 0x1p64f) ? 1 : 0)) {
-    attn_pass<D, BS, MODE, true, false>(a, it, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
+    attn_pass<D, BS, MODE, true, false>(a, it, n_blk, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
                                  oacc, rs);
 #pragma unroll
     for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
     rs.mref = rs.mseen;
     rs.lsum = 0.f;
-    attn_pass<D, BS, MODE, false, false>(a, it, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
+    attn_pass<D, BS, MODE, false, false>(a, it, n_blk, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
                                   oacc, rs);
   }
 
@@ -858,7 +897,12 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
 }
 
 template <int D, int BS>
-hipError_t launch_attn_t(const Dims& d, const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attn_t(const Dims& d, AttnArgs a, hipStream_t stream) {
+  using C = Cfg<D, BS>;
+  a.tile_off[0] = 0;
+  a.tile_off[1] = C::KTILE_A;
+  a.tile_off[2] = 2 * C::KTILE_A;
+  a.tile_off[3] = 2 * C::KTILE_A + C::VTILE_A;
   const int total = d.B * d.Hq * d.nb;
   const dim3 block(Cfg<D, BS>::NT);
   if (a.mode == 1) return launch(attn_fwd_kernel<D, BS, 1>, dim3(total), block, 0, stream, a);
@@ -896,11 +940,6 @@ hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, cons
   a.qm = q_rows(d);
   a.km = kv_rows(d);
   a.kv_rs = a.km.stride();
-  const int ktile = kStageKeys * (d.d + 8), vtile = kStageKeys * (d.d + 32);
-  a.tile_off[0] = 0;
-  a.tile_off[1] = ktile;
-  a.tile_off[2] = 2 * ktile;
-  a.tile_off[3] = 2 * ktile + vtile;
   if (d.d == 128 && d.Bs == 128) return launch_attn_t<128, 128>(d, a, stream);
   if (d.d == 128 && d.Bs == 64) return launch_attn_t<128, 64>(d, a, stream);
   if (d.d == 64 && d.Bs == 128) return launch_attn_t<64, 128>(d, a, stream);

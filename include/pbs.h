@@ -23,8 +23,8 @@
  *  - Query head g reads KV head g / (Hq / Hkv) (grouped-query attention).
  *  - Block size Bs (the pages' B) and segment size S (the pages' S) come in pbs_shape.
  *    Required: Hq % Hkv == 0, d in {64, 128}, Bs in {64, 128}, S % Bs == 0, N % S == 0,
- *    S <= 16384, N / Bs <= 8192, and for PBS_LAYOUT_BNHD N * Hkv * d * 2 < 2^32 bytes
- *    (PBS_E_SHAPE otherwise).  batch == 0 or seq_len == 0 is an
+ *    S <= 16384, N / Bs <= 8192, and for PBS_LAYOUT_BNHD N * Hkv * d * 2 < 2^32 bytes and
+ *    Hkv * d * 2 < 2^24 bytes (PBS_E_SHAPE otherwise).  batch == 0 or seq_len == 0 is an
  *    empty problem: once the shape and the scalar arguments are valid the call returns PBS_OK
  *    without launching anything or inspecting the pointers.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).  The

@@ -39,7 +39,9 @@ def test_shape_rules():
            P.make_shape(1, 32, 8, 1024, 128, 128, 256, 2),      # unknown layout
            P.make_shape(1, 32, 8, 1024, 128, 128, 256, -1),     # unknown layout
            # token-major K/V head wider than 32-bit byte offsets: N * Hkv * d * 2 = 2^32
-           P.make_shape(1, 64, 16, 8192 * 128, 128, 128, 8192, P.PBS_LAYOUT_BNHD)]
+           P.make_shape(1, 64, 16, 8192 * 128, 128, 128, 8192, P.PBS_LAYOUT_BNHD),
+           # one token's K/V row (all KV heads) of 2^24 bytes: Hkv * d * 2 = 65536 * 128 * 2
+           P.make_shape(1, 65536, 65536, 128, 128, 128, 128, P.PBS_LAYOUT_BNHD)]
     for s in bad:
         assert P.pbs_max_offdiag(s) == -1
         assert P.pbs_workspace_bytes(s) == 0

@@ -174,12 +174,7 @@ def density_main(args):
         i_idx = np.arange(nb)
         candidates = B * Hq * int(((i_idx // bps) * bps).sum())
         dense_blocks = B * Hq * nb * (nb + 1) // 2
-        minpos = bf.blk_minpos.cpu().numpy()
-        last_row = (i_idx + 1) * Bs - 1
-        own_perm = 0
-        for i in range(nb):
-            s0 = (i // bps) * bps
-            own_perm += int((minpos[:, :, s0:s0 + bps] <= last_row[i]).sum()) * G
+        own_perm = own_segment_blocks(bf.perm.cpu().numpy(), Bs, S, G)   # the key stream's work
         own_nat = B * Hq * int((i_idx - (i_idx // bps) * bps + 1).sum())
         res = {}
         for order in ("permuted", "natural"):

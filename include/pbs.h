@@ -191,14 +191,17 @@ int pbs_block_select(const pbs_shape* shape, const uint16_t* q, const uint16_t* 
  *
  * PBS mode (counts and idx given): query row t of block i in segment s attends to
  *   - every key of the kept blocks idx[b,g,i,0..counts) (whole blocks, no mask), and
- *   - every key of segment s with original position <= t: the own segment's blocks are
- *     walked in the order of `k`, and slot p is visible to row t iff perm[b,h,p] <= t
+ *   - every key of segment s with original position <= t: slot p is visible to row t iff
+ *     perm[b,h,p] <= t.  The kernel reads only the slots visible to some row of the block
+ *     (perm <= the block's last row), in slot order, those visible to every row unmasked
  *     (perm NULL: identity order, plain block-sparse attention).
  * Dense mode (perm, counts, idx all NULL): plain causal attention over keys 0..t.
  *   q      [B,Hq,N,d] bf16 (natural order)
  *   k, v   [B,Hkv,N,d] bf16: k_perm/v_perm from pbs_permute in PBS mode, natural K/V in
  *          dense mode or with perm == NULL
- *   perm   [B,Hkv,N] int32 or NULL;  blk_minpos [B,Hkv,N/Bs] int32 or NULL (skip hint)
+ *   perm   [B,Hkv,N] int32 or NULL
+ *   blk_minpos [B,Hkv,N/Bs] int32 or NULL: accepted for the other attention entry points'
+ *          sake and not read here (the own segment's visibility is taken from perm itself)
  *   counts [B,Hq,N/Bs], idx [B,Hq,N/Bs,pbs_max_offdiag] int32 from pbs_block_select, or NULL
  *   o      [B,Hq,N,d] bf16, written, original token order
  *   lse    [B,Hq,N] float32 natural-log softmax normaliser of every row, or NULL

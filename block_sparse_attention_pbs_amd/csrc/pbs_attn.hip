@@ -313,6 +313,29 @@ struct StageIter {
     half = halves - 1;   // one stage per stream step
     return true;
   }
+  // next() where the caller knows the following stage is a key-block stage (KIND 1) or a
+  // key-stream stage (KIND 2): the same result with the other case's code left out.
+  template <int KIND>
+  __device__ __forceinline__ bool next_of(int tid, int nt, int w, int lane) {
+    if constexpr (KIND == 1) {
+      if (half >= 0 && half + 1 < halves) {
+        ++half;
+        return true;
+      }
+      half = 0;
+      kidx = -1;
+      return next_block(tid, nt);
+    } else if constexpr (KIND == 2) {
+      if (ks * 32 >= n_ks) return false;
+      kidx = __builtin_amdgcn_readfirstlane(ks * 32);
+      ks = __builtin_amdgcn_readfirstlane(ks + 1);
+      if (kidx + 32 > kwin + kOwnWin) refill(kidx, w, lane);
+      masked = kidx + 32 > n_ks_full;
+      return true;
+    } else {
+      return next(tid, nt, w, lane);
+    }
+  }
 };
 
 struct Stage {
@@ -395,12 +418,12 @@ __device__ __forceinline__ void issue_gathered(const AttnArgs& a, const Rsrc& rr
   }
 }
 
-template <int D, int BS>
+template <int D, int BS, bool MAYBE_STREAM = true>
 __device__ __forceinline__ void issue_stage(const AttnArgs& a, const Rsrc& rr, Stage st,
                                             uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
                                             int lane) {
   using C = Cfg<D, BS>;
-  if (st.slots != nullptr) {
+  if (MAYBE_STREAM && st.slots != nullptr) {
     issue_gathered<D, BS>(a, rr, st, Kst, Vst, Pst, w, lane);
     return;
   }
@@ -570,7 +593,8 @@ struct Pipe {
 // both lands the current stage and frees the other buffer.  Buffers are picked by parity through
 // uniform offsets, so the loop body is one straight copy of the stage code and the accumulators
 // stay in place from one iteration to the next.
-template <int D, int BS, int MODE, bool MASKED, bool MAXONLY, bool STREAM>
+// KIND: 0 any stage may follow, 1 only key-block stages follow, 2 only key-stream stages.
+template <int D, int BS, int MODE, bool MASKED, bool MAXONLY, int KIND>
 __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int count, Pipe& pp,
                                            const Rsrc& rr, uint16_t* smem,
                                            int32_t* Ps0, int32_t* Ps1, int w, int lane, int t,
@@ -582,16 +606,16 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // the current stage landed; the other buffer is no longer read
     const int p = pp.p;
-    const bool more = it.next(tid, C::NT, w, lane);
+    const bool more = it.template next_of<KIND>(tid, C::NT, w, lane);
     const Stage nxt = stage_of<BS, C::SK>(it);
     uint16_t* Kn = smem + (p ? a.tile_off[0] : a.tile_off[1]);
     uint16_t* Vn = smem + (p ? a.tile_off[2] : a.tile_off[3]);
-    if constexpr (STREAM) {
+    if constexpr (KIND == 2) {
       // Key stream: no branch around the loads.  Past the end of the stream the iterator still
       // names the current stage, which is then loaded again into the free buffer.
       issue_gathered<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
     } else if (more) {
-      issue_stage<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
+      issue_stage<D, BS, KIND == 0>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
     }
     attn_stage<D, BS, MODE, MASKED, MAXONLY>(
         a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
@@ -634,14 +658,24 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
     }
     // n_blk_stages contiguous stages (key blocks), then, in mode 1, the rest of the unmasked
     // stages and all masked ones are the own segment's key stream
-    constexpr bool KS = (MODE == 1);
-    run_stages<D, BS, MODE, false, MAXONLY, false>(a, it, KS ? n_blk_stages : n_unm_stages, pp,
-                                                   rr, smem, Ps0, Ps1, w, lane, t, qf, oacc, rs);
-    if constexpr (KS)
-      run_stages<D, BS, MODE, false, MAXONLY, true>(a, it, n_unm_stages - n_blk_stages, pp, rr,
-                                                    smem, Ps0, Ps1, w, lane, t, qf, oacc, rs);
-    run_stages<D, BS, MODE, true, MAXONLY, KS>(a, it, n_msk_stages, pp, rr, smem, Ps0, Ps1, w,
-                                               lane, t, qf, oacc, rs);
+    if constexpr (MODE == 1) {
+      // key blocks (the last one hands over to the stream), then the stream's stages
+      if (n_blk_stages > 0) {
+        run_stages<D, BS, MODE, false, MAXONLY, 1>(a, it, n_blk_stages - 1, pp, rr, smem, Ps0,
+                                                   Ps1, w, lane, t, qf, oacc, rs);
+        run_stages<D, BS, MODE, false, MAXONLY, 0>(a, it, 1, pp, rr, smem, Ps0, Ps1, w, lane, t,
+                                                   qf, oacc, rs);
+      }
+      run_stages<D, BS, MODE, false, MAXONLY, 2>(a, it, n_unm_stages - n_blk_stages, pp, rr,
+                                                 smem, Ps0, Ps1, w, lane, t, qf, oacc, rs);
+      run_stages<D, BS, MODE, true, MAXONLY, 2>(a, it, n_msk_stages, pp, rr, smem, Ps0, Ps1, w,
+                                                lane, t, qf, oacc, rs);
+    } else {
+      run_stages<D, BS, MODE, false, MAXONLY, 1>(a, it, n_unm_stages, pp, rr, smem, Ps0, Ps1, w,
+                                                 lane, t, qf, oacc, rs);
+      run_stages<D, BS, MODE, true, MAXONLY, 1>(a, it, n_msk_stages, pp, rr, smem, Ps0, Ps1, w,
+                                                lane, t, qf, oacc, rs);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // every wave is done with both buffers before another pass refills them

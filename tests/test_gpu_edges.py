@@ -280,3 +280,36 @@ def test_long_lists_refill_the_window(dominant):
     gl = np.stack([lg[i * Bs:(i + 1) * Bs] for i in blocks])
     check_attn(got, od, f"long lists dominant={dominant}")
     assert np.abs(gl - ol).max() < 1e-3
+
+
+def test_key_stream_refill_and_fallback():
+    """The own segment's key stream longer than the kernel's slot window (2048 keys) together
+    with the fallback passes: N=16384, Bs=128, S=8192, keep 1 (the result equals dense causal
+    attention).  A dominant key at position 11192 of the second segment sorts to its first slot,
+    so for the rows after it the stream meets a logit far above the first stage's reference, the
+    row sums overflow, and the fallback passes must walk the stream again from its first window
+    (query blocks late in the segment see up to 8192 keys, four windows)."""
+    say("key stream refill + fallback, d=128 Bs=128 S=8192 N=16384")
+    N, d, Bs, S = 16384, 128, 128, 8192
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    v = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q += np.float32(3.0) * u.astype(np.float32)
+    k[0, 0, 11192] = (300.0 * u).astype(np.float32)
+    q, k, v = (pbs_synth.f32_to_bf16_bits(x) for x in (q, k, v))
+    scale = oracle.default_scale(d)
+    blocks = [127, 126, 110, 88, 87, 70, 64, 63, 0]
+    od, ol = oracle.dense_causal(q, k, v, block=Bs, scale=scale, qblocks=[(0, 0, i) for i in blocks])
+    bufs = P.prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), block=Bs, segment=S, keep=1.0,
+                     scale=scale)
+    torch.cuda.synchronize()
+    assert int(bufs.perm.cpu().numpy()[0, 0, S]) == 11192   # the dominant key leads its segment
+    og = bufs.o.float().cpu().numpy()[0, 0]
+    lg = bufs.lse.cpu().numpy()[0, 0]
+    got = np.stack([og[i * Bs:(i + 1) * Bs] for i in blocks])
+    gl = np.stack([lg[i * Bs:(i + 1) * Bs] for i in blocks])
+    check_attn(got, od, "key stream refill + fallback")
+    assert np.abs(gl - ol).max() < 1e-3

@@ -4,16 +4,17 @@
 // gist.science summary, Methodik 3 "Handling von Queries" and Methodik 4 "Kernel"): every query
 // row t of query block i, segment s, attends to the keys of the kept earlier-segment blocks of
 // its row (whole blocks) and to every key of its own segment whose ORIGINAL position is <= t.
-// The own segment is walked in the order of the given key tensor (the permuted copies), the
-// causal test going through the stored original positions.  Queries are never permuted, so
-// the output is written in original token order.
+// The own segment is read from the given key tensor (the permuted copies), the causal test
+// going through the stored original positions; only its slots whose original position is at or
+// before the query block's last row are loaded (any other key adds exactly zero to every row).
+// Queries are never permuted, so the output is written in original token order.
 //
 // Design (CDNA4, wave64):
 //  * one workgroup of Bs/32 waves per (query block, query head); wave w owns 32 query rows and
 //    sees every key of every visited block, so no cross-wave reduction is needed;
 //  * keys stream through LDS in stages of 32 keys, double-buffered and filled by asynchronous
 //    direct buffer->LDS loads (buffer_load_dwordx4 ... lds, bounds-checked) one stage ahead of
-//    the compute.  A workgroup needs ~42 KiB of LDS and at most 168 VGPRs per lane, so three
+//    the compute.  A workgroup needs at most ~52 KiB of LDS and 168 VGPRs per lane, so three
 //    workgroups share a CU (three waves per SIMD): while one waits or runs its softmax, the
 //    others keep the matrix cores busy;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 (A = K rows from
@@ -32,6 +33,10 @@
 //    A later max more than 2^64 above the reference only sets a flag, and the workgroup then
 //    recomputes with the exact row max (never seen on realistic inputs, but it keeps every value
 //    in range on any input);
+//  * the own segment of the permuted-key path is a stream of its visible slots: per workgroup,
+//    two LDS bitmaps (slots every row sees, slots some row sees) from one coalesced read of the
+//    segment's positions, expanded into a window of slot numbers; each stream stage gathers 32
+//    rows, the fully visible ones unmasked;
 //  * work order: heaviest query blocks first, and consecutive workgroups of one XCD (the
 //    hardware deals workgroups round-robin over the 8 XCDs) walk one KV head, so the K/V tiles a
 //    head's query blocks share stay in that XCD's L2.
@@ -78,7 +83,7 @@ struct AttnArgs {
 constexpr int kStageKeys = PBS_ATTN_STAGE_KEYS;  // keys per LDS stage
 constexpr int kOffWindow = 1792; // off-diagonal list entries held in LDS at a time
 constexpr int kOwnMax = 256;     // own-segment blocks (S / Bs <= 16384 / 64)
-constexpr int kOwnWin = 2048;    // visible own-segment keys held in LDS at a time (modes 1, 4)
+constexpr int kOwnWin = 2048;    // visible own-segment keys held in LDS at a time (mode 1)
 constexpr int kSegWords = 16384 / 64;   // 64-slot words of the largest segment's visibility bitmap
 
 template <int D, int BS>
@@ -189,7 +194,7 @@ struct StageIter {
   uint16_t* offw;       // LDS window of the off-diagonal list
   const uint16_t* ownl; // LDS list of the visible own-segment blocks
   int ent;              // the next entry's LDS word, read ahead (per lane, all lanes equal)
-  // Modes 1 and 4: the own segment is walked as a stream of its VISIBLE keys -- the slots whose
+  // Mode 1: the own segment is walked as a stream of its VISIBLE keys -- the slots whose
   // original position is at or before the query block's last row, in permuted (slot) order -- 32
   // per stage.  A key after every row of the query block adds exactly zero to every row, so it
   // is never loaded; the rest still go through the per-key causal test.
@@ -342,7 +347,7 @@ struct Stage {
   int key0;     // first key of the stage in the head's key order (block * Bs + stage * 32)
   bool masked;
   bool orig;    // read from the original keys and values (mode 3 own segment)
-  // Own-segment key-stream stage (modes 1, 4): the segment slots of its keys and how many are
+  // Own-segment key-stream stage (mode 1): the segment slots of its keys and how many are
   // valid (1..32); slots == nullptr for a contiguous stage.  seg0: first key of the segment.
   const uint16_t* slots;
   int cnt, seg0;

@@ -843,7 +843,14 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
       __syncthreads();
       it.n_ks = own_count;
       it.n_ks_full = own_full;
-      if (w == 0) it.scan_fill(lane);
+      if (w == 0) {
+        // The window's tail starts as slot 0: a stage near the window's end reads up to four
+        // entries past the expanded ones into its spare rows, so those entries must always
+        // name a slot of the segment (LDS holds whatever an earlier workgroup left there).
+        ownk[kOwnWin + lane] = 0;
+        ownk[kOwnWin + 64 + lane] = 0;
+        it.scan_fill(lane);
+      }
       __syncthreads();
     } else {
       // Own-segment blocks, compacted by wave 0.  Permuted queries (mode 4): a permuted block is

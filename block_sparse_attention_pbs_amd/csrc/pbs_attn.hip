@@ -221,7 +221,40 @@ struct StageIter {
   }
   // Wave 0: expand bitmap words from kscan on into the slot window until it holds at least
   // kOwnWin entries or the bitmap ends (LDS only: the bitmap is built once per workgroup).
+  // 64 words at a time: lane l takes word kscan + l, a prefix sum of the words' bit counts gives
+  // each lane its place in the window, and the lanes whose words start before the window is
+  // full write their slots (word order, then bit order, as a word-by-word walk would).
   __device__ __forceinline__ void scan_fill(int lane) {
+    const int nwords = 2 * seg_words;
+    while (kfill < kOwnWin && kscan < nwords) {
+      const int wi = kscan + lane;
+      const uint64_t bal = wi < nwords ? bits[wi] : 0ull;
+      const int cnt = __builtin_popcountll(bal);
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const int excl = incl - cnt;
+      const bool take = wi < nwords && kfill + excl < kOwnWin;   // lanes 0 .. ntake-1
+      const int ntake = __builtin_popcountll(__builtin_amdgcn_ballot_w64(take));
+      if (take) {
+        const int word = wi < seg_words ? wi : wi - seg_words;
+        int pos = kfill + excl;
+        for (uint64_t m = bal; m != 0ull; m &= m - 1ull)
+          ownk[pos++] = static_cast<uint16_t>(word * 64 + __builtin_ctzll(m));
+      }
+      kfill += __shfl(incl, ntake - 1);
+      kscan += ntake;
+    }
+    // the stream has ended inside the window: the entries behind it name slot 0, so the rows
+    // of a last partial stage (masked out) and the spare rows read a key of the segment
+    if (kscan >= nwords) ownk[kfill + lane] = 0;
+  }
+  // The same expansion one word at a time: less code, for the refills inside the stage loop
+  // (there the words are dense, a window holds about 32 of them).
+  __device__ __forceinline__ void scan_fill_serial(int lane) {
     while (kfill < kOwnWin && kscan < 2 * seg_words) {
       const uint64_t bal = bits[kscan];
       const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
@@ -231,8 +264,6 @@ struct StageIter {
       kfill += __builtin_popcountll(bal);
       ++kscan;
     }
-    // the stream has ended inside the window: the entries behind it name slot 0, so the rows
-    // of a last partial stage (masked out) and the spare rows read a key of the segment
     if (kscan >= 2 * seg_words) ownk[kfill + lane] = 0;
   }
   // Make stream indices [k0, k0 + 32) available in the window.  Called by every wave right after
@@ -247,7 +278,7 @@ struct StageIter {
       if (lane < keep) ownk[lane] = e0;
       if (lane + 64 < keep) ownk[64 + lane] = e1;
       kfill = max(keep, 0);
-      scan_fill(lane);
+      scan_fill_serial(lane);
     }
     kwin = k0;
     __syncthreads();

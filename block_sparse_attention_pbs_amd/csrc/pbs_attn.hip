@@ -115,7 +115,6 @@ struct Cfg {
   static constexpr int VSLK = NGV * RV + (64 % VROW ? 1 : 0) - SK;
   static constexpr int KTILE_A = KTILE + KSLK * (D + 8 * KPAD);      // LDS elements per K stage
   static constexpr int VTILE_A = VTILE + VSLK * (D + 8 * VPAD);      // LDS elements per V stage
-  static constexpr int GPAD = 64;   // slot-window entries a stage may read past its 32
 };
 
 // LDS row layouts.  K rows: stride = 16 B mod 256 B, so the 16 lanes of a K fragment read
@@ -730,7 +729,6 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
   __shared__ uint64_t ownbits[MODE == 1 ? 2 * kSegWords : 1];
   __shared__ int own_count;
   __shared__ int qmax_w[C::NW];
-  __shared__ int qmin_w[C::NW];
   __shared__ int own_full;
   // Visit-list and key-mask rules: mode 4 (permuted queries) walks the permuted keys like mode 1.
   constexpr int LM = (MODE == 4) ? 1 : MODE;
@@ -821,30 +819,20 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
     int last_row = i * BS + BS - 1;   // the latest original position among the block's rows
     int first_row = i * BS;           // the earliest
     if constexpr (MODE == 4) {
-      int mx = t, mn = t;
+      int mx = t;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        mx = max(mx, __shfl_xor(mx, o));
-        mn = min(mn, __shfl_xor(mn, o));
-      }
-      if (lane == 0) {
-        qmax_w[w] = mx;
-        qmin_w[w] = mn;
-      }
+      for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+      if (lane == 0) qmax_w[w] = mx;
       __syncthreads();
       last_row = qmax_w[0];
-      first_row = qmin_w[0];
 #pragma unroll
-      for (int ww = 1; ww < C::NW; ++ww) {
-        last_row = max(last_row, qmax_w[ww]);
-        first_row = min(first_row, qmin_w[ww]);
-      }
+      for (int ww = 1; ww < C::NW; ++ww) last_row = max(last_row, qmax_w[ww]);
     }
     if constexpr (MODE == 1) {
-      // The own segment as a key stream.  Every wave reads a quarter of the segment's positions
-      // (four independent coalesced loads per step) and stores one 64-slot visibility word per
-      // ballot (visible: position at or before the block's last row); then wave 0 expands the
-      // first words into the LDS window of slots.
+      // The own segment as a key stream.  Every wave reads its share of the segment's positions
+      // (four independent coalesced loads per step) and stores, per 64 slots, one word of each
+      // bitmap (ballots: position before the block's first row; position from its first to its
+      // last row); then wave 0 expands the first words into the LDS window of slots.
       const int32_t* pseg = a.perm + kv_head + static_cast<size_t>(it.seg_first) * BS;
       if (tid == 0) {
         own_count = 0;

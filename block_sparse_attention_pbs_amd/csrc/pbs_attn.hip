@@ -542,11 +542,12 @@ struct RowState {
 // row's reference is set to its max over the pass's first stage (0 for a row that sees no key of
 // it; the MAXONLY form of this function computes that max), and a row sum outside [2^-60, 2^64]
 // after the pass sends the workgroup through the exact-max fallback.
-template <int D, int BS, int MODE, bool MASKED, bool MAXONLY>
+template <int D, int BS, int MODE, bool MASKED, bool MAXONLY, class Pre>
 __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vs,
                                            const int32_t* Ps, int key0, int lane, int t,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NKS],
-                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
+                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs,
+                                           Pre&& pre) {
   using C = Cfg<D, BS>;
   const int hl = lane >> 5;
   const int c32 = lane & 31;
@@ -557,6 +558,7 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
       k0[kt] = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kt * 32 + c32, hl * 8)]);
+    pre();   // the next stage's loads, if the caller issues them here
     if constexpr (MASKED) {
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
@@ -645,16 +647,18 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
     const Stage nxt = stage_of<BS, C::SK>(it);
     uint16_t* Kn = smem + (p ? a.tile_off[0] : a.tile_off[1]);
     uint16_t* Vn = smem + (p ? a.tile_off[2] : a.tile_off[3]);
-    if constexpr (KIND == 2) {
-      // Key stream: no branch around the loads.  Past the end of the stream the iterator still
-      // names the current stage, which is then loaded again into the free buffer.
-      issue_gathered<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
-    } else if (more) {
-      issue_stage<D, BS, KIND == 0>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
+    if constexpr (KIND != 2) {
+      if (more) issue_stage<D, BS, KIND == 0>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
     }
+    // Key stream: the loads go out after the stage's first K fragment reads, so the LDS reads of
+    // their slots overlap those; no branch around them.  Past the end of the stream the
+    // iterator still names the current stage, which is then loaded again into the free buffer.
+    auto stream_issue = [&]() {
+      if constexpr (KIND == 2) issue_gathered<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
+    };
     attn_stage<D, BS, MODE, MASKED, MAXONLY>(
         a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
-        p ? Ps1 : Ps0, pp.cur.key0, lane, t, qf, oacc, rs);
+        p ? Ps1 : Ps0, pp.cur.key0, lane, t, qf, oacc, rs, stream_issue);
     pp.cur = nxt;
     pp.p = p ^ 1;
   }
@@ -685,10 +689,10 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
       RowState first{0.f, 0.f, -INFINITY};
       if (n_unm_stages > 0)
         attn_stage<D, BS, MODE, false, true>(a, smem + a.tile_off[0], smem + a.tile_off[2], Ps0,
-                                             pp.cur.key0, lane, t, qf, oacc, first);
+                                             pp.cur.key0, lane, t, qf, oacc, first, [] {});
       else
         attn_stage<D, BS, MODE, true, true>(a, smem + a.tile_off[0], smem + a.tile_off[2], Ps0,
-                                            pp.cur.key0, lane, t, qf, oacc, first);
+                                            pp.cur.key0, lane, t, qf, oacc, first, [] {});
       rs.mref = (first.mseen == -INFINITY) ? 0.f : first.mseen;
     }
     // n_blk_stages contiguous stages (key blocks), then, in mode 1, the rest of the unmasked

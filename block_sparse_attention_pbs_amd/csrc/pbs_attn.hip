@@ -427,11 +427,17 @@ __device__ __forceinline__ void issue_gathered(const AttnArgs& a, const Rsrc& rr
   constexpr int UK = (C::NGK + C::NW - 1) / C::NW, UV = (C::NGV + C::NW - 1) / C::NW;
   const int rk = lane / C::KROW, ck = lane - rk * C::KROW;
   const int rv = lane / C::VROW, cv = lane - rv * C::VROW;
+  // Load u of wave w is load w + u*NW of the stage; only the last u can pass the last load
+  // (UK, UV round up), so the others are a fixed offset from one per-stage address.
   uint32_t sk[UK], sv[UV];
+  const uint16_t* slk = st.slots + rk + w * C::RK;
+  const uint16_t* slv = st.slots + rv + w * C::RV;
 #pragma unroll
-  for (int u = 0; u < UK; ++u) sk[u] = st.slots[rk + min(w + u * C::NW, C::NGK - 1) * C::RK];
+  for (int u = 0; u + 1 < UK; ++u) sk[u] = slk[u * C::NW * C::RK];
+  sk[UK - 1] = st.slots[rk + min(w + (UK - 1) * C::NW, C::NGK - 1) * C::RK];
 #pragma unroll
-  for (int u = 0; u < UV; ++u) sv[u] = st.slots[rv + min(w + u * C::NW, C::NGV - 1) * C::RV];
+  for (int u = 0; u + 1 < UV; ++u) sv[u] = slv[u * C::NW * C::RV];
+  sv[UV - 1] = st.slots[rv + min(w + (UV - 1) * C::NW, C::NGV - 1) * C::RV];
   const uint32_t cok = static_cast<uint32_t>(ck < C::CPR ? ck : 0) * 16;
   const uint32_t cov = static_cast<uint32_t>(cv < C::CPR ? cv : 0) * 16;
 #pragma unroll
@@ -834,7 +840,7 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
     }
     if constexpr (MODE == 1) {
       // The own segment as a key stream.  Every wave reads its share of the segment's positions
-      // (four independent coalesced loads per step) and stores, per 64 slots, one word of each
+      // (eight independent coalesced loads per step) and stores, per 64 slots, one word of each
       // bitmap (ballots: position before the block's first row; position from its first to its
       // last row); then wave 0 expands the first words into the LDS window of slots.
       const int32_t* pseg = a.perm + kv_head + static_cast<size_t>(it.seg_first) * BS;
@@ -844,9 +850,9 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
       }
       __syncthreads();
       int n = 0, nf = 0;
-      for (int c = w * 4; c < it.seg_words; c += C::NW * 4) {
+      for (int c = w * 8; c < it.seg_words; c += C::NW * 8) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 8; ++q) {
           const int word = c + q;
           const int pos = word < it.seg_words ? pseg[word * 64 + lane] : 0x7fffffff;
           const uint64_t full = __builtin_amdgcn_ballot_w64(pos < first_row);

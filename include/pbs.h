@@ -126,7 +126,8 @@ int pbs_score(const pbs_shape* shape, const uint16_t* q, const uint16_t* k, floa
  *   k_pool[b,h,j,:]  float32 mean of k_perm rows of block j (optional, may be NULL;
  *                    pbs_block_select can reuse it)
  *   blk_minpos[b,h,j] smallest original position held by block j (optional, may be NULL;
- *                    lets pbs_attn_fwd skip own-segment blocks no query of a block can see)
+ *                    lets pbs_attn_fwd_permuted_queries skip own-segment blocks no query of
+ *                    a block can see)
  *   scores [B,Hkv,N] float32, k/v [B,Hkv,N,d] bf16 -> perm [B,Hkv,N], k_perm/v_perm
  *   [B,Hkv,N,d], k_pool [B,Hkv,N/Bs,d], blk_minpos [B,Hkv,N/Bs].
  */

@@ -677,7 +677,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(eff_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "work_per_launch": f"{computed} computed blocks x {flop_per_block / 1e6:.3f} MFLOP",
+            "work_per_launch": (f"{computed} computed blocks x {flop_per_block / 1e6:.3f} MFLOP "
+                                "(selected off-diagonal blocks + visible own-segment keys in "
+                                f"32-key stages / {Bs})"),
         },
         "hip_graph_replay": graph,
         "library_gemm_reference": gemm,

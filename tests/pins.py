@@ -509,6 +509,113 @@ def pin_segment0_rows_are_dense(O):
     assert np.abs(out["o"][:, :, 8:] - od[:, :, 8:]).max() > 1e-3
 
 
+def pin_default_scale(O):
+    """The default softmax temperature is 1/sqrt(d) rounded to float32: exactly 1/8 at d = 64 and
+    2^-3.5 rounded to float32 at d = 128."""
+    assert O.default_scale(64) == 0.125
+    assert O.default_scale(128) == float(np.float32(2.0 ** -3.5))
+
+
+# ----------------------------------------------------------------------------- whole pipeline
+
+def pin_prefill_selects_on_permuted_keys(O):
+    """Hand-worked pipeline where the permutation decides which block is kept ([GS Methodik 4,
+    Block-Auswahl]: block importance by mean pooling on the PERMUTED keys; [SS Fig. 2]: coverage
+    is the mass of the selected blocks).
+
+    N=16, Bs=2, S=8, one head, d=2, every query (1, 0); keys 3 and 5 are (2, 0), all others 0;
+    scale = ln(5)/2, so a salient key's logit is ln 5 and every other logit is 0.
+      scores, segment 0 (rows 14 and 15 see all of it): 5/16 for keys 3 and 5, 1/16 otherwise,
+        so perm[0:8] = [3, 5, 0, 1, 2, 4, 6, 7];
+      segment 1: all keys 0, row 14 sees 8..14 and row 15 sees 8..15, so keys 8..14 tie and key
+        15 scores lower: perm[8:16] = [8 .. 15];
+      pooled permuted keys: block 0 = mean(k3, k5) = (2, 0), blocks 1..3 = 0;
+      P of query blocks 4..7 over candidate blocks 0..3: softmax(ln 5, 0, 0, 0) = [5/8, 1/8, 1/8, 1/8];
+      keep 0.25 -> max(1, floor(1.0)) = 1 block -> [0];  keep 0.5 -> 2 blocks -> [0, 1];
+      coverage 0.6 -> 5/8 already reaches it -> [0];  coverage 0.7 -> 5/8 + 1/8 -> [0, 1].
+    (Pooling the unpermuted keys instead gives natural blocks {2,3} and {4,5} the salient mass
+    and ranks block 1 first; reading a coverage threshold as a keep ratio keeps 2 blocks at
+    0.6.)  The outputs of segment-1 rows then see keys {3, 5} (or {3, 5, 0, 1}) plus their own
+    segment up to t; checked against brute force with that visibility."""
+    N, Bs, S, d = 16, 2, 8, 2
+    scale = math.log(5.0) / 2.0
+    qf = np.zeros((1, 1, N, d), np.float32)
+    qf[..., 0] = 1.0
+    kf = np.zeros((1, 1, N, d), np.float32)
+    kf[0, 0, [3, 5], 0] = 2.0
+    q, k = f32_to_bf16_bits(qf), f32_to_bf16_bits(kf)
+    v = random_bf16((1, 1, N, d), 141)
+    cases = [(O.KEEP, 0.25, [0]), (O.KEEP, 0.5, [0, 1]), (O.COVERAGE, 0.6, [0]), (O.COVERAGE, 0.7, [0, 1])]
+    for mode, param, want in cases:
+        out = O.prefill(q, k, v, block=Bs, segment=S, scale=scale, mode=mode, param=param)
+        assert out["perm"][0, 0].tolist() == [3, 5, 0, 1, 2, 4, 6, 7] + list(range(8, 16)), out["perm"]
+        for i in range(4, 8):
+            assert np.allclose(out["P"][0, 0, i, :4], [0.625, 0.125, 0.125, 0.125], rtol=1e-6), out["P"][0, 0, i]
+            assert (out["P"][0, 0, i, 4:] == 0).all()
+            assert out["idx"][0, 0, i, :out["counts"][0, 0, i]].tolist() == want, (mode, param, i, out["idx"][0, 0, i])
+        assert (out["counts"][0, 0, :4] == 0).all()
+        sel = [[] for _ in range(4)] + [want] * 4
+        perm = out["perm"][0, 0]
+        vis = bf.visibility(N, Bs, S, perm=perm, sel=sel)
+        keys_of_block = {0: {3, 5}, 1: {0, 1}}
+        for t in range(8, N):
+            assert {j for j in range(N) if vis[t][j]} == set().union(*(keys_of_block[b] for b in want)) | set(range(8, t + 1))
+        ref = bf.attention(bf.mat(q[0, 0]), bf.mat(k[0, 0]), bf.mat(v[0, 0]), vis, scale)
+        assert np.allclose(out["o"][0, 0], ref, atol=1e-12), (mode, param)
+
+
+def pin_prefill_pipeline_bruteforce(O):
+    """The whole pipeline on a random tiny GQA input, in both selection modes, against brute
+    force stage by stage: scores from explicit per-segment softmaxes; the permutation sorts
+    each segment of the returned float32 scores (descending, ties to the lower position); P is
+    the explicit pooled softmax over the candidates of the brute-force PERMUTED keys; the lists
+    follow the selection rules applied to the returned P (keep: the top max(1, floor(r*n));
+    coverage: the shortest prefix of the ranking whose sequential float32 sum reaches tau); the
+    output is brute-force attention over the visibility those lists and that permutation give."""
+    N, Bs, S, Hq, Hkv, d = 32, 4, 8, 4, 2, 8
+    G, nb, bps = Hq // Hkv, N // Bs, S // Bs
+    scale = 0.4
+    q, k, v = _tiny(151, Hq=Hq, Hkv=Hkv, N=N, d=d, scale_k=1.7)
+    for mode, param in ((O.KEEP, 0.34), (O.COVERAGE, 0.7), (O.COVERAGE, 0.95)):
+        out = O.prefill(q, k, v, block=Bs, segment=S, scale=scale, mode=mode, param=param)
+        for h in range(Hkv):
+            sc = bf.key_scores([bf.mat(q[0, g]) for g in range(h * G, (h + 1) * G)], bf.mat(k[0, h]), Bs, S, scale)
+            assert np.allclose(out["scores"][0, h], sc, rtol=2e-6, atol=1e-9)
+            s32 = out["scores"][0, h]
+            for s0 in range(0, N, S):
+                want = sorted(range(s0, s0 + S), key=lambda j: (-float(s32[j]), j))
+                assert out["perm"][0, h, s0:s0 + S].tolist() == want, (h, s0)
+        for g in range(Hq):
+            h = g // G
+            perm = out["perm"][0, h]
+            kp = np.stack([k[0, h, int(perm[p])] for p in range(N)])
+            ref = bf.block_probs(bf.mat(q[0, g]), bf.mat(kp), Bs, S, scale)
+            Pg = out["P"][0, g]
+            for (i, j), pij in ref.items():
+                assert math.isclose(float(Pg[i, j]), pij, rel_tol=2e-6), (g, i, j)
+            sel = []
+            for i in range(nb):
+                n = (i // bps) * bps
+                ranked = sorted(range(n), key=lambda j: (-float(Pg[i, j]), j))
+                if n == 0:
+                    kk = 0
+                elif mode == O.KEEP:
+                    kk = max(1, math.floor(param * n))
+                else:
+                    c, kk = np.float32(0), n
+                    for m, j in enumerate(ranked):
+                        c = np.float32(c + Pg[i, j])
+                        if float(c) >= param:
+                            kk = m + 1
+                            break
+                sel.append(sorted(ranked[:kk]))
+                assert int(out["counts"][0, g, i]) == kk, (mode, g, i)
+                assert out["idx"][0, g, i, :kk].tolist() == sel[-1], (mode, g, i)
+            vis = bf.visibility(N, Bs, S, perm=perm, sel=sel)
+            o_ref = bf.attention(bf.mat(q[0, g]), bf.mat(k[0, h]), bf.mat(v[0, h]), vis, scale)
+            assert np.allclose(out["o"][0, g], o_ref, atol=1e-12), (mode, g)
+
+
 # ----------------------------------------------------------------------------- packed sequences
 
 def _pack(x):

@@ -55,6 +55,36 @@ MUTANTS = {
     "varlen_P_rows_only": ('out["P"][:, :, i0:i1, i0:i1] = r["P"]', 'out["P"][:, :, i0:i1, :i1 - i0] = r["P"]'),
     "density_perm_max_position": ("perm[b, h, j * block:(j + 1) * block].min() <= last",
                                   "perm[b, h, j * block:(j + 1) * block].max() <= last"),
+    # the score softmax over the whole sequence instead of one segment at a time
+    "scores_global_softmax": (
+        "            for s0 in range(0, N, segment):\n"
+        "                keys = np.arange(s0, s0 + segment)\n"
+        "                Z = scale * (Qr @ bf16_to_f64(k[b, h, s0:s0 + segment]).T)      # [G*Bs, S]\n"
+        "                visible = keys[None, :] <= t_of_row[:, None]\n"
+        "                Z = np.where(visible, Z, -np.inf)\n"
+        "                Z = Z - Z.max(axis=1, keepdims=True)\n"
+        "                E = np.exp(Z)\n"
+        "                Pm = E / E.sum(axis=1, keepdims=True)\n"
+        "                acc[s0:s0 + segment] = Pm.sum(axis=0)\n",
+        "            for s0 in range(0, N, N):\n"
+        "                keys = np.arange(s0, s0 + N)\n"
+        "                Z = scale * (Qr @ bf16_to_f64(k[b, h, s0:s0 + N]).T)      # [G*Bs, S]\n"
+        "                visible = keys[None, :] <= t_of_row[:, None]\n"
+        "                Z = np.where(visible, Z, -np.inf)\n"
+        "                Z = Z - Z.max(axis=1, keepdims=True)\n"
+        "                E = np.exp(Z)\n"
+        "                Pm = E / E.sum(axis=1, keepdims=True)\n"
+        "                acc[s0:s0 + N] = Pm.sum(axis=0)\n"),
+    # block selection fed the unpermuted keys, or always run as keep ratio
+    "prefill_unpermuted_kbar": ("P = block_probabilities(q, k_perm, block=block, segment=segment, scale=scale)",
+                                "P = block_probabilities(q, k, block=block, segment=segment, scale=scale)"),
+    "prefill_mode_ignored": ("counts, idx = select_blocks(P, block=block, segment=segment, mode=mode, param=param)",
+                             "counts, idx = select_blocks(P, block=block, segment=segment, mode=KEEP, param=param)"),
+    # attention of the pipeline in the identity order, or over the permuted copies as if unpermuted
+    "prefill_attention_identity_order": ("o, lse = attention(q, k, v, block=block, segment=segment, scale=scale, perm=perm,",
+                                         "o, lse = attention(q, k, v, block=block, segment=segment, scale=scale, perm=None,"),
+    "prefill_attention_permuted_copies": ("o, lse = attention(q, k, v, block=block, segment=segment, scale=scale, perm=perm,",
+                                          "o, lse = attention(q, k_perm, v_perm, block=block, segment=segment, scale=scale, perm=perm,"),
 }
 
 

@@ -164,7 +164,8 @@ def density_main(args):
         nb, bps, G = N // Bs, S // Bs, Hq // Hkv
         bf = P.Buffers(sh, dev)
         P.pbs_score(sh, q, k, scale, bf.scores, bf.workspace)
-        P.pbs_permute(sh, bf.scores, k, v, bf.perm, bf.k_perm, bf.v_perm, bf.k_pool, bf.blk_minpos)
+        P.pbs_permute(sh, bf.scores, k, v, bf.perm, bf.k_perm, bf.v_perm, bf.k_pool, bf.blk_minpos,
+                      bf.perm_inv)
         o = torch.empty_like(q)
         lse_d = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
         P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale, o, lse_d)
@@ -183,7 +184,7 @@ def density_main(args):
                 if order == "permuted":
                     P.pbs_block_select(sh, q, bf.k_perm, bf.k_pool, scale, P.PBS_SELECT_COVERAGE, tau, None, 0,
                                        bf.counts, bf.idx, bf.workspace)
-                    P.pbs_attn_fwd(sh, q, bf.k_perm, bf.v_perm, bf.perm, bf.blk_minpos, bf.counts, bf.idx,
+                    P.pbs_attn_fwd(sh, q, bf.k_perm, bf.v_perm, bf.perm, bf.perm_inv, bf.counts, bf.idx,
                                    scale, o, lse)
                     own = own_perm
                 else:
@@ -261,11 +262,11 @@ def sweep_main(args):
             ev[0].record(stream)
             P.pbs_score(sh, q, k, scale, bf.scores, bf.workspace, stream=stream)
             P.pbs_permute(sh, bf.scores, k, v, bf.perm, bf.k_perm, bf.v_perm, bf.k_pool,
-                          bf.blk_minpos, stream=stream)
+                          bf.blk_minpos, bf.perm_inv, stream=stream)
             P.pbs_block_select(sh, q, bf.k_perm, bf.k_pool, scale, P.PBS_SELECT_KEEP_RATIO, keep,
                                None, 0, bf.counts, bf.idx, bf.workspace, stream=stream)
             ev[1].record(stream)
-            P.pbs_attn_fwd(sh, q, bf.k_perm, bf.v_perm, bf.perm, bf.blk_minpos, bf.counts, bf.idx,
+            P.pbs_attn_fwd(sh, q, bf.k_perm, bf.v_perm, bf.perm, bf.perm_inv, bf.counts, bf.idx,
                            scale, bf.o, bf.lse, stream=stream)
             ev[2].record(stream)
 
@@ -404,14 +405,14 @@ def main():
         if record:
             ev[1].record(stream)
         P.pbs_permute(sh, bf.scores, k, v, bf.perm, bf.k_perm, bf.v_perm, bf.k_pool, bf.blk_minpos,
-                      stream=stream)
+                      bf.perm_inv, stream=stream)
         if record:
             ev[2].record(stream)
         P.pbs_block_select(sh, q, bf.k_perm, bf.k_pool, scale, mode, param, None, 0, bf.counts,
                            bf.idx, bf.workspace, stream=stream)
         if record:
             ev[3].record(stream)
-        P.pbs_attn_fwd(sh, q, bf.k_perm, bf.v_perm, bf.perm, bf.blk_minpos, bf.counts, bf.idx,
+        P.pbs_attn_fwd(sh, q, bf.k_perm, bf.v_perm, bf.perm, bf.perm_inv, bf.counts, bf.idx,
                        scale, bf.o, bf.lse, stream=stream)
         if record:
             ev[4].record(stream)

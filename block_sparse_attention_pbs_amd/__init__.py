@@ -77,7 +77,7 @@ def lib():
     L.pbs_strerror.argtypes = [ctypes.c_int]
     L.pbs_strerror.restype = ctypes.c_char_p
     L.pbs_score.argtypes = [S, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
-    L.pbs_permute.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    L.pbs_permute.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     L.pbs_block_select.argtypes = [S, _P, _P, _P, ctypes.c_float, ctypes.c_int, ctypes.c_double,
                                    _P, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]
     L.pbs_attn_fwd.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
@@ -158,10 +158,10 @@ def pbs_score(shape, q, k, scale, scores, workspace, workspace_bytes=None, strea
 
 
 def pbs_permute(shape, scores, k, v, perm, k_perm, v_perm, k_pool=None, blk_minpos=None,
-                stream=None):
+                perm_inv=None, stream=None):
     _check(lib().pbs_permute(ctypes.byref(shape), _ptr(scores), _ptr(k), _ptr(v), _ptr(perm),
                              _ptr(k_perm), _ptr(v_perm), _ptr(k_pool), _ptr(blk_minpos),
-                             _stream(stream)))
+                             _ptr(perm_inv), _stream(stream)))
 
 
 def pbs_block_select(shape, q, k_perm, k_pool, scale, mode, param, blk_scores, flags, counts,
@@ -193,9 +193,9 @@ def pbs_block_select_varlen(shape, cu_seqlens, n_seqs, q, k_perm, k_pool, scale,
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
-def pbs_attn_fwd(shape, q, k, v, perm, blk_minpos, counts, idx, scale, o, lse=None, stream=None):
+def pbs_attn_fwd(shape, q, k, v, perm, perm_inv, counts, idx, scale, o, lse=None, stream=None):
     _check(lib().pbs_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm),
-                              _ptr(blk_minpos), _ptr(counts), _ptr(idx), scale, _ptr(o), _ptr(lse),
+                              _ptr(perm_inv), _ptr(counts), _ptr(idx), scale, _ptr(o), _ptr(lse),
                               _stream(stream)))
 
 
@@ -239,6 +239,7 @@ class Buffers:
         self.v_perm = torch.empty(kv, dtype=torch.bfloat16, **e)
         self.k_pool = torch.empty((B, Hkv, nb, d), dtype=torch.float32, **e)
         self.blk_minpos = torch.empty((B, Hkv, nb), dtype=torch.int32, **e)
+        self.perm_inv = torch.empty((B, Hkv, N), dtype=torch.int32, **e)
         self.counts = torch.empty((B, Hq, nb), dtype=torch.int32, **e)
         self.idx = torch.empty((B, Hq, nb, mo), dtype=torch.int32, **e)
         self.blk_scores = torch.empty((B, Hq, nb, nb), dtype=torch.float32, **e) if with_scores else None
@@ -263,10 +264,10 @@ def prefill(q, k, v, *, block: int, segment: int, keep: Optional[float] = None,
     mode, param = (PBS_SELECT_KEEP_RATIO, keep) if keep is not None else (PBS_SELECT_COVERAGE, coverage)
     pbs_score(shape, q, k, scale, bf.scores, bf.workspace, stream=stream)
     pbs_permute(shape, bf.scores, k, v, bf.perm, bf.k_perm, bf.v_perm, bf.k_pool, bf.blk_minpos,
-                stream=stream)
+                bf.perm_inv, stream=stream)
     pbs_block_select(shape, q, bf.k_perm, bf.k_pool, scale, mode, param, bf.blk_scores, 0,
                      bf.counts, bf.idx, bf.workspace, stream=stream)
-    pbs_attn_fwd(shape, q, bf.k_perm, bf.v_perm, bf.perm, bf.blk_minpos, bf.counts, bf.idx, scale,
+    pbs_attn_fwd(shape, q, bf.k_perm, bf.v_perm, bf.perm, bf.perm_inv, bf.counts, bf.idx, scale,
                  bf.o, bf.lse, stream=stream)
     return bf
 
@@ -288,10 +289,10 @@ def prefill_varlen(q, k, v, cu_seqlens, *, block: int, segment: int,
     mode, param = (PBS_SELECT_KEEP_RATIO, keep) if keep is not None else (PBS_SELECT_COVERAGE, coverage)
     pbs_score_varlen(shape, cu_seqlens, n_seqs, q, k, scale, bf.scores, bf.workspace, stream=stream)
     pbs_permute(shape, bf.scores, k, v, bf.perm, bf.k_perm, bf.v_perm, bf.k_pool, bf.blk_minpos,
-                stream=stream)
+                bf.perm_inv, stream=stream)
     pbs_block_select_varlen(shape, cu_seqlens, n_seqs, q, bf.k_perm, bf.k_pool, scale, mode, param,
                             bf.blk_scores, 0, bf.counts, bf.idx, bf.workspace, stream=stream)
-    pbs_attn_fwd(shape, q, bf.k_perm, bf.v_perm, bf.perm, bf.blk_minpos, bf.counts, bf.idx, scale,
+    pbs_attn_fwd(shape, q, bf.k_perm, bf.v_perm, bf.perm, bf.perm_inv, bf.counts, bf.idx, scale,
                  bf.o, bf.lse, stream=stream)
     return bf
 

@@ -176,7 +176,7 @@ int pbs_score_varlen(const pbs_shape* shape, const int32_t* cu_seqlens, int32_t 
 
 int pbs_permute(const pbs_shape* shape, const float* scores, const uint16_t* k,
                 const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
-                float* k_pool, int32_t* blk_minpos, void* stream) {
+                float* k_pool, int32_t* blk_minpos, int32_t* perm_inv, void* stream) {
   Dims d;
   int st = check_shape(shape, &d);
   if (st != PBS_OK) return st;
@@ -185,8 +185,9 @@ int pbs_permute(const pbs_shape* shape, const float* scores, const uint16_t* k,
   if ((st = check_required(req)) != PBS_OK) return st;
   if ((st = check_optional(k_pool)) != PBS_OK) return st;
   if ((st = check_optional(blk_minpos)) != PBS_OK) return st;
+  if ((st = check_optional(perm_inv)) != PBS_OK) return st;
   return status_of(pbs::launch_permute(d, scores, k, v, perm, k_perm, v_perm, k_pool, blk_minpos,
-                                       static_cast<hipStream_t>(stream)));
+                                       perm_inv, static_cast<hipStream_t>(stream)));
 }
 
 int pbs_permute_queries(const pbs_shape* shape, const int32_t* perm, const uint16_t* q,
@@ -221,7 +222,7 @@ int pbs_block_select_varlen(const pbs_shape* shape, const int32_t* cu_seqlens, i
 }
 
 int pbs_attn_fwd(const pbs_shape* shape, const uint16_t* q, const uint16_t* k,
-                 const uint16_t* v, const int32_t* perm, const int32_t* blk_minpos,
+                 const uint16_t* v, const int32_t* perm, const int32_t* perm_inv,
                  const int32_t* counts, const int32_t* idx, float scale, uint16_t* o,
                  float* lse, void* stream) {
   Dims d;
@@ -229,16 +230,18 @@ int pbs_attn_fwd(const pbs_shape* shape, const uint16_t* q, const uint16_t* k,
   if (st != PBS_OK) return st;
   if (!finite_positive(scale)) return PBS_E_ARG;
   if ((counts == nullptr) != (idx == nullptr)) return PBS_E_ARG;
-  if (!counts && (perm || blk_minpos)) return PBS_E_ARG;  // dense mode takes no permutation
+  if ((perm == nullptr) != (perm_inv == nullptr)) return PBS_E_ARG;  // both or neither
+  if (!counts && perm) return PBS_E_ARG;  // dense mode takes no permutation
   if (empty(d)) return PBS_OK;
   const void* const req[] = {q, k, v, o};
   if ((st = check_required(req)) != PBS_OK) return st;
-  const void* const opt[] = {perm, blk_minpos, counts, idx, lse};
+  const void* const opt[] = {perm, perm_inv, counts, idx, lse};
   for (const void* p : opt)
     if ((st = check_optional(p)) != PBS_OK) return st;
   const int mode = !counts ? 0 : (perm ? 1 : 2);
-  return status_of(pbs::launch_attn(d, q, k, v, perm, blk_minpos, counts, idx, nullptr, nullptr,
-                                    mode, scale, o, lse, static_cast<hipStream_t>(stream)));
+  return status_of(pbs::launch_attn(d, q, k, v, perm, perm_inv, nullptr, counts, idx, nullptr,
+                                    nullptr, mode, scale, o, lse,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 int pbs_attn_fwd_permuted_queries(const pbs_shape* shape, const uint16_t* q_perm,
@@ -255,8 +258,8 @@ int pbs_attn_fwd_permuted_queries(const pbs_shape* shape, const uint16_t* q_perm
   if ((st = check_required(req)) != PBS_OK) return st;
   if ((st = check_optional(blk_minpos)) != PBS_OK) return st;
   if ((st = check_optional(lse)) != PBS_OK) return st;
-  return status_of(pbs::launch_attn(d, q_perm, k_perm, v_perm, perm, blk_minpos, counts, idx,
-                                    nullptr, nullptr, 4, scale, o, lse,
+  return status_of(pbs::launch_attn(d, q_perm, k_perm, v_perm, perm, nullptr, blk_minpos, counts,
+                                    idx, nullptr, nullptr, 4, scale, o, lse,
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -272,8 +275,8 @@ int pbs_attn_fwd_hybrid(const pbs_shape* shape, const uint16_t* q, const uint16_
   const void* const req[] = {q, k_perm, v_perm, k, v, counts, idx, o};
   if ((st = check_required(req)) != PBS_OK) return st;
   if ((st = check_optional(lse)) != PBS_OK) return st;
-  return status_of(pbs::launch_attn(d, q, k_perm, v_perm, nullptr, nullptr, counts, idx, k, v, 3,
-                                    scale, o, lse, static_cast<hipStream_t>(stream)));
+  return status_of(pbs::launch_attn(d, q, k_perm, v_perm, nullptr, nullptr, nullptr, counts, idx,
+                                    k, v, 3, scale, o, lse, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -33,10 +33,13 @@
 //    A later max more than 2^64 above the reference only sets a flag, and the workgroup then
 //    recomputes with the exact row max (never seen on realistic inputs, but it keeps every value
 //    in range on any input);
-//  * the own segment of the permuted-key path is a stream of its visible slots: per workgroup,
-//    two LDS bitmaps (slots every row sees, slots some row sees) from one coalesced read of the
-//    segment's positions, expanded into a window of slot numbers; each stream stage gathers 32
-//    rows, the fully visible ones unmasked;
+//  * the own segment of the permuted-key path is a stream of its visible keys, taken in the order
+//    of their original positions: the inverse permutation (from pbs_permute) names the slot of
+//    every position, so the keys of positions seg_start .. the block's last row are exactly the
+//    slots perm_inv[seg_start ..], 32 per stage, read two stages ahead into a small LDS ring;
+//    each stream stage gathers its 32 rows from the permuted copies, the stages of positions
+//    before the block's first row unmasked, the last Bs keys masked through the stored
+//    positions perm[slot];
 //  * work order: heaviest query blocks first, and consecutive workgroups of one XCD (the
 //    hardware deals workgroups round-robin over the 8 XCDs) walk one KV head, so the K/V tiles a
 //    head's query blocks share stay in that XCD's L2.
@@ -51,6 +54,7 @@ struct AttnArgs {
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* perm;
+  const int32_t* inv;   // mode 1: slot of every original position (the inverse permutation)
   const int32_t* minpos;
   const int32_t* counts;
   const int32_t* idx;
@@ -83,8 +87,7 @@ struct AttnArgs {
 constexpr int kStageKeys = PBS_ATTN_STAGE_KEYS;  // keys per LDS stage
 constexpr int kOffWindow = 1792; // off-diagonal list entries held in LDS at a time
 constexpr int kOwnMax = 256;     // own-segment blocks (S / Bs <= 16384 / 64)
-constexpr int kOwnWin = 2048;    // visible own-segment keys held in LDS at a time (mode 1)
-constexpr int kSegWords = 16384 / 64;   // 64-slot words of the largest segment's visibility bitmap
+constexpr int kRing = 3;         // key-stream stages whose slots are held in LDS (mode 1)
 
 template <int D, int BS>
 struct Cfg {
@@ -193,20 +196,19 @@ struct StageIter {
   uint16_t* offw;       // LDS window of the off-diagonal list
   const uint16_t* ownl; // LDS list of the visible own-segment blocks
   int ent;              // the next entry's LDS word, read ahead (per lane, all lanes equal)
-  // Mode 1: the own segment is walked as a stream of its VISIBLE keys -- the slots whose
-  // original position is at or before the query block's last row, in permuted (slot) order -- 32
-  // per stage.  A key after every row of the query block adds exactly zero to every row, so it
-  // is never loaded; the rest still go through the per-key causal test.
+  // Mode 1: after the off-diagonal blocks, the own segment is walked as a stream of its VISIBLE
+  // keys in the order of their original positions: stream key x is the key at original position
+  // seg_start + x, held in slot perm_inv[seg_start + x] of the permuted copies.  Query block i
+  // sees positions up to its last row, so the stream is (i - seg_first + 1) * Bs keys long: the
+  // keys before the block's first row (visible to every row, unmasked stages), then the block's
+  // own Bs positions (masked stages, the causal test through perm[slot]).  A key after every row
+  // of the block adds exactly zero to every row and is never part of the stream.
   bool ks_on;
-  int n_ks;             // visible own-segment keys: first those visible to every row of the
-  int n_ks_full;        // block (n_ks_full of them, unmasked stages), then the others
+  int n_ks;             // stream keys
+  int n_ks_full;        // of which visible to every row of the block
   int ks;               // next stream stage
   int kidx;             // stream index of the stage just returned (-1: a contiguous block stage)
-  int kwin;             // first stream index held in the LDS window
-  int kfill, kscan;     // wave 0 only: entries in the window, next bitmap word to expand
-  uint16_t* ownk;       // LDS window: segment slots of visible keys (kOwnWin + 128 entries)
-  const uint64_t* bits; // LDS bitmaps of the segment's slots, 64 per word: seg_words words of
-  int seg_words;        // slots visible to every row, then seg_words words of the other visible ones
+  const int32_t* ring;  // LDS: kRing x 32 slots of upcoming stream stages (stage x in x % kRing)
 
   // Load off-diagonal entries [w0, w0 + kOffWindow) into LDS (all threads; barrier after).
   __device__ __forceinline__ void fill(int w0, int tid, int nt) {
@@ -218,71 +220,7 @@ struct StageIter {
   __device__ __forceinline__ int read_entry(int k) const {
     return k < n_off ? offw[k - win] : static_cast<int>(ownl[k - n_off]);
   }
-  // Wave 0: expand bitmap words from kscan on into the slot window until it holds at least
-  // kOwnWin entries or the bitmap ends (LDS only: the bitmap is built once per workgroup).
-  // 64 words at a time: lane l takes word kscan + l, a prefix sum of the words' bit counts gives
-  // each lane its place in the window, and the lanes whose words start before the window is
-  // full write their slots (word order, then bit order, as a word-by-word walk would).
-  __device__ __forceinline__ void scan_fill(int lane) {
-    const int nwords = 2 * seg_words;
-    while (kfill < kOwnWin && kscan < nwords) {
-      const int wi = kscan + lane;
-      const uint64_t bal = wi < nwords ? bits[wi] : 0ull;
-      const int cnt = __builtin_popcountll(bal);
-      int incl = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      const int excl = incl - cnt;
-      const bool take = wi < nwords && kfill + excl < kOwnWin;   // lanes 0 .. ntake-1
-      const int ntake = __builtin_popcountll(__builtin_amdgcn_ballot_w64(take));
-      if (take) {
-        const int word = wi < seg_words ? wi : wi - seg_words;
-        int pos = kfill + excl;
-        for (uint64_t m = bal; m != 0ull; m &= m - 1ull)
-          ownk[pos++] = static_cast<uint16_t>(word * 64 + __builtin_ctzll(m));
-      }
-      kfill += __shfl(incl, ntake - 1);
-      kscan += ntake;
-    }
-    // the stream has ended inside the window: the entries behind it name slot 0, so the rows
-    // of a last partial stage (masked out) and the spare rows read a key of the segment
-    if (kscan >= nwords) ownk[kfill + lane] = 0;
-  }
-  // The same expansion one word at a time: less code, for the refills inside the stage loop
-  // (there the words are dense, a window holds about 32 of them).
-  __device__ __forceinline__ void scan_fill_serial(int lane) {
-    while (kfill < kOwnWin && kscan < 2 * seg_words) {
-      const uint64_t bal = bits[kscan];
-      const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
-      const int word = kscan < seg_words ? kscan : kscan - seg_words;
-      if ((bal >> lane) & 1ull) ownk[kfill + before] = static_cast<uint16_t>(word * 64 + lane);
-      kfill += __builtin_popcountll(bal);
-      ++kscan;
-    }
-    if (kscan >= 2 * seg_words) ownk[kfill + lane] = 0;
-  }
-  // Make stream indices [k0, k0 + 32) available in the window.  Called by every wave right after
-  // a barrier, so no wave still reads the window; the entries from k0 to the end of the window
-  // (at most 94) move to its front, the scan continues behind them.
-  __device__ __forceinline__ void refill(int k0, int w, int lane) {
-    if (w == 0) {
-      const int keep = kwin + kfill - k0;
-      const int src = k0 - kwin;
-      const uint16_t e0 = lane < keep ? ownk[src + lane] : static_cast<uint16_t>(0);
-      const uint16_t e1 = lane + 64 < keep ? ownk[src + 64 + lane] : static_cast<uint16_t>(0);
-      if (lane < keep) ownk[lane] = e0;
-      if (lane + 64 < keep) ownk[64 + lane] = e1;
-      kfill = max(keep, 0);
-      scan_fill_serial(lane);
-    }
-    kwin = k0;
-    __syncthreads();
-  }
-  __device__ __forceinline__ void start(int tid, int nt, int w, int lane) {
+  __device__ __forceinline__ void start(int tid, int nt) {
     m = 0;
     half = -1;
     ks = 0;
@@ -294,16 +232,6 @@ struct StageIter {
         __syncthreads();
       }
       if (n_off + n_own > 0) ent = read_entry(0);
-    }
-    if (ks_on && kwin != 0) {  // a long stream left a later window in LDS: scan again from 0
-      __syncthreads();
-      if (w == 0) {
-        kfill = 0;
-        kscan = 0;
-        scan_fill(lane);
-      }
-      kwin = 0;
-      __syncthreads();
     }
   }
   __device__ __forceinline__ bool next_block(int tid, int nt) {
@@ -327,8 +255,16 @@ struct StageIter {
     orig = (mode == 3) && (m - 1 >= n_off);
     return true;
   }
+  // The next stream stage; false at the end of the stream.
+  __device__ __forceinline__ bool next_stream() {
+    if (ks * 32 >= n_ks) return false;
+    kidx = __builtin_amdgcn_readfirstlane(ks * 32);
+    ks = __builtin_amdgcn_readfirstlane(ks + 1);
+    masked = kidx + 32 > n_ks_full;   // holds a key that some row of the block must not see
+    return true;
+  }
   // Advance to the next stage; false when the list is exhausted.
-  __device__ __forceinline__ bool next(int tid, int nt, int w, int lane) {
+  __device__ __forceinline__ bool next(int tid, int nt) {
     if (half >= 0 && half + 1 < halves) {
       ++half;
       return true;
@@ -338,20 +274,14 @@ struct StageIter {
       kidx = -1;
       return next_block(tid, nt);
     }
-    if (ks * 32 >= n_ks) return false;
-    kidx = __builtin_amdgcn_readfirstlane(ks * 32);
-    ks = __builtin_amdgcn_readfirstlane(ks + 1);
-    if (kidx + 32 > kwin + kOwnWin) refill(kidx, w, lane);
-    j = seg_first;
-    masked = kidx + 32 > n_ks_full;   // holds a key that some row of the block must not see
     orig = false;
     half = halves - 1;   // one stage per stream step
-    return true;
+    return next_stream();
   }
   // next() where the caller knows the following stage is a key-block stage (KIND 1) or a
   // key-stream stage (KIND 2): the same result with the other case's code left out.
   template <int KIND>
-  __device__ __forceinline__ bool next_of(int tid, int nt, int w, int lane) {
+  __device__ __forceinline__ bool next_of(int tid, int nt) {
     if constexpr (KIND == 1) {
       if (half >= 0 && half + 1 < halves) {
         ++half;
@@ -361,14 +291,9 @@ struct StageIter {
       kidx = -1;
       return next_block(tid, nt);
     } else if constexpr (KIND == 2) {
-      if (ks * 32 >= n_ks) return false;
-      kidx = __builtin_amdgcn_readfirstlane(ks * 32);
-      ks = __builtin_amdgcn_readfirstlane(ks + 1);
-      if (kidx + 32 > kwin + kOwnWin) refill(kidx, w, lane);
-      masked = kidx + 32 > n_ks_full;
-      return true;
+      return next_stream();
     } else {
-      return next(tid, nt, w, lane);
+      return next(tid, nt);
     }
   }
 };
@@ -377,10 +302,9 @@ struct Stage {
   int key0;     // first key of the stage in the head's key order (block * Bs + stage * 32)
   bool masked;
   bool orig;    // read from the original keys and values (mode 3 own segment)
-  // Own-segment key-stream stage (mode 1): the segment slots of its keys and how many are
-  // valid (1..32); slots == nullptr for a contiguous stage.  seg0: first key of the segment.
-  const uint16_t* slots;
-  int cnt, seg0;
+  // Own-segment key-stream stage (mode 1): the slots of its 32 keys (perm_inv entries, in LDS);
+  // slots == nullptr for a contiguous stage.
+  const int32_t* slots;
 };
 
 // The stage the iterator just returned.
@@ -391,81 +315,77 @@ __device__ __forceinline__ Stage stage_of(const StageIter& it) {
   st.masked = it.masked;
   st.orig = it.orig;
   st.slots = nullptr;
-  st.cnt = 0;
-  st.seg0 = it.seg_first * BS;
-  if (it.kidx >= 0) {
-    st.slots = it.ownk + (it.kidx - it.kwin);
-    st.cnt = min(32, it.n_ks - it.kidx);
-    st.key0 = st.seg0;
-  }
+  if (it.kidx >= 0) st.slots = it.ring + ((it.kidx >> 5) % kRing) * 32;
   return st;
 }
 
 // Buffer resources of one head: keys, values, key positions, and (mode 3) the original keys
-// and values.
+// and values; mode 1: the own segment's rows of the permuted keys and values (ks, vs) and the
+// head's inverse permutation.
 struct Rsrc {
-  u32x4 k, v, p, k2, v2;
+  u32x4 k, v, p, k2, v2, ks, vs, inv;
 };
+
+// Mode 1: load the slots of stream stage x (perm_inv of its 32 positions) into the ring; wave 0,
+// one 4-byte direct load per lane, awaited by the next stage barrier.
+__device__ __forceinline__ void issue_ring(const Rsrc& rr, const StageIter& it, int x, int seg_pos,
+                                           int w, int lane) {
+  if (w == 0 && lane < 32 && x * 32 < it.n_ks)
+    load_lds4(rr.inv, it.ring + (x % kRing) * 32, static_cast<uint32_t>(seg_pos + x * 32 + lane) * 4,
+              0u);
+}
 
 // Start the asynchronous loads of one stage (K, V and, for masked permuted blocks, the original
 // positions of its keys) into LDS.  A spare chunk of a padded row re-reads chunk 0 of its row.
-// A key-stream stage gathers its rows: row r of the stage is segment slot slots[r] (rows past
-// the valid count read slot 0, the window's padding, and get a position after every row, so
-// they are masked out).
+// A key-stream stage gathers its rows: row r of the stage is the slot slots[r] of the own
+// segment, read through buffer resources that span only that segment, so a slot outside it
+// reads zeros instead of another segment's or head's memory.
 template <int D, int BS>
 __device__ __forceinline__ void issue_gathered(const AttnArgs& a, const Rsrc& rr, Stage st,
                                                uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
-                                               int lane) {
+                                               int lane, uint32_t cok, uint32_t cov) {
   using C = Cfg<D, BS>;
-  const uint32_t base = static_cast<uint32_t>(st.seg0) * static_cast<uint32_t>(a.kv_rs) * 2;
   const uint32_t rowb = static_cast<uint32_t>(a.kv_rs) * 2;   // < 2^24: checked on the host
-  // Straight-line code (no lane masks, no branches).  Every slot is read from the window before
+  // Straight-line code (no lane masks, no branches).  Every slot is read from the ring before
   // the first load is issued: the loads are asm with side effects, which the compiler never
   // moves an LDS read across, so reading the slots in between would wait out one LDS round
   // trip per load.  A wave with fewer loads than the others repeats the last one (the same
-  // bytes to the same place).
+  // bytes to the same place).  cok / cov: this lane's chunk offset minus the segment's first
+  // row, so that one 24-bit multiply-add turns a global slot into an offset in the segment.
   constexpr int UK = (C::NGK + C::NW - 1) / C::NW, UV = (C::NGV + C::NW - 1) / C::NW;
-  const int rk = lane / C::KROW, ck = lane - rk * C::KROW;
-  const int rv = lane / C::VROW, cv = lane - rv * C::VROW;
+  const int rk = lane / C::KROW, rv = lane / C::VROW;
   // Load u of wave w is load w + u*NW of the stage; only the last u can pass the last load
   // (UK, UV round up), so the others are a fixed offset from one per-stage address.
   uint32_t sk[UK], sv[UV];
-  const uint16_t* slk = st.slots + rk + w * C::RK;
-  const uint16_t* slv = st.slots + rv + w * C::RV;
+  const int32_t* slk = st.slots + rk + w * C::RK;
+  const int32_t* slv = st.slots + rv + w * C::RV;
 #pragma unroll
-  for (int u = 0; u + 1 < UK; ++u) sk[u] = slk[u * C::NW * C::RK];
-  sk[UK - 1] = st.slots[rk + min(w + (UK - 1) * C::NW, C::NGK - 1) * C::RK];
+  for (int u = 0; u + 1 < UK; ++u) sk[u] = static_cast<uint32_t>(slk[u * C::NW * C::RK]);
+  sk[UK - 1] = static_cast<uint32_t>(st.slots[rk + min(w + (UK - 1) * C::NW, C::NGK - 1) * C::RK]);
 #pragma unroll
-  for (int u = 0; u + 1 < UV; ++u) sv[u] = slv[u * C::NW * C::RV];
-  sv[UV - 1] = st.slots[rv + min(w + (UV - 1) * C::NW, C::NGV - 1) * C::RV];
-  const uint32_t cok = static_cast<uint32_t>(ck < C::CPR ? ck : 0) * 16;
-  const uint32_t cov = static_cast<uint32_t>(cv < C::CPR ? cv : 0) * 16;
+  for (int u = 0; u + 1 < UV; ++u) sv[u] = static_cast<uint32_t>(slv[u * C::NW * C::RV]);
+  sv[UV - 1] = static_cast<uint32_t>(st.slots[rv + min(w + (UV - 1) * C::NW, C::NGV - 1) * C::RV]);
 #pragma unroll
   for (int u = 0; u < UK; ++u) {
     const int j = min(w + u * C::NW, C::NGK - 1);
-    load_lds16_free(rr.k, Kst + j * C::RK * C::KROW * 8, __umul24(sk[u], rowb) + cok, base);
+    load_lds16_free(rr.ks, Kst + j * C::RK * C::KROW * 8, __umul24(sk[u], rowb) + cok, 0u);
   }
 #pragma unroll
   for (int u = 0; u < UV; ++u) {
     const int j = min(w + u * C::NW, C::NGV - 1);
-    load_lds16_free(rr.v, Vst + j * C::RV * C::VROW * 8, __umul24(sv[u], rowb) + cov, base);
+    load_lds16_free(rr.vs, Vst + j * C::RV * C::VROW * 8, __umul24(sv[u], rowb) + cov, 0u);
   }
-  if (st.masked && w == 0 && lane < C::SK) {
-    if (lane < st.cnt)
-      load_lds4(rr.p, Pst, static_cast<uint32_t>(st.slots[lane]) * 4,
-                static_cast<uint32_t>(st.seg0) * 4);
-    else
-      Pst[lane] = a.N + 1;   // after every row: the padding row is masked
-  }
+  if (st.masked && w == 0 && lane < C::SK)
+    load_lds4(rr.p, Pst, static_cast<uint32_t>(st.slots[lane]) * 4, 0u);
 }
 
 template <int D, int BS, bool MAYBE_STREAM = true>
 __device__ __forceinline__ void issue_stage(const AttnArgs& a, const Rsrc& rr, Stage st,
                                             uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
-                                            int lane) {
+                                            int lane, uint32_t cok, uint32_t cov) {
   using C = Cfg<D, BS>;
   if (MAYBE_STREAM && st.slots != nullptr) {
-    issue_gathered<D, BS>(a, rr, st, Kst, Vst, Pst, w, lane);
+    issue_gathered<D, BS>(a, rr, st, Kst, Vst, Pst, w, lane, cok, cov);
     return;
   }
   const uint32_t base = static_cast<uint32_t>(st.key0) * static_cast<uint32_t>(a.kv_rs) * 2;
@@ -489,7 +409,7 @@ __device__ __forceinline__ void issue_stage(const AttnArgs& a, const Rsrc& rr, S
       load_lds16(rv, Vst + n * 512,
                  static_cast<uint32_t>((r * a.kv_rs + (pc < C::CPR ? pc : 0) * 8) * 2), base);
   }
-  if (st.masked && (a.mode == 1 || a.mode == 4) && w == 0 && lane < C::SK)
+  if (st.masked && a.mode == 4 && w == 0 && lane < C::SK)
     load_lds4(rp, Pst, static_cast<uint32_t>(lane * 4), static_cast<uint32_t>(st.key0) * 4);
 }
 
@@ -631,6 +551,13 @@ struct Pipe {
   int p;        // LDS buffer of `cur`
 };
 
+// Per-lane constants of the loaders and the stream (computed once per workgroup).
+struct LoadCtx {
+  uint32_t cok, cov;   // mode 1: chunk offset of this lane's gathered K / V rows, minus the
+                       // segment's first slot (see issue_gathered)
+  int seg_pos;         // mode 1: first original position of the own segment
+};
+
 // `count` stages of one mask kind, one per iteration.  The loads of the next stage go into the
 // other buffer before the current stage is computed; the wait + barrier at the top of an iteration
 // both lands the current stage and frees the other buffer.  Buffers are picked by parity through
@@ -639,7 +566,7 @@ struct Pipe {
 // KIND: 0 any stage may follow, 1 only key-block stages follow, 2 only key-stream stages.
 template <int D, int BS, int MODE, bool MASKED, bool MAXONLY, int KIND>
 __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int count, Pipe& pp,
-                                           const Rsrc& rr, uint16_t* smem,
+                                           const Rsrc& rr, const LoadCtx& lc, uint16_t* smem,
                                            int32_t* Ps0, int32_t* Ps1, int w, int lane, int t,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                            f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
@@ -649,18 +576,23 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // the current stage landed; the other buffer is no longer read
     const int p = pp.p;
-    const bool more = it.template next_of<KIND>(tid, C::NT, w, lane);
+    const bool more = it.template next_of<KIND>(tid, C::NT);
     const Stage nxt = stage_of<BS, C::SK>(it);
     uint16_t* Kn = smem + (p ? a.tile_off[0] : a.tile_off[1]);
     uint16_t* Vn = smem + (p ? a.tile_off[2] : a.tile_off[3]);
     if constexpr (KIND != 2) {
-      if (more) issue_stage<D, BS, KIND == 0>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
+      if (more) issue_stage<D, BS, KIND == 0>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane, lc.cok,
+                                              lc.cov);
     }
     // Key stream: the loads go out after the stage's first K fragment reads, so the LDS reads of
     // their slots overlap those; no branch around them.  Past the end of the stream the
     // iterator still names the current stage, which is then loaded again into the free buffer.
+    // The slots of the stage after the next one go into the ring at the same time.
     auto stream_issue = [&]() {
-      if constexpr (KIND == 2) issue_gathered<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane);
+      if constexpr (KIND == 2) {
+        issue_gathered<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane, lc.cok, lc.cov);
+        issue_ring(rr, it, it.ks, lc.seg_pos, w, lane);
+      }
     };
     attn_stage<D, BS, MODE, MASKED, MAXONLY>(
         a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
@@ -671,24 +603,34 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
 }
 
 // One pass over the visited stages: every visit list is its unmasked blocks followed by its masked
-// ones (off-diagonal then own-segment blocks in permuted order; blocks before the diagonal then the
+// ones (off-diagonal blocks, then the key stream in mode 1; blocks before the diagonal then the
 // diagonal in identity and dense order), so a pass is two loops, one per mask kind.  With PRIME,
 // the rows' references are first set from the max of the pass's first stage (computed once more,
 // scores only, as soon as that stage has landed).
 template <int D, int BS, int MODE, bool MAXONLY, bool PRIME>
 __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int n_blk_stages,
                                           int n_unm_stages, int n_msk_stages, const Rsrc& rr,
-                                          uint16_t* smem, int32_t* Ps0, int32_t* Ps1, int w,
-                                          int lane, int t, const bf16x8 (&qf)[Cfg<D, BS>::NKS],
+                                          const LoadCtx& lc, uint16_t* smem, int32_t* Ps0,
+                                          int32_t* Ps1, int w, int lane, int t,
+                                          const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                           f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs) {
   using C = Cfg<D, BS>;
   const int tid = threadIdx.x;
-  it.start(tid, C::NT, w, lane);
-  if (it.next(tid, C::NT, w, lane)) {
+  if constexpr (MODE == 1) {
+    // the slots of the first two stream stages, landed (with the off-diagonal list window)
+    // before any stage is issued
+    issue_ring(rr, it, 0, lc.seg_pos, w, lane);
+    issue_ring(rr, it, 1, lc.seg_pos, w, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  it.start(tid, C::NT);
+  if (it.next(tid, C::NT)) {
     Pipe pp;
     pp.cur = stage_of<BS, C::SK>(it);
     pp.p = 0;
-    issue_stage<D, BS>(a, rr, pp.cur, smem + a.tile_off[0], smem + a.tile_off[2], Ps0, w, lane);
+    issue_stage<D, BS>(a, rr, pp.cur, smem + a.tile_off[0], smem + a.tile_off[2], Ps0, w, lane,
+                       lc.cok, lc.cov);
     if constexpr (PRIME) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -706,20 +648,20 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
     if constexpr (MODE == 1) {
       // key blocks (the last one hands over to the stream), then the stream's stages
       if (n_blk_stages > 0) {
-        run_stages<D, BS, MODE, false, MAXONLY, 1>(a, it, n_blk_stages - 1, pp, rr, smem, Ps0,
+        run_stages<D, BS, MODE, false, MAXONLY, 1>(a, it, n_blk_stages - 1, pp, rr, lc, smem, Ps0,
                                                    Ps1, w, lane, t, qf, oacc, rs);
-        run_stages<D, BS, MODE, false, MAXONLY, 0>(a, it, 1, pp, rr, smem, Ps0, Ps1, w, lane, t,
-                                                   qf, oacc, rs);
+        run_stages<D, BS, MODE, false, MAXONLY, 0>(a, it, 1, pp, rr, lc, smem, Ps0, Ps1, w, lane,
+                                                   t, qf, oacc, rs);
       }
-      run_stages<D, BS, MODE, false, MAXONLY, 2>(a, it, n_unm_stages - n_blk_stages, pp, rr,
+      run_stages<D, BS, MODE, false, MAXONLY, 2>(a, it, n_unm_stages - n_blk_stages, pp, rr, lc,
                                                  smem, Ps0, Ps1, w, lane, t, qf, oacc, rs);
-      run_stages<D, BS, MODE, true, MAXONLY, 2>(a, it, n_msk_stages, pp, rr, smem, Ps0, Ps1, w,
-                                                lane, t, qf, oacc, rs);
+      run_stages<D, BS, MODE, true, MAXONLY, 2>(a, it, n_msk_stages, pp, rr, lc, smem, Ps0, Ps1,
+                                                w, lane, t, qf, oacc, rs);
     } else {
-      run_stages<D, BS, MODE, false, MAXONLY, 1>(a, it, n_unm_stages, pp, rr, smem, Ps0, Ps1, w,
-                                                 lane, t, qf, oacc, rs);
-      run_stages<D, BS, MODE, true, MAXONLY, 1>(a, it, n_msk_stages, pp, rr, smem, Ps0, Ps1, w,
-                                                lane, t, qf, oacc, rs);
+      run_stages<D, BS, MODE, false, MAXONLY, 1>(a, it, n_unm_stages, pp, rr, lc, smem, Ps0, Ps1,
+                                                 w, lane, t, qf, oacc, rs);
+      run_stages<D, BS, MODE, true, MAXONLY, 1>(a, it, n_msk_stages, pp, rr, lc, smem, Ps0, Ps1,
+                                                w, lane, t, qf, oacc, rs);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -735,11 +677,9 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
   __shared__ __attribute__((aligned(16))) int32_t Ps1[C::SK];
   __shared__ uint16_t offw[kOffWindow];
   __shared__ uint16_t ownl[kOwnMax];
-  __shared__ uint16_t ownk[MODE == 1 ? kOwnWin + 128 : 1];
-  __shared__ uint64_t ownbits[MODE == 1 ? 2 * kSegWords : 1];
+  __shared__ __attribute__((aligned(16))) int32_t ring[MODE == 1 ? kRing * 32 : 1];
   __shared__ int own_count;
   __shared__ int qmax_w[C::NW];
-  __shared__ int own_full;
   // Visit-list and key-mask rules: mode 4 (permuted queries) walks the permuted keys like mode 1.
   constexpr int LM = (MODE == 4) ? 1 : MODE;
 
@@ -791,12 +731,33 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
   rr.v2 = make_rsrc(MODE == 3 ? a.v2 + kv0 : nullptr, MODE == 3 ? head_bytes : 0u);
   rr.p =
       make_rsrc(a.perm ? a.perm + kv_head : nullptr, a.perm ? static_cast<uint32_t>(a.N) * 4 : 0u);
+  const int seg_first = (i / a.bps) * a.bps;
+  LoadCtx lc;
+  lc.seg_pos = seg_first * BS;
+  lc.cok = lc.cov = 0u;
+  if constexpr (MODE == 1) {
+    // The own segment's rows of the permuted keys and values: the key stream gathers only there.
+    // A lane of a gathered load fetches chunk (lane % row chunks) of its row; the segment's first
+    // slot is taken off here, so a global slot s lands at (s - seg_pos) * row bytes + chunk.
+    using CC = Cfg<D, BS>;
+    const uint32_t rowb = static_cast<uint32_t>(a.kv_rs) * 2;
+    const size_t seg_off = a.km.off(b, h, lc.seg_pos);
+    const uint32_t seg_bytes =
+        static_cast<uint32_t>((static_cast<size_t>(a.bps * BS - 1) * a.kv_rs + D) * 2);
+    rr.ks = make_rsrc(a.k + seg_off, seg_bytes);
+    rr.vs = make_rsrc(a.v + seg_off, seg_bytes);
+    rr.inv = make_rsrc(a.inv + kv_head, static_cast<uint32_t>(a.N) * 4);
+    const int ck = lane % CC::KROW, cv = lane % CC::VROW;
+    const uint32_t sub = static_cast<uint32_t>(lc.seg_pos) * rowb;
+    lc.cok = static_cast<uint32_t>(ck < CC::CPR ? ck : 0) * 16 - sub;
+    lc.cov = static_cast<uint32_t>(cv < CC::CPR ? cv : 0) * 16 - sub;
+  }
 
   StageIter it;
   it.mode = LM;
   it.halves = C::HALVES;
   it.i = i;
-  it.seg_first = (i / a.bps) * a.bps;
+  it.seg_first = seg_first;
   it.n_off = 0;
   it.n_own = 0;
   it.win = 0;
@@ -812,12 +773,7 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
   it.n_ks_full = 0;
   it.ks = 0;
   it.kidx = -1;
-  it.kwin = 0;
-  it.kfill = 0;
-  it.kscan = 0;
-  it.ownk = ownk;
-  it.bits = ownbits;
-  it.seg_words = (a.bps * BS) / 64;
+  it.ring = ring;
   if (MODE != 0) {
     const size_t row = (static_cast<size_t>(b) * a.Hq + g) * a.nb + i;
     it.n_off = min(max(a.counts[row], 0), it.seg_first);
@@ -839,48 +795,10 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
       for (int ww = 1; ww < C::NW; ++ww) last_row = max(last_row, qmax_w[ww]);
     }
     if constexpr (MODE == 1) {
-      // The own segment as a key stream.  Every wave reads its share of the segment's positions
-      // (eight independent coalesced loads per step) and stores, per 64 slots, one word of each
-      // bitmap (ballots: position before the block's first row; position from its first to its
-      // last row); then wave 0 expands the first words into the LDS window of slots.
-      const int32_t* pseg = a.perm + kv_head + static_cast<size_t>(it.seg_first) * BS;
-      if (tid == 0) {
-        own_count = 0;
-        own_full = 0;
-      }
-      __syncthreads();
-      int n = 0, nf = 0;
-      for (int c = w * 8; c < it.seg_words; c += C::NW * 8) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int word = c + q;
-          const int pos = word < it.seg_words ? pseg[word * 64 + lane] : 0x7fffffff;
-          const uint64_t full = __builtin_amdgcn_ballot_w64(pos < first_row);
-          const uint64_t part = __builtin_amdgcn_ballot_w64(pos >= first_row && pos <= last_row);
-          if (word < it.seg_words && lane == 0) {
-            ownbits[word] = full;
-            ownbits[it.seg_words + word] = part;
-          }
-          nf += __builtin_popcountll(full);
-          n += __builtin_popcountll(full) + __builtin_popcountll(part);
-        }
-      }
-      if (lane == 0) {
-        atomicAdd(&own_count, n);
-        atomicAdd(&own_full, nf);
-      }
-      __syncthreads();
-      it.n_ks = own_count;
-      it.n_ks_full = own_full;
-      if (w == 0) {
-        // The window's tail starts as slot 0: a stage near the window's end reads up to four
-        // entries past the expanded ones into its spare rows, so those entries must always
-        // name a slot of the segment (LDS holds whatever an earlier workgroup left there).
-        ownk[kOwnWin + lane] = 0;
-        ownk[kOwnWin + 64 + lane] = 0;
-        it.scan_fill(lane);
-      }
-      __syncthreads();
+      // The own segment as a key stream: the positions from the segment's start to the block's
+      // last row, those before its first row visible to every row of the block.
+      it.n_ks = last_row + 1 - lc.seg_pos;
+      it.n_ks_full = first_row - lc.seg_pos;
     } else {
       // Own-segment blocks, compacted by wave 0.  Permuted queries (mode 4): a permuted block is
       // skipped when its smallest original position is after every row of the block, every
@@ -938,20 +856,20 @@ __global__ __launch_bounds__(BS * 2, PBS_ATTN_MIN_WAVES) void attn_fwd_kernel(At
 #pragma unroll
   for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
   RowState rs{-INFINITY, 0.f, -INFINITY};
-  attn_pass<D, BS, MODE, false, true>(a, it, n_blk, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
-                                oacc, rs);
+  attn_pass<D, BS, MODE, false, true>(a, it, n_blk, n_unm, n_msk, rr, lc, smem, Ps0, Ps1, w, lane,
+                                      t, qf, oacc, rs);
   // A row whose sum left [2^-60, 2^64] (scores far above or below its reference) is recomputed:
   // first its exact maximum, then the pass against that maximum.
   const float l0 = pair_sum(rs.lsum);
   if (__syncthreads_or(!(l0 >= 0x1p-60f && l0 <= 0x1p64f) ? 1 : 0)) {
-    attn_pass<D, BS, MODE, true, false>(a, it, n_blk, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
-                                 oacc, rs);
+    attn_pass<D, BS, MODE, true, false>(a, it, n_blk, n_unm, n_msk, rr, lc, smem, Ps0, Ps1, w,
+                                        lane, t, qf, oacc, rs);
 #pragma unroll
     for (int mt = 0; mt < C::NMT; ++mt) oacc[mt] = f32x16{};
     rs.mref = rs.mseen;
     rs.lsum = 0.f;
-    attn_pass<D, BS, MODE, false, false>(a, it, n_blk, n_unm, n_msk, rr, smem, Ps0, Ps1, w, lane, t, qf,
-                                  oacc, rs);
+    attn_pass<D, BS, MODE, false, false>(a, it, n_blk, n_unm, n_msk, rr, lc, smem, Ps0, Ps1, w,
+                                         lane, t, qf, oacc, rs);
   }
 
   const float l = pair_sum(rs.lsum);   // the two halves of the row
@@ -990,13 +908,14 @@ hipError_t launch_attn_t(const Dims& d, AttnArgs a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                       const int32_t* perm, const int32_t* blk_minpos, const int32_t* counts,
-                       const int32_t* idx, const uint16_t* k_orig, const uint16_t* v_orig,
-                       int mode, float scale, uint16_t* o, float* lse, hipStream_t stream) {
+                       const int32_t* perm, const int32_t* perm_inv, const int32_t* blk_minpos,
+                       const int32_t* counts, const int32_t* idx, const uint16_t* k_orig,
+                       const uint16_t* v_orig, int mode, float scale, uint16_t* o, float* lse,
+                       hipStream_t stream) {
   AttnArgs a;
   a.q = q; a.k = k; a.v = v;
   a.k2 = k_orig; a.v2 = v_orig;
-  a.perm = perm; a.minpos = blk_minpos; a.counts = counts; a.idx = idx;
+  a.perm = perm; a.inv = perm_inv; a.minpos = blk_minpos; a.counts = counts; a.idx = idx;
   a.o = o; a.lse = lse;
   a.B = d.B; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.N = d.N; a.nb = d.nb; a.bps = d.bps;
   a.max_off = d.max_off > 0 ? d.max_off : 1;

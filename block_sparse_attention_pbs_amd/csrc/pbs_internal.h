@@ -48,9 +48,11 @@ hipError_t launch_score(const Dims& d, const uint16_t* q, const uint16_t* k, flo
                         float* scores, void* ws, const int32_t* cu, int nseq,
                         hipStream_t stream);
 
+// perm_inv (may be null): perm_inv[perm[p]] = p, the slot of every original position.
 hipError_t launch_permute(const Dims& d, const float* scores, const uint16_t* k,
                           const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
-                          float* k_pool, int32_t* blk_minpos, hipStream_t stream);
+                          float* k_pool, int32_t* blk_minpos, int32_t* perm_inv,
+                          hipStream_t stream);
 
 // The query-permutation variant: q_perm[b, g, p] = q[b, g, perm[b, g / G, p]].
 hipError_t launch_permute_queries(const Dims& d, const int32_t* perm, const uint16_t* q,
@@ -67,9 +69,11 @@ hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t*
 // mode: 0 dense causal, 1 PBS with a permutation, 2 PBS in the identity order, 3 PBS with
 // permuted off-diagonal blocks and the own segment read from k_orig/v_orig in natural order,
 // 4 PBS with permuted queries (q holds them; rows are written back at their original positions).
+// perm_inv: mode 1, the slot of every original position (the inverse of perm).
 hipError_t launch_attn(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                       const int32_t* perm, const int32_t* blk_minpos, const int32_t* counts,
-                       const int32_t* idx, const uint16_t* k_orig, const uint16_t* v_orig,
-                       int mode, float scale, uint16_t* o, float* lse, hipStream_t stream);
+                       const int32_t* perm, const int32_t* perm_inv, const int32_t* blk_minpos,
+                       const int32_t* counts, const int32_t* idx, const uint16_t* k_orig,
+                       const uint16_t* v_orig, int mode, float scale, uint16_t* o, float* lse,
+                       hipStream_t stream);
 
 }  // namespace pbs

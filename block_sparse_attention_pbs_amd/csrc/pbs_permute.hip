@@ -10,7 +10,9 @@
 //  * seg_sort: one workgroup per (batch, KV head, segment).  The segment's scores become 64-bit
 //    keys (order-preserving float bits, inverted for descending order, with the in-segment
 //    position in the low word so equal scores keep their original order) and are sorted by a
-//    bitonic network in LDS (S <= 16384 keys = 128 KiB).
+//    bitonic network in LDS (S <= 16384 keys = 128 KiB).  The same pass writes the inverse
+//    permutation (the slot of every original position), which the attention kernel walks to
+//    read a query block's visible own-segment keys without searching the segment.
 //  * gather: one workgroup per (batch, KV head, block of Bs slots).  16-byte lanes read whole
 //    source rows (a row of K is contiguous, so every group of D/8 lanes issues one coalesced
 //    row read) and write the permuted rows contiguously; the same pass produces the float32
@@ -24,6 +26,7 @@ namespace {
 struct SortArgs {
   const float* scores;
   int32_t* perm;
+  int32_t* inv;   // may be null
   int N, S, n2;
 };
 
@@ -35,8 +38,11 @@ __global__ __launch_bounds__(1024) void seg_sort_kernel(SortArgs a) {
     keys[p] = (p < a.S) ? desc_sort_key(a.scores[base + p], static_cast<uint32_t>(p)) : ~0ull;
   bitonic_sort_lds(keys, a.n2);
   const int s0 = sigma * a.S;
-  for (int p = threadIdx.x; p < a.S; p += blockDim.x)
-    a.perm[base + p] = s0 + static_cast<int32_t>(keys[p] & 0xffffffffull);
+  for (int p = threadIdx.x; p < a.S; p += blockDim.x) {
+    const int32_t src = static_cast<int32_t>(keys[p] & 0xffffffffull);   // position in segment
+    a.perm[base + p] = s0 + src;
+    if (a.inv) a.inv[base + src] = s0 + p;
+  }
 }
 
 struct GatherArgs {
@@ -154,9 +160,10 @@ hipError_t launch_permute_queries(const Dims& d, const int32_t* perm, const uint
 
 hipError_t launch_permute(const Dims& d, const float* scores, const uint16_t* k,
                           const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
-                          float* k_pool, int32_t* blk_minpos, hipStream_t stream) {
+                          float* k_pool, int32_t* blk_minpos, int32_t* perm_inv,
+                          hipStream_t stream) {
   SortArgs sa;
-  sa.scores = scores; sa.perm = perm; sa.N = d.N; sa.S = d.S;
+  sa.scores = scores; sa.perm = perm; sa.inv = perm_inv; sa.N = d.N; sa.S = d.S;
   int n2 = 1;
   while (n2 < d.S) n2 <<= 1;
   sa.n2 = n2;

@@ -128,12 +128,16 @@ int pbs_score(const pbs_shape* shape, const uint16_t* q, const uint16_t* k, floa
  *   blk_minpos[b,h,j] smallest original position held by block j (optional, may be NULL;
  *                    lets pbs_attn_fwd_permuted_queries skip own-segment blocks no query of
  *                    a block can see)
+ *   perm_inv[b,h,j]  slot that holds original position j: perm_inv[b,h,perm[b,h,p]] = p
+ *                    (optional, may be NULL; pbs_attn_fwd walks it to read exactly the own-
+ *                    segment keys a query block can see; SK Implementation Steps keep the
+ *                    permutation so that it can be undone)
  *   scores [B,Hkv,N] float32, k/v [B,Hkv,N,d] bf16 -> perm [B,Hkv,N], k_perm/v_perm
- *   [B,Hkv,N,d], k_pool [B,Hkv,N/Bs,d], blk_minpos [B,Hkv,N/Bs].
+ *   [B,Hkv,N,d], k_pool [B,Hkv,N/Bs,d], blk_minpos [B,Hkv,N/Bs], perm_inv [B,Hkv,N].
  */
 int pbs_permute(const pbs_shape* shape, const float* scores, const uint16_t* k,
                 const uint16_t* v, int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
-                float* k_pool, int32_t* blk_minpos, void* stream);
+                float* k_pool, int32_t* blk_minpos, int32_t* perm_inv, void* stream);
 
 /*
  * pbs_permute_queries -- queries moved with their tokens (the query-permutation variant).
@@ -193,24 +197,27 @@ int pbs_block_select(const pbs_shape* shape, const uint16_t* q, const uint16_t* 
  * PBS mode (counts and idx given): query row t of block i in segment s attends to
  *   - every key of the kept blocks idx[b,g,i,0..counts) (whole blocks, no mask), and
  *   - every key of segment s with original position <= t: slot p is visible to row t iff
- *     perm[b,h,p] <= t.  The kernel reads only the slots visible to some row of the block
- *     (perm <= the block's last row), in slot order, those visible to every row unmasked
- *     (perm NULL: identity order, plain block-sparse attention).
- * Dense mode (perm, counts, idx all NULL): plain causal attention over keys 0..t.
- *   q      [B,Hq,N,d] bf16 (natural order)
- *   k, v   [B,Hkv,N,d] bf16: k_perm/v_perm from pbs_permute in PBS mode, natural K/V in
- *          dense mode or with perm == NULL
- *   perm   [B,Hkv,N] int32 or NULL
- *   blk_minpos [B,Hkv,N/Bs] int32 or NULL: accepted for the other attention entry points'
- *          sake and not read here (the own segment's visibility is taken from perm itself)
+ *     perm[b,h,p] <= t.  The kernel reads only the slots some row of the block can see: those
+ *     holding positions s*S .. the block's last row, found through perm_inv and taken in the
+ *     order of their positions; the keys before the block's first row unmasked, the block's
+ *     own Bs positions under the causal test on perm[slot]
+ *     (perm and perm_inv NULL: identity order, plain block-sparse attention).
+ * Dense mode (perm, perm_inv, counts, idx all NULL): plain causal attention over keys 0..t.
+ *   q        [B,Hq,N,d] bf16 (natural order)
+ *   k, v     [B,Hkv,N,d] bf16: k_perm/v_perm from pbs_permute in PBS mode, natural K/V in
+ *            dense mode or with perm == NULL
+ *   perm     [B,Hkv,N] int32 or NULL
+ *   perm_inv [B,Hkv,N] int32, the inverse of perm (from pbs_permute); required with perm and
+ *            NULL without it (PBS_E_ARG otherwise)
  *   counts [B,Hq,N/Bs], idx [B,Hq,N/Bs,pbs_max_offdiag] int32 from pbs_block_select, or NULL
  *   o      [B,Hq,N,d] bf16, written, original token order
  *   lse    [B,Hq,N] float32 natural-log softmax normaliser of every row, or NULL
- * counts and idx are trusted to come from pbs_block_select; an out-of-range count or index is
- * clamped into range (memory-safe, result unspecified).
+ * counts, idx, perm and perm_inv are trusted to come from pbs_block_select / pbs_permute; an
+ * out-of-range count, index or slot is clamped into range or reads zeros (memory-safe, result
+ * unspecified).
  */
 int pbs_attn_fwd(const pbs_shape* shape, const uint16_t* q, const uint16_t* k,
-                 const uint16_t* v, const int32_t* perm, const int32_t* blk_minpos,
+                 const uint16_t* v, const int32_t* perm, const int32_t* perm_inv,
                  const int32_t* counts, const int32_t* idx, float scale, uint16_t* o,
                  float* lse, void* stream);
 

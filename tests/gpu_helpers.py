@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 import block_sparse_attention_pbs_amd as P
+import oracle
 
 # Attention tolerance of the bf16 GPU path against the float64 oracle.
 ATTN_MAX_ABS = 2e-2
@@ -54,7 +55,7 @@ def run_score(sh, q, k, scale):
     return scores
 
 
-def run_permute(sh, scores, k, v, pool=True, minpos=True):
+def run_permute(sh, scores, k, v, pool=True, minpos=True, inv=True):
     B, H, N, d = sh.batch, sh.heads_kv, sh.seq_len, sh.head_dim
     nb = N // sh.block
     perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
@@ -62,9 +63,16 @@ def run_permute(sh, scores, k, v, pool=True, minpos=True):
     vp = torch.empty_like(kp)
     kpool = torch.empty((B, H, nb, d), dtype=torch.float32, device="cuda") if pool else None
     mpos = torch.empty((B, H, nb), dtype=torch.int32, device="cuda") if minpos else None
-    P.pbs_permute(sh, scores, k, v, perm, kp, vp, kpool, mpos)
+    pinv = torch.empty((B, H, N), dtype=torch.int32, device="cuda") if inv else None
+    P.pbs_permute(sh, scores, k, v, perm, kp, vp, kpool, mpos, pinv)
     torch.cuda.synchronize()
-    return perm, kp, vp, kpool, mpos
+    return perm, kp, vp, kpool, mpos, pinv
+
+
+def inverse_of(perm: np.ndarray) -> np.ndarray:
+    """The slot of every original position (what pbs_permute writes as perm_inv), from the
+    oracle's inverse permutation."""
+    return np.ascontiguousarray(oracle.inverse_permutation(np.ascontiguousarray(perm)), dtype=np.int32)
 
 
 def run_select(sh, q, k_perm, k_pool, scale, mode, param, blk_scores=None, flags=0):
@@ -79,10 +87,10 @@ def run_select(sh, q, k_perm, k_pool, scale, mode, param, blk_scores=None, flags
     return counts, idx
 
 
-def run_attn(sh, q, k, v, perm, minpos, counts, idx, scale, want_lse=True):
+def run_attn(sh, q, k, v, perm, perm_inv, counts, idx, scale, want_lse=True):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda") if want_lse else None
-    P.pbs_attn_fwd(sh, q, k, v, perm, minpos, counts, idx, scale, o, lse)
+    P.pbs_attn_fwd(sh, q, k, v, perm, perm_inv, counts, idx, scale, o, lse)
     torch.cuda.synchronize()
     return o, lse
 

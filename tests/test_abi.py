@@ -77,8 +77,9 @@ def test_errors_before_any_launch():
     assert _call("pbs_score", S, fake + 4, fake, 0.1, fake, fake, 1 << 30, None) == P.PBS_E_ALIGN
     assert _call("pbs_score", S, fake, fake, 0.1, fake, fake, 16, None) == P.PBS_E_WORKSPACE
     assert _call("pbs_score", S, fake, fake, -1.0, fake, fake, 1 << 30, None) == P.PBS_E_ARG
-    assert _call("pbs_permute", S, fake, None, fake, fake, fake, fake, None, None, None) == P.PBS_E_ARG
-    assert _call("pbs_permute", S, fake, fake, fake, fake, fake, fake, fake + 8, None, None) == P.PBS_E_ALIGN
+    assert _call("pbs_permute", S, fake, None, fake, fake, fake, fake, None, None, None, None) == P.PBS_E_ARG
+    assert _call("pbs_permute", S, fake, fake, fake, fake, fake, fake, fake + 8, None, None, None) == P.PBS_E_ALIGN
+    assert _call("pbs_permute", S, fake, fake, fake, fake, fake, fake, None, None, fake + 4, None) == P.PBS_E_ALIGN
     sel = lambda mode, param, flags, ws=1 << 30, bs=None: _call(
         "pbs_block_select", S, fake, fake, None, 0.1, mode, param, bs, flags, fake, fake, fake, ws, None)
     assert sel(2, 0.5, 0) == P.PBS_E_ARG
@@ -89,10 +90,12 @@ def test_errors_before_any_launch():
     assert sel(0, 0.5, P.PBS_FLAG_KEEP_FIRST | 8, ws=16) == P.PBS_E_ARG
     assert sel(0, 0.5, P.PBS_FLAG_SCORES_IN) == P.PBS_E_ARG   # probabilities in, but none given
     assert sel(0, 0.5, 0, ws=16) == P.PBS_E_WORKSPACE
-    attn = lambda perm, minpos, counts, idx: _call(
-        "pbs_attn_fwd", S, fake, fake, fake, perm, minpos, counts, idx, 0.1, fake, None, None)
+    attn = lambda perm, inv, counts, idx: _call(
+        "pbs_attn_fwd", S, fake, fake, fake, perm, inv, counts, idx, 0.1, fake, None, None)
     assert attn(None, None, fake, None) == P.PBS_E_ARG          # counts without idx
-    assert attn(fake, None, None, None) == P.PBS_E_ARG          # permutation in dense mode
+    assert attn(fake, fake, None, None) == P.PBS_E_ARG          # permutation in dense mode
+    assert attn(fake, None, fake, fake) == P.PBS_E_ARG          # permutation without its inverse
+    assert attn(None, fake, fake, fake) == P.PBS_E_ARG          # inverse without the permutation
     assert attn(fake, fake + 4, fake, fake) == P.PBS_E_ALIGN
     pq = lambda perm, q, qp: _call("pbs_permute_queries", S, perm, q, qp, None)
     assert pq(None, fake, fake + 256) == P.PBS_E_ARG
@@ -144,7 +147,7 @@ def test_empty_problem_is_ok_without_pointers():
                  None, None, None) == P.PBS_OK
     s = P.make_shape(2, 4, 2, 0, 128, 128, 256)
     assert _call("pbs_permute", ctypes.byref(s), None, None, None, None, None, None, None, None,
-                 None) == P.PBS_OK
+                 None, None) == P.PBS_OK
 
 
 def test_strerror():

@@ -10,7 +10,7 @@ import torch
 import block_sparse_attention_pbs_amd as P
 import oracle
 import pbs_synth
-from gpu_helpers import dev, dev_bf16, run_attn, run_permute, run_select, say, shape
+from gpu_helpers import dev, dev_bf16, inverse_of, run_attn, run_permute, run_select, say, shape
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,8 @@ def test_coverage_and_density(permuted, tau):
     assert np.array_equal(counts.cpu().numpy(), rc)
     if permuted:
         minpos = perm.reshape(1, Hkv, N // Bs, Bs).min(-1).astype(np.int32)
-        _, lse = run_attn(sh, gq, dev_bf16(kp), dev_bf16(vp), dev(perm), dev(minpos), counts, idx, scale)
+        _, lse = run_attn(sh, gq, dev_bf16(kp), dev_bf16(vp), dev(perm), dev(inverse_of(perm)), counts,
+                          idx, scale)
     else:
         _, lse = run_attn(sh, gq, gk, gv, None, None, counts, idx, scale)
     _, lse_d = run_attn(sh, gq, gk, gv, None, None, None, None, scale)
@@ -94,7 +95,8 @@ def test_coverage_full_size_sampled():
     sh = shape(1, Hq, Hkv, N, d, Bs, S)
     gq, gk, gv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
     minpos = perm.reshape(1, Hkv, nb, Bs).min(-1).astype(np.int32)
-    _, lse = run_attn(sh, gq, dev_bf16(kp), dev_bf16(vp), dev(perm), dev(minpos), dev(rc), dev(ri), scale)
+    _, lse = run_attn(sh, gq, dev_bf16(kp), dev_bf16(vp), dev(perm), dev(inverse_of(perm)), dev(rc),
+                      dev(ri), scale)
     _, lse_d = run_attn(sh, gq, gk, gv, None, None, None, None, scale)
     cov = torch.exp(lse - lse_d).cpu().numpy()
     got = np.stack([cov[b, g, i * Bs:(i + 1) * Bs] for b, g, i in samples])

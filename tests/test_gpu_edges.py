@@ -6,8 +6,8 @@ import torch
 import block_sparse_attention_pbs_amd as P
 import oracle
 import pbs_synth
-from gpu_helpers import (check_attn, dev, dev_bf16, lists_equal, run_attn, run_permute, run_select,
-                         say, shape)
+from gpu_helpers import (check_attn, dev, dev_bf16, inverse_of, lists_equal, run_attn, run_permute,
+                         run_select, say, shape)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +72,8 @@ def test_sort_specials_bitexact():
     k = pbs_synth.random_bf16((B, H, N, d), 5)
     v = pbs_synth.random_bf16((B, H, N, d), 6)
     sh = shape(B, H, H, N, d, Bs, S)
-    perm, kp, vp, _, _ = run_permute(sh, dev(sc), dev_bf16(k), dev_bf16(v), pool=False, minpos=False)
+    perm, kp, vp, _, _, _ = run_permute(sh, dev(sc), dev_bf16(k), dev_bf16(v), pool=False,
+                                        minpos=False, inv=False)
     assert np.array_equal(perm.cpu().numpy(), oracle.segment_permutation(sc, segment=S))
 
 
@@ -171,10 +172,11 @@ def test_permute_largest_segment():
     k = pbs_synth.random_bf16((B, H, N, d), 10)
     v = pbs_synth.random_bf16((B, H, N, d), 11)
     sh = shape(B, H, H, N, d, Bs, S)
-    perm, kp, vp, _, mpos = run_permute(sh, dev(sc), dev_bf16(k), dev_bf16(v), pool=False)
+    perm, kp, vp, _, mpos, pinv = run_permute(sh, dev(sc), dev_bf16(k), dev_bf16(v), pool=False)
     ref = oracle.segment_permutation(sc, segment=S)
     assert np.array_equal(perm.cpu().numpy(), ref)
     assert np.array_equal(mpos.cpu().numpy(), ref.reshape(B, H, N // Bs, Bs).min(-1))
+    assert np.array_equal(pinv.cpu().numpy(), inverse_of(ref))
 
 
 def test_deterministic():
@@ -239,9 +241,8 @@ def test_dominant_late_key_pbs(permuted):
                               idx=idx)
     assert ol.max() > 60.0
     sh = shape(1, 2, 1, N, 128, Bs, S)
-    minpos = perm.reshape(1, 1, N // Bs, Bs).min(-1).astype(np.int32)
     o, lse = run_attn(sh, dev_bf16(q), dev_bf16(kp), dev_bf16(vp),
-                      dev(perm) if permuted else None, dev(minpos) if permuted else None,
+                      dev(perm) if permuted else None, dev(inverse_of(perm)) if permuted else None,
                       dev(counts), dev(idx), scale)
     check_attn(o.float().cpu().numpy(), oo, f"dominant key PBS permuted={permuted}")
     assert np.abs(lse.cpu().numpy() - ol).max() < 1e-3
@@ -283,12 +284,12 @@ def test_long_lists_refill_the_window(dominant):
 
 
 def test_key_stream_refill_and_fallback():
-    """The own segment's key stream longer than the kernel's slot window (2048 keys) together
-    with the fallback passes: N=16384, Bs=128, S=8192, keep 1 (the result equals dense causal
-    attention).  A dominant key at position 11192 of the second segment sorts to its first slot,
-    so for the rows after it the stream meets a logit far above the first stage's reference, the
-    row sums overflow, and the fallback passes must walk the stream again from its first window
-    (query blocks late in the segment see up to 8192 keys, four windows)."""
+    """The own segment's key stream at its longest (query blocks late in an 8192-key segment see
+    up to 8192 keys, 256 stages through the kernel's slot ring) together with the fallback
+    passes: N=16384, Bs=128, S=8192, keep 1 (the result equals dense causal attention).  A
+    dominant key at position 11192 of the second segment sorts to its first slot, so for the rows
+    after it the stream meets a logit far above the first stage's reference, the row sums
+    overflow, and the fallback passes must walk the stream again from its first stage."""
     say("key stream refill + fallback, d=128 Bs=128 S=8192 N=16384")
     N, d, Bs, S = 16384, 128, 128, 8192
     rng = np.random.default_rng(77)

@@ -6,11 +6,14 @@ times (the same entry points, shapes and parameters), on outputs the oracle can 
     float32 scores;
   * block selection: every row, bit-exact, given the oracle's float32 block probabilities;
   * attention with the oracle's permutation and lists: sampled query blocks (the first and last
-    block of every segment and every 16th block) of a few query heads, max-abs 2e-2 / mean-abs
+    block of every segment and every 16th block) of every query head, max-abs 2e-2 / mean-abs
     2e-3, through pbs_attn_fwd and through pbs_attn_fwd_hybrid;
   * the query-permutation variant: query gather and selection bit-exact, attention on sampled
     permuted query blocks;
-  * the whole GPU pipeline end to end: the same sampled blocks against the whole oracle pipeline.
+  * the whole GPU pipeline end to end: the same sampled blocks of every query head against the
+    whole oracle pipeline, with the permutation and the kept-block counts agreeing almost
+    everywhere (they can differ only where the two sides' float32 scores round a near-tie
+    differently).
 
 Each workload is generated once per module (seconds) and the oracle stages cost tens of seconds
 at 128K on the host."""
@@ -21,8 +24,8 @@ import torch
 import block_sparse_attention_pbs_amd as P
 import oracle
 import pbs_synth
-from gpu_helpers import (check_attn, dev, dev_bf16, host_bits, lists_equal, run_attn, run_permute,
-                         run_score, run_select, say)
+from gpu_helpers import (check_attn, dev, dev_bf16, host_bits, inverse_of, lists_equal, run_attn,
+                         run_permute, run_score, run_select, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,8 +74,9 @@ def test_full_scores(full):
 def test_full_permute_bitexact(full):
     say(full["name"], "pbs_permute")
     ref, sh = full["ref"], full["sh"]
-    perm, kp, vp, kpool, mpos = run_permute(sh, dev(ref["scores"]), full["g"]["k"], full["g"]["v"])
+    perm, kp, vp, kpool, mpos, pinv = run_permute(sh, dev(ref["scores"]), full["g"]["k"], full["g"]["v"])
     assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+    assert np.array_equal(pinv.cpu().numpy(), inverse_of(ref["perm"]))
     assert np.array_equal(host_bits(kp), ref["k_perm"])
     assert np.array_equal(host_bits(vp), ref["v_perm"])
     B, H, N = ref["perm"].shape
@@ -98,17 +102,14 @@ def test_full_select_bitexact(full):
 def test_full_attention_sampled(full):
     w, ref, inp = full["w"], full["ref"], full["inp"]
     mode = oracle.KEEP if w.mode == "keep" else oracle.COVERAGE
-    G = w.heads_q // w.heads_kv
-    heads = sorted({0, G - 1, w.heads_q - 1})
+    heads = list(range(w.heads_q))
     for param in sorted({w.params[0], w.params[-1]}):
         say(full["name"], f"attention, param {param}")
         rc, ri = oracle.select_blocks(ref["P"], block=w.block, segment=w.segment, mode=mode, param=param)
-        B, H, N = ref["perm"].shape
-        minpos = ref["perm"].reshape(B, H, N // w.block, w.block).min(-1).astype(np.int32)
         kp = full.get("gpu_kp") if full.get("gpu_kp") is not None else dev_bf16(ref["k_perm"])
         vp = full.get("gpu_vp") if full.get("gpu_vp") is not None else dev_bf16(ref["v_perm"])
-        o, lse = run_attn(full["sh"], full["g"]["q"], kp, vp, dev(ref["perm"]), dev(minpos), dev(rc),
-                          dev(ri), full["scale"])
+        o, lse = run_attn(full["sh"], full["g"]["q"], kp, vp, dev(ref["perm"]), dev(inverse_of(ref["perm"])),
+                          dev(rc), dev(ri), full["scale"])
         samples = _sample_blocks(w, heads)
         oo, ol = oracle.attention(inp["q"], inp["k"], inp["v"], block=w.block, segment=w.segment,
                                   scale=full["scale"], perm=ref["perm"], counts=rc, idx=ri,
@@ -179,7 +180,7 @@ def test_full_end_to_end_sampled(full):
     torch.cuda.synchronize()
     mode = oracle.KEEP if w.mode == "keep" else oracle.COVERAGE
     rc, ri = oracle.select_blocks(ref["P"], block=w.block, segment=w.segment, mode=mode, param=param)
-    heads = [0, w.heads_q - 1]
+    heads = list(range(w.heads_q))
     samples = _sample_blocks(w, heads)
     oo, _ = oracle.attention(inp["q"], inp["k"], inp["v"], block=w.block, segment=w.segment,
                              scale=full["scale"], perm=ref["perm"], counts=rc, idx=ri, qblocks=samples)
@@ -189,3 +190,4 @@ def test_full_end_to_end_sampled(full):
     cnt_agree = float(np.mean(bufs.counts.cpu().numpy() == rc))
     say(f"perm agreement {perm_agree:.4f}, count agreement {cnt_agree:.4f}")
     check_attn(got, oo, f"{full['name']} end-to-end ({len(samples)} blocks)")
+    assert perm_agree >= 0.995 and cnt_agree >= 0.99, (perm_agree, cnt_agree)

@@ -15,7 +15,7 @@ import torch
 import block_sparse_attention_pbs_amd as P
 import oracle
 import pbs_synth
-from gpu_helpers import check_attn, dev, dev_bf16, lists_equal, say
+from gpu_helpers import check_attn, dev, dev_bf16, inverse_of, lists_equal, say
 
 pytestmark = pytest.mark.gpu
 
@@ -146,9 +146,8 @@ def test_layout_bnhd_against_oracle():
     B, H, N = ref["perm"].shape
     k_perm = _tok(dev_bf16(ref["k_perm"]))
     v_perm = _tok(dev_bf16(ref["v_perm"]))
-    minpos = ref["perm"].reshape(B, H, N // w.block, w.block).min(-1).astype(np.int32)
     o = torch.empty_like(q)
-    P.pbs_attn_fwd(sh, q, k_perm, v_perm, dev(ref["perm"]), dev(minpos), dev(ref["counts"]),
+    P.pbs_attn_fwd(sh, q, k_perm, v_perm, dev(ref["perm"]), dev(inverse_of(ref["perm"])), dev(ref["counts"]),
                    dev(ref["idx"]), scale, o, None)
     torch.cuda.synchronize()
     check_attn(_head(o).float().cpu().numpy().astype(np.float64), ref["o"],

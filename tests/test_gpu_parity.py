@@ -16,8 +16,8 @@ import torch
 import block_sparse_attention_pbs_amd as P
 import oracle
 import pbs_synth
-from gpu_helpers import (check_attn, dev, dev_bf16, host_bits, lists_equal, run_attn, run_permute,
-                         run_score, run_select, say, shape)
+from gpu_helpers import (check_attn, dev, dev_bf16, host_bits, inverse_of, lists_equal, run_attn,
+                         run_permute, run_score, run_select, say, shape)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +31,8 @@ CASES = {
     "d64_bs128_cov": (4, 2, 1024, 64, 128, 256, "coverage", 0.9),
     "d128_bs64_cov": (4, 1, 1152, 128, 64, 192, "coverage", 0.8),
     "batch3_gqa2_keep": (4, 2, 1024, 128, 128, 256, "keep", 0.4, 3),
+    # B*Hkv = 8: the attention's work order gives each XCD whole KV heads
+    "gqa2_8kv_xcd": (16, 8, 1024, 128, 128, 256, "keep", 0.3),
 }
 
 
@@ -75,7 +77,8 @@ def test_scores(case):
 def test_permute_bitexact_given_oracle_scores(case):
     say(case["name"], "pbs_permute")
     sh, ref = case["sh"], case["ref"]
-    perm, kp, vp, kpool, mpos = run_permute(sh, dev(ref["scores"]), case["g"]["k"], case["g"]["v"])
+    perm, kp, vp, kpool, mpos, pinv = run_permute(sh, dev(ref["scores"]), case["g"]["k"], case["g"]["v"])
+    assert np.array_equal(pinv.cpu().numpy(), inverse_of(ref["perm"]))
     assert np.array_equal(perm.cpu().numpy(), ref["perm"])
     assert np.array_equal(host_bits(kp), ref["k_perm"])
     assert np.array_equal(host_bits(vp), ref["v_perm"])
@@ -111,10 +114,9 @@ def test_select_keep_first_bitexact(case):
     c = counts.cpu().numpy()
     first = idx.cpu().numpy()[..., 0]
     assert ((c == 0) | (first == 0)).all()
-    B, H, N = ref["perm"].shape
-    minpos = ref["perm"].reshape(B, H, N // w.block, w.block).min(-1).astype(np.int32)
     o, _ = run_attn(sh, case["g"]["q"], dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
-                    dev(ref["perm"]), dev(minpos), counts, idx, case["scale"], want_lse=False)
+                    dev(ref["perm"]), dev(inverse_of(ref["perm"])), counts, idx, case["scale"],
+                    want_lse=False)
     oo, _ = oracle.attention(case["inp"]["q"], case["inp"]["k"], case["inp"]["v"], block=w.block,
                              segment=w.segment, scale=case["scale"], perm=ref["perm"], counts=rc,
                              idx=ri)
@@ -144,18 +146,11 @@ def test_block_probabilities(case):
 def test_attention_given_oracle_lists(case):
     say(case["name"], "pbs_attn_fwd (oracle permutation and lists)")
     ref, sh = case["ref"], case["sh"]
-    B, H, N = ref["perm"].shape
-    Bs = sh.block
-    minpos = ref["perm"].reshape(B, H, N // Bs, Bs).min(-1).astype(np.int32)
     o, lse = run_attn(sh, case["g"]["q"], dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
-                      dev(ref["perm"]), dev(minpos), dev(ref["counts"]), dev(ref["idx"]),
-                      case["scale"])
+                      dev(ref["perm"]), dev(inverse_of(ref["perm"])), dev(ref["counts"]),
+                      dev(ref["idx"]), case["scale"])
     check_attn(o.float().cpu().numpy(), ref["o"], f"{case['name']} attention")
     assert np.abs(lse.cpu().numpy() - ref["lse"]).max() < 1e-3
-    # the block-skip hint is only an optimisation: without it the result is the same
-    o2, _ = run_attn(sh, case["g"]["q"], dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
-                     dev(ref["perm"]), None, dev(ref["counts"]), dev(ref["idx"]), case["scale"])
-    assert torch.equal(o, o2)
 
 
 def test_hybrid_own_segment_natural(case):
@@ -262,4 +257,6 @@ def test_end_to_end(case):
     cnt_agree = float(np.mean(bufs.counts.cpu().numpy() == ref["counts"]))
     say(f"perm agreement {perm_agree:.4f}, count agreement {cnt_agree:.4f}")
     check_attn(bufs.o.float().cpu().numpy(), ref["o"], f"{case['name']} end-to-end")
-    assert perm_agree > 0.5
+    # a flip needs two keys whose float32 scores round differently on the two sides (scores
+    # agree to ~1e-6 relative), so nearly every slot and every count must agree
+    assert perm_agree >= 0.99 and cnt_agree >= 0.98, (perm_agree, cnt_agree)

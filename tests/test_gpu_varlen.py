@@ -14,7 +14,7 @@ import torch
 import block_sparse_attention_pbs_amd as P
 import oracle
 import pbs_synth
-from gpu_helpers import check_attn, dev, dev_bf16, host_bits, lists_equal, say
+from gpu_helpers import check_attn, dev, dev_bf16, host_bits, inverse_of, lists_equal, say
 
 pytestmark = pytest.mark.gpu
 
@@ -88,9 +88,12 @@ def test_varlen_permute_bitexact_given_oracle_scores(case):
     perm = torch.empty((1, w.heads_kv, w.seq_len), dtype=torch.int32, device="cuda")
     kp, vp = torch.empty_like(case["g"]["k"]), torch.empty_like(case["g"]["v"])
     mpos = torch.empty((1, w.heads_kv, nb), dtype=torch.int32, device="cuda")
-    P.pbs_permute(sh, dev(ref["scores"]), case["g"]["k"], case["g"]["v"], perm, kp, vp, None, mpos)
+    pinv = torch.empty_like(perm)
+    P.pbs_permute(sh, dev(ref["scores"]), case["g"]["k"], case["g"]["v"], perm, kp, vp, None, mpos,
+                  pinv)
     torch.cuda.synchronize()
     assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+    assert np.array_equal(pinv.cpu().numpy(), inverse_of(ref["perm"]))
     assert np.array_equal(host_bits(kp), ref["k_perm"])
     assert np.array_equal(host_bits(vp), ref["v_perm"])
 
@@ -119,13 +122,11 @@ def test_varlen_block_probabilities(case):
 
 def test_varlen_attention_given_oracle_lists(case):
     ref, sh, w = case["ref"], case["sh"], case["w"]
-    N = w.seq_len
-    minpos = ref["perm"].reshape(1, w.heads_kv, N // w.block, w.block).min(-1).astype(np.int32)
     o = torch.empty_like(case["g"]["q"])
     lse = torch.empty(o.shape[:3], dtype=torch.float32, device="cuda")
     P.pbs_attn_fwd(sh, case["g"]["q"], dev_bf16(ref["k_perm"]), dev_bf16(ref["v_perm"]),
-                   dev(ref["perm"]), dev(minpos), dev(ref["counts"]), dev(ref["idx"]),
-                   case["scale"], o, lse)
+                   dev(ref["perm"]), dev(inverse_of(ref["perm"])), dev(ref["counts"]),
+                   dev(ref["idx"]), case["scale"], o, lse)
     torch.cuda.synchronize()
     check_attn(o.float().cpu().numpy(), ref["o"], f"{case['name']} varlen attention")
     assert np.abs(lse.cpu().numpy() - ref["lse"]).max() < 1e-3

@@ -26,6 +26,8 @@ PBS_E_SHAPE = -2
 PBS_E_ALIGN = -3
 PBS_E_WORKSPACE = -4
 PBS_E_LAUNCH = -5
+PBS_E_SCRATCH = -6
+PBS_NOALLOC_SCRATCH_BYTES = 16 << 20
 PBS_SELECT_KEEP_RATIO = 0
 PBS_SELECT_COVERAGE = 1
 PBS_LAYOUT_BHND = 0
@@ -36,7 +38,7 @@ PBS_FLAG_KEEP_FIRST = 2
 ENTRY_POINTS = ("pbs_workspace_bytes", "pbs_max_offdiag", "pbs_strerror", "pbs_score",
                 "pbs_permute", "pbs_block_select", "pbs_attn_fwd", "pbs_attn_fwd_hybrid",
                 "pbs_permute_queries", "pbs_attn_fwd_permuted_queries", "pbs_score_varlen",
-                "pbs_block_select_varlen")
+                "pbs_block_select_varlen", "pbs_score_noalloc")
 
 
 class PbsError(RuntimeError):
@@ -77,6 +79,7 @@ def lib():
     L.pbs_strerror.argtypes = [ctypes.c_int]
     L.pbs_strerror.restype = ctypes.c_char_p
     L.pbs_score.argtypes = [S, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+    L.pbs_score_noalloc.argtypes = [S, _P, _P, ctypes.c_float, _P, _P]
     L.pbs_permute.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     L.pbs_block_select.argtypes = [S, _P, _P, _P, ctypes.c_float, ctypes.c_int, ctypes.c_double,
                                    _P, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]
@@ -92,7 +95,7 @@ def lib():
                                           _P, ctypes.c_size_t, _P]
     for name in ("pbs_score", "pbs_permute", "pbs_block_select", "pbs_attn_fwd",
                  "pbs_attn_fwd_hybrid", "pbs_permute_queries", "pbs_attn_fwd_permuted_queries",
-                 "pbs_score_varlen", "pbs_block_select_varlen"):
+                 "pbs_score_varlen", "pbs_block_select_varlen", "pbs_score_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -155,6 +158,11 @@ def pbs_score(shape, q, k, scale, scores, workspace, workspace_bytes=None, strea
         workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib().pbs_score(ctypes.byref(shape), _ptr(q), _ptr(k), scale, _ptr(scores),
                            _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def pbs_score_noalloc(shape, q, k, scale, scores, stream=None):
+    _check(lib().pbs_score_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), scale, _ptr(scores),
+                                   _stream(stream)))
 
 
 def pbs_permute(shape, scores, k, v, perm, k_perm, v_perm, k_pool=None, blk_minpos=None,

@@ -92,6 +92,7 @@ const char* pbs_strerror(int status) {
     case PBS_E_ALIGN: return "pointer not 16-byte aligned";
     case PBS_E_WORKSPACE: return "workspace too small";
     case PBS_E_LAUNCH: return "kernel launch failed";
+    case PBS_E_SCRATCH: return "problem larger than the static scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -164,6 +165,22 @@ extern "C" {
 int pbs_score(const pbs_shape* shape, const uint16_t* q, const uint16_t* k, float scale,
               float* scores, void* workspace, size_t workspace_bytes, void* stream) {
   return score_impl(shape, nullptr, 0, q, k, scale, scores, workspace, workspace_bytes, stream);
+}
+
+int pbs_score_noalloc(const pbs_shape* shape, const uint16_t* q, const uint16_t* k, float scale,
+                      float* scores, void* stream) {
+  Dims d;
+  int st = check_shape(shape, &d);
+  if (st != PBS_OK) return st;
+  if (!finite_positive(scale)) return PBS_E_ARG;
+  if (empty(d)) return PBS_OK;
+  const void* const req[] = {q, k, scores};
+  if ((st = check_required(req)) != PBS_OK) return st;
+  if (pbs::score_workspace_bytes(d) > pbs::kNoAllocScratchBytes) return PBS_E_SCRATCH;
+  void* ws = nullptr;
+  if (pbs::score_noalloc_scratch(&ws) != hipSuccess) return PBS_E_LAUNCH;
+  return status_of(pbs::launch_score(d, q, k, scale, scores, ws, nullptr, 0,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int pbs_score_varlen(const pbs_shape* shape, const int32_t* cu_seqlens, int32_t n_seqs,

@@ -43,6 +43,10 @@ inline hipError_t launch(void (*kernel)(Args), dim3 grid, dim3 block, size_t shm
 
 // Workspace of pbs_score: per (batch, KV head, segment, scoring row) softmax max and sum.
 size_t score_workspace_bytes(const Dims& d);
+// pbs_score_noalloc: capacity of the library's static scratch and its address on the current
+// device (looked up on the first call per device, no allocation).
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(16) << 20;
+hipError_t score_noalloc_scratch(void** ptr);
 // cu / nseq: packed sequences (nseq + 1 starts along N) or null / 0 for one sequence per row.
 hipError_t launch_score(const Dims& d, const uint16_t* q, const uint16_t* k, float scale,
                         float* scores, void* ws, const int32_t* cu, int nseq,

@@ -24,6 +24,8 @@
 // that reach them apply the causal test.  Both passes run eight waves per workgroup: a stats
 // workgroup streams each K tile once for 256 scoring rows, a reduce workgroup stages each chunk
 // of rows once for 256 keys.
+#include <mutex>
+
 #include "pbs_device.h"
 #include "pbs_internal.h"
 
@@ -269,6 +271,31 @@ static int score_chunk(const Dims& d) {
   int c = d.S;
   while (c > 1024 && c % 2 == 0 && (c / 2) % kStatKeys == 0) c /= 2;
   return c;
+}
+
+// Scratch of pbs_score_noalloc: the score partials live in this array instead of a caller's
+// workspace.  Every GPU the library runs on holds its own copy until the process ends; its device
+// address is looked up once per device (the array's name is only a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t score_noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 size_t score_workspace_bytes(const Dims& d) {

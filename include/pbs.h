@@ -65,7 +65,8 @@ typedef enum pbs_status {
   PBS_E_SHAPE = -2,     /* shape outside the supported set above                          */
   PBS_E_ALIGN = -3,     /* a pointer not 16-byte aligned                                  */
   PBS_E_WORKSPACE = -4, /* workspace smaller than pbs_workspace_bytes()                   */
-  PBS_E_LAUNCH = -5     /* the HIP runtime rejected a kernel launch                       */
+  PBS_E_LAUNCH = -5,    /* the HIP runtime rejected a kernel launch                       */
+  PBS_E_SCRATCH = -6    /* pbs_score_noalloc: the problem needs more than its static scratch */
 } pbs_status;
 
 typedef enum pbs_select_mode {
@@ -112,6 +113,27 @@ const char* pbs_strerror(int status);
  */
 int pbs_score(const pbs_shape* shape, const uint16_t* q, const uint16_t* k, float scale,
               float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pbs_score_noalloc -- pbs_score for callers that cannot allocate device memory (code recorded
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and the same result, bit for bit, with the score partials in a static scratch array
+ * of the library instead of a caller's workspace.
+ *   - The scratch holds PBS_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, a file-scope device array
+ *     that each GPU the library runs on keeps until the process ends; its device address is
+ *     looked up once per device, on the first call there.  No call allocates or frees memory.
+ *   - A shape whose score partials (68 bytes per scoring row and segment at S = 8192, Bs = 128)
+ *     do not fit returns PBS_E_SCRATCH before anything is enqueued; 32 query / 8 KV heads at
+ *     Bs = 128 and S = 8192 fit up to 480K tokens.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents:
+ *     calls that overlap on one GPU (different streams, or graphs replayed concurrently) race
+ *     and give unspecified scores.  Calls ordered on one stream are safe.  Nothing in the
+ *     scratch needs to start at zero.
+ * Arguments, outputs and errors otherwise as pbs_score.
+ */
+#define PBS_NOALLOC_SCRATCH_BYTES (16u << 20)
+int pbs_score_noalloc(const pbs_shape* shape, const uint16_t* q, const uint16_t* k, float scale,
+                      float* scores, void* stream);
 
 /*
  * pbs_permute -- segmented permutation of keys and values.

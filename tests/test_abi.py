@@ -107,6 +107,11 @@ def test_errors_before_any_launch():
     assert aq(None, fake) == P.PBS_E_ARG                         # the permutation is required
     assert aq(fake, None) == P.PBS_E_ARG                         # lists are required
     assert aq(fake, fake, minpos=fake + 4) == P.PBS_E_ALIGN
+    na = lambda shape, q: _call("pbs_score_noalloc", shape, q, fake, 0.1, fake, None)
+    assert na(S, None) == P.PBS_E_ARG
+    assert na(S, fake + 2) == P.PBS_E_ALIGN
+    # partials of 1M tokens (64 segments of 16384) exceed the static scratch: rejected on the host
+    assert na(ctypes.byref(P.make_shape(1, 32, 8, 1 << 20, 128, 128, 16384)), fake) == P.PBS_E_SCRATCH
     hyb = lambda kp, k, counts, lse=None: _call(
         "pbs_attn_fwd_hybrid", S, fake, kp, fake, k, fake, counts, fake, 0.1, fake, lse, None)
     assert hyb(fake, fake, None) == P.PBS_E_ARG                  # lists are required
@@ -151,7 +156,7 @@ def test_empty_problem_is_ok_without_pointers():
 
 
 def test_strerror():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert P.pbs_strerror(code)
     assert P.pbs_strerror(-99) == "unknown status"
 

@@ -17,13 +17,14 @@
 // Kernels:
 //  * pool: float32 mean of every block of Bs rows (queries; keys too when the caller has no
 //    pooled keys from pbs_permute).  HBM-bound, one workgroup per (head, block).
-//  * select: one workgroup per (query block, up to 4 query heads of one KV head), 256 threads per
-//    head.  Logits are plain fp32 dot products (n <= 8192 candidates x d), the softmax uses
-//    per-row reductions.  Keep ratio: the top-k set comes from a radix select over the ranking
-//    keys (no sort).  Coverage: the ranking is a bitonic sort of next_pow2(n) 64-bit keys in LDS
-//    and the coverage prefix is one strictly sequential fp32 sum (so it is bit-identical to any
-//    other sequential fp32 sum of the same values).  The kept blocks are compacted in ascending
-//    order with a per-row prefix scan.
+//  * select: one workgroup per (query block, up to 4 query heads of one KV head), one wave per
+//    head.  Logits are plain fp32 dot products (n <= 8192 candidates x d) computed by the whole
+//    workgroup, so each pooled key is read once for the group; after one barrier every row is
+//    its wave's own: softmax with wave reductions; keep ratio: the top-k set from a radix select
+//    over the ranking keys with a per-row histogram in LDS (no sort); coverage: a bitonic sort
+//    of next_pow2(n) 64-bit keys in LDS and one strictly sequential fp32 coverage sum (so it is
+//    bit-identical to any other sequential fp32 sum of the same values); the kept blocks are
+//    compacted in ascending order with a wave scan.  No workgroup barrier after the logits.
 #include <cmath>
 
 #include "pbs_device.h"
@@ -53,9 +54,14 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   float sum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sum[e] = 0.f;
-#pragma unroll 4
-  for (int r = rg; r < BS; r += RP) {
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(x0 + static_cast<size_t>(r) * rs);
+  // every row load of the thread in flight at once (BS / RP of them)
+  u32x4 rows[BS / RP];
+#pragma unroll
+  for (int q = 0; q < BS / RP; ++q)
+    rows[q] = *reinterpret_cast<const u32x4*>(x0 + static_cast<size_t>(rg + q * RP) * rs);
+#pragma unroll
+  for (int q = 0; q < BS / RP; ++q) {
+    const u32x4 xv = rows[q];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       sum[2 * e] += __uint_as_float(xv[e] << 16);
@@ -89,63 +95,92 @@ struct SelArgs {
   float scale;
 };
 
-constexpr int kSub = 256;   // threads per row (one row = one query head of the workgroup)
-static_assert(kSub == 256, "the radix select keeps one 8-bit histogram bin per thread of a row");
-
-// Sum / max over the kSub threads of one row (sub = the row's index in the workgroup).  Every thread
-// of the workgroup calls these together.
-__device__ __forceinline__ float row_reduce_max(float v, float* red, int sub, int st) {
-  v = wave_max(v);
-  __syncthreads();
-  if ((st & 63) == 0) red[sub * 4 + (st >> 6)] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(red[sub * 4], red[sub * 4 + 1]), fmaxf(red[sub * 4 + 2], red[sub * 4 + 3]));
-}
-__device__ __forceinline__ float row_reduce_sum(float v, float* red, int sub, int st) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((st & 63) == 0) red[sub * 4 + (st >> 6)] = v;
-  __syncthreads();
-  return (red[sub * 4] + red[sub * 4 + 1]) + (red[sub * 4 + 2] + red[sub * 4 + 3]);
+// Synchronisation of the lanes of one wave around its LDS work: the LDS executes a wave's
+// instructions in order, so only the compiler has to be kept from moving memory operations across
+// this point (no hardware barrier is involved).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Ascending bitonic sort of n2 (power of two) 64-bit keys by the kSub threads of one row; every
-// thread of the workgroup takes part in the barriers.
-__device__ __forceinline__ void bitonic_sort_row(uint64_t* keys, int n2, int st) {
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      for (int t = st; t < (n2 >> 1); t += kSub) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        const uint64_t x = keys[lo], y = keys[hi];
-        if ((x > y) == up) {
-          keys[lo] = y;
-          keys[hi] = x;
-        }
-      }
-    }
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan_incl(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  __syncthreads();
+  return x;
 }
 
-// One workgroup per (query block, group of hpw query heads sharing a KV head); kSub threads per
-// head.  The heads of a group have the same candidates, so their logits read each pooled key once
-// (through the cache) and their sorts run side by side.
-template <int D>
-__global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ float red[4 * 4];
-  __shared__ int32_t scan[4 * kSub];
-  __shared__ int32_t kept[4];
+// One chunk of the coverage sum: c runs through the chunk's 64 ranked values (staged in LDS by
+// lane) one float32 addition at a time, strictly sequentially, every lane doing the same uniform
+// work; returns the position (0..63) of the first value at which the running sum reaches tf, or
+// -1, and leaves c at the sum after all 64 (values past the end of the row are +0).
+__device__ __forceinline__ int seq_sum64(float& c, float pv, float* stage, int lane, float tf) {
+  stage[lane] = pv;
+  wave_sync();
+  int first = -1;
+#pragma unroll
+  for (int e4 = 0; e4 < 16; ++e4) {
+    const float4 v = reinterpret_cast<const float4*>(stage)[e4];
+    c = __fadd_rn(c, v.x);
+    first = (first < 0 && c >= tf) ? 4 * e4 : first;
+    c = __fadd_rn(c, v.y);
+    first = (first < 0 && c >= tf) ? 4 * e4 + 1 : first;
+    c = __fadd_rn(c, v.z);
+    first = (first < 0 && c >= tf) ? 4 * e4 + 2 : first;
+    c = __fadd_rn(c, v.w);
+    first = (first < 0 && c >= tf) ? 4 * e4 + 3 : first;
+  }
+  wave_sync();   // the stage is refilled by the next chunk
+  return first;
+}
 
+// Per-row LDS of the select kernel (one wave per row), carved from the dynamic LDS: the ranking
+// keys (64-bit for the coverage sort, their 32-bit top words for the keep-ratio select), the
+// probabilities, the kept flags and a 256-bin histogram.
+struct RowLds {
+  uint64_t* keys;   // n2max entries (coverage) / n2max 32-bit words (keep ratio)
+  float* P;         // n2max
+  uint8_t* flag;    // n2max
+  int32_t* hist;    // 256
+};
+
+__host__ __device__ inline size_t row_lds_bytes(int n2max, int mode) {
+  const size_t key_bytes = (mode == 0 ? 4u : 8u) * static_cast<size_t>(n2max);
+  return (key_bytes + 4u * n2max + n2max + 256u * 4u + 15u) & ~static_cast<size_t>(15);
+}
+
+__device__ __forceinline__ RowLds row_lds(unsigned char* base, int n2max, int mode, int r) {
+  unsigned char* p = base + static_cast<size_t>(r) * row_lds_bytes(n2max, mode);
+  RowLds L;
+  L.keys = reinterpret_cast<uint64_t*>(p);
+  p += (mode == 0 ? 4u : 8u) * static_cast<size_t>(n2max);
+  L.hist = reinterpret_cast<int32_t*>(p);
+  p += 256u * 4u;
+  L.P = reinterpret_cast<float*>(p);
+  p += 4u * n2max;
+  L.flag = p;
+  return L;
+}
+
+// One workgroup per (query block, group of hpw query heads sharing a KV head), one wave per head
+// (row).  The heads of a group have the same candidates, so their logits are computed together
+// (each pooled key is read once per workgroup); everything after that is the wave's own work on
+// its row: softmax, ranking and compaction with wave reductions and scans, with no workgroup
+// barrier.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x;
-  const int sub = tid / kSub, st = tid - sub * kSub;
+  const int sub = tid >> 6, lane = tid & 63;   // row of the workgroup, lane of its wave
   const int i = blockIdx.x;
   const int groups = a.Hq / a.hpw;
   const int b = blockIdx.y / groups;
-  const int g = (blockIdx.y - b * groups) * a.hpw + sub;   // this row's query head
+  const int g0 = (blockIdx.y - b * groups) * a.hpw;
+  const int g = g0 + sub;                      // this row's query head
   const int h = g / a.G;
   // candidates: the blocks of earlier segments of the query block's own sequence
   const int seg_first = (i / a.bps) * a.bps;
@@ -155,33 +190,31 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const int n = seg_first - first;                    // candidates first .. seg_first - 1
   int n2 = 1;
   while (n2 < n) n2 <<= 1;
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem) + static_cast<size_t>(sub) * a.n2max;
-  float* Ps = reinterpret_cast<float*>(reinterpret_cast<uint64_t*>(smem) + static_cast<size_t>(a.hpw) * a.n2max) +
-              static_cast<size_t>(sub) * a.n2max;
-  int32_t* flag = reinterpret_cast<int32_t*>(Ps + static_cast<size_t>(a.hpw - sub) * a.n2max) +
-                  static_cast<size_t>(sub) * a.n2max;
+  const RowLds L = row_lds(smem, a.n2max, MODE, sub);
   const size_t row = (static_cast<size_t>(b) * a.Hq + g) * a.nb + i;
   float* prow = a.P ? a.P + row * a.nb : nullptr;
 
   if (n == 0) {   // the whole workgroup takes this branch (n depends on the query block only)
-    if (st == 0) a.counts[row] = 0;
+    if (lane == 0) a.counts[row] = 0;
     if (prow && !a.p_in)
-      for (int j = st; j < a.nb; j += kSub) prow[j] = 0.f;
+      for (int j = lane; j < a.nb; j += 64) prow[j] = 0.f;
     return;
   }
 
   if (a.p_in) {
-    for (int j = st; j < n; j += kSub) Ps[j] = prow[first + j];
-    __syncthreads();
+    for (int j = lane; j < n; j += 64) L.P[j] = prow[first + j];
+    wave_sync();
   } else {
-    // Logits of all hpw rows: TPC threads per candidate, each with an 8-wide slice of the head
-    // dimension (the rows' pooled queries in registers), so a wave reads whole pooled-key rows
-    // contiguously; the slices are summed across the TPC lanes.
+    // Logits of all hpw rows.  A group of TPC lanes holds the rows' pooled queries in 8-wide
+    // slices of the head dimension and takes TPC candidates at a time: every lane forms the
+    // partial dot products of its slice with each candidate (each candidate row is read by the
+    // group as one contiguous run), then a transposing butterfly over the group sums them so that
+    // lane sl ends with the full logits of candidate sl (one exchange per dot product instead of
+    // log2(TPC)).
     constexpr int TPC = D / 8;
-    const int nt = kSub * a.hpw;
-    const int cpi = nt / TPC;                   // candidates per sweep
-    const int sl = tid % TPC, cj = tid / TPC;
-    const size_t row0 = (static_cast<size_t>(b) * a.Hq + (g - sub)) * a.nb + i;   // first row
+    const int nt = 64 * a.hpw;
+    const int sl = tid % TPC, grp = tid / TPC;
+    const size_t row0 = (static_cast<size_t>(b) * a.Hq + g0) * a.nb + i;   // first row
     float qv[4][8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -190,185 +223,175 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
         const float4 x0 = qp[0], x1 = qp[1];
         qv[r][0] = x0.x; qv[r][1] = x0.y; qv[r][2] = x0.z; qv[r][3] = x0.w;
         qv[r][4] = x1.x; qv[r][5] = x1.y; qv[r][6] = x1.z; qv[r][7] = x1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[r][e] = 0.f;
       }
     }
     const float* kb = a.kbar + ((static_cast<size_t>(b) * a.Hkv + h) * a.nb + first) * D;
-    float* Pall = reinterpret_cast<float*>(reinterpret_cast<uint64_t*>(smem) + static_cast<size_t>(a.hpw) * a.n2max);
-#pragma unroll 2
-    for (int j0 = 0; j0 < n; j0 += cpi) {
-      const int j = j0 + cj;
-      float4 k0 = make_float4(0.f, 0.f, 0.f, 0.f), k1 = k0;
-      if (j < n) {
+    for (int j0 = grp * TPC; j0 < n; j0 += nt) {
+      float part[4][TPC];
+#pragma unroll
+      for (int c = 0; c < TPC; ++c) {
+        const int j = min(j0 + c, n - 1);
         const float4* kp = reinterpret_cast<const float4*>(kb + static_cast<size_t>(j) * D + sl * 8);
-        k0 = kp[0];
-        k1 = kp[1];
+        const float4 k0 = kp[0], k1 = kp[1];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          part[r][c] = qv[r][0] * k0.x + qv[r][1] * k0.y + qv[r][2] * k0.z + qv[r][3] * k0.w +
+                       qv[r][4] * k1.x + qv[r][5] * k1.y + qv[r][6] * k1.z + qv[r][7] * k1.w;
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (r < a.hpw) {
-          float acc = qv[r][0] * k0.x + qv[r][1] * k0.y + qv[r][2] * k0.z + qv[r][3] * k0.w +
-                      qv[r][4] * k1.x + qv[r][5] * k1.y + qv[r][6] * k1.z + qv[r][7] * k1.w;
+      for (int hw = TPC / 2; hw >= 1; hw >>= 1) {
+        const bool upper = (sl & hw) != 0;
 #pragma unroll
-          for (int o = 1; o < TPC; o <<= 1) acc += __shfl_xor(acc, o);
-          if (sl == 0 && j < n) Pall[static_cast<size_t>(r) * a.n2max + j] = acc * a.scale;
-        }
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < hw; ++c) {
+            const float send = upper ? part[r][c] : part[r][c + hw];
+            const float keep = upper ? part[r][c + hw] : part[r][c];
+            part[r][c] = keep + __shfl_xor(send, hw);
+          }
       }
+      const int j = j0 + sl;
+      if (j < n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (r < a.hpw) row_lds(smem, a.n2max, MODE, r).P[j] = part[r][0] * a.scale;
     }
-    __syncthreads();
+    __syncthreads();   // the only workgroup barrier: every row's logits are in place
+    // softmax of this row (wave reductions)
     float lmax = -INFINITY;
-    for (int j = st; j < n; j += kSub) lmax = fmaxf(lmax, Ps[j]);
-    const float mx = row_reduce_max(lmax, red, sub, st);
+    for (int j = lane; j < n; j += 64) lmax = fmaxf(lmax, L.P[j]);
+    const float mx = wave_max(lmax);
     float lsum = 0.f;
-    for (int j = st; j < n; j += kSub) {
-      const float e = __expf(Ps[j] - mx);
-      Ps[j] = e;
+    for (int j = lane; j < n; j += 64) {
+      const float e = __expf(L.P[j] - mx);
+      L.P[j] = e;
       lsum += e;
     }
-    const float tot = row_reduce_sum(lsum, red, sub, st);
-    const float inv = 1.f / tot;
-    for (int j = st; j < n; j += kSub) {
-      const float p = Ps[j] * inv;
-      Ps[j] = p;
+    const float inv = 1.f / wave_sum(lsum);
+    for (int j = lane; j < n; j += 64) {
+      const float p = L.P[j] * inv;
+      L.P[j] = p;
       if (prow) prow[first + j] = p;
     }
     if (prow)
-      for (int j = st; j < a.nb; j += kSub)
+      for (int j = lane; j < a.nb; j += 64)
         if (j < first || j >= seg_first) prow[j] = 0.f;
-    __syncthreads();
+    wave_sync();
   }
 
-  // Rank keys: (descending P, ascending block) as one ascending 64-bit key whose top word is the
-  // complemented orderable value of P and whose low word is the block; with keep_first, block 0
-  // gets key 0, below every real key (whose top word is never 0).
-  if (a.mode == 0) {
+  // Ranking keys: (descending P, ascending block) as one ascending 64-bit key whose top word is
+  // the complemented orderable value of P and whose low word is the block; with keep_first,
+  // block 0 gets key 0, below every real key (whose top word is never 0).
+  int kk;
+  if constexpr (MODE == 0) {
     // Keep ratio: the kk lowest keys, found without sorting.  A radix select over the top words
-    // (4 passes of 8 bits, per-row histograms in LDS) finds the kk-th lowest top word H and how
-    // many keys with top word H belong to the kept set; those are the lowest blocks among the keys
-    // equal to H (the low word is the block), taken by an exclusive scan in block order.  The kept
+    // (4 passes of 8 bits, a 256-bin histogram per row in LDS) finds the kk-th lowest top word H
+    // and how many keys with top word H belong to the kept set; those are the lowest blocks among
+    // the keys equal to H (the low word is the block), taken by a scan in block order.  The kept
     // set is exactly the first kk of the full ranking.
-    uint32_t* hi = reinterpret_cast<uint32_t*>(keys);
-    for (int p = st; p < n; p += kSub)
-      hi[p] = (a.keep_first && p == 0) ? 0u
-                                       : static_cast<uint32_t>(desc_sort_key(Ps[p], 0u) >> 32);
-    const int kk = max(1, min(static_cast<int>(floor(a.param * static_cast<double>(n))), n));
-    int32_t* hist = scan + sub * kSub;      // 256 bins per row (kSub == 256)
+    uint32_t* hi = reinterpret_cast<uint32_t*>(L.keys);
+    for (int p = lane; p < n; p += 64)
+      hi[p] = (a.keep_first && p == 0) ? 0u : static_cast<uint32_t>(desc_sort_key(L.P[p], 0u) >> 32);
+    kk = max(1, min(static_cast<int>(floor(a.param * static_cast<double>(n))), n));
     uint32_t prefix = 0, pmask = 0;
     int need = kk;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[st] = 0;
-      __syncthreads();
-      for (int p = st; p < n; p += kSub) {
+      L.hist[4 * lane] = 0;
+      L.hist[4 * lane + 1] = 0;
+      L.hist[4 * lane + 2] = 0;
+      L.hist[4 * lane + 3] = 0;
+      wave_sync();
+      for (int p = lane; p < n; p += 64) {
         const uint32_t x = hi[p];
-        if ((x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1);
+        if ((x & pmask) == prefix) atomicAdd(&L.hist[(x >> shift) & 255u], 1);
       }
-      __syncthreads();
-      if (st < 64) {   // the row's first wave finds the digit where the running count reaches need
-        const int c0 = hist[4 * st], c1 = hist[4 * st + 1], c2 = hist[4 * st + 2], c3 = hist[4 * st + 3];
-        const int mine = c0 + c1 + c2 + c3;
-        int incl = mine;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o);
-          if (st >= o) incl += y;
-        }
-        const int excl = incl - mine;
-        if (excl < need && need <= incl) {   // exactly one lane
-          int dgt = 4 * st, below = excl;
-          if (below + c0 < need) { below += c0; ++dgt;
-            if (below + c1 < need) { below += c1; ++dgt;
-              if (below + c2 < need) { below += c2; ++dgt; } } }
-          red[sub * 4] = __int_as_float(dgt);
-          red[sub * 4 + 1] = __int_as_float(need - below);
-        }
-      }
-      __syncthreads();
-      prefix |= static_cast<uint32_t>(__float_as_int(red[sub * 4])) << shift;
+      wave_sync();
+      const int c0 = L.hist[4 * lane], c1 = L.hist[4 * lane + 1], c2 = L.hist[4 * lane + 2],
+                c3 = L.hist[4 * lane + 3];
+      const int mine = c0 + c1 + c2 + c3;
+      const int incl = wave_scan_incl(mine, lane);
+      const int excl = incl - mine;
+      // the lane whose four bins hold the need-th key: its digit and the count below it
+      int dgt = 4 * lane, below = excl;
+      if (below + c0 < need) { below += c0; ++dgt;
+        if (below + c1 < need) { below += c1; ++dgt;
+          if (below + c2 < need) { below += c2; ++dgt; } } }
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(excl < need && need <= incl);
+      const int src = __builtin_ctzll(bal);
+      dgt = __shfl(dgt, src);
+      below = __shfl(below, src);
+      prefix |= static_cast<uint32_t>(dgt) << shift;
       pmask |= 0xffu << shift;
-      need = __float_as_int(red[sub * 4 + 1]);
-      __syncthreads();
+      need -= below;
+      wave_sync();   // the histogram is reset by the next pass
     }
     // keep every key below H and the first `need` keys equal to H in block order
     const uint32_t H = prefix;
-    const int per = (n + kSub - 1) / kSub;
-    const int lo = min(st * per, n), hi_end = min(lo + per, n);
+    const int per = (n + 63) / 64;
+    const int lo = min(lane * per, n), hend = min(lo + per, n);
     int eq = 0;
-    for (int j = lo; j < hi_end; ++j) eq += (hi[j] == H);
-    hist[st] = eq;
-    __syncthreads();
-    for (int off = 1; off < kSub; off <<= 1) {
-      const int vv = (st >= off) ? hist[st - off] : 0;
-      __syncthreads();
-      hist[st] += vv;
-      __syncthreads();
-    }
-    int rank = hist[st] - eq;
-    for (int j = lo; j < hi_end; ++j) {
+    for (int j = lo; j < hend; ++j) eq += (hi[j] == H);
+    int rank = wave_scan_incl(eq, lane) - eq;
+    for (int j = lo; j < hend; ++j) {
       const uint32_t x = hi[j];
-      flag[j] = (x < H || (x == H && rank++ < need)) ? 1 : 0;
+      L.flag[j] = (x < H || (x == H && rank++ < need)) ? 1 : 0;
     }
-    if (st == 0) kept[sub] = kk;
-    __syncthreads();
+    wave_sync();
   } else {
-    for (int p = st; p < n2; p += kSub)
-      keys[p] = (p < n) ? ((a.keep_first && p == 0) ? 0ull : desc_sort_key(Ps[p], static_cast<uint32_t>(p)))
-                        : ~0ull;
-    bitonic_sort_row(keys, n2, st);
-  }
-
-  if (a.mode == 0) {
-    // flags are set
-  } else if (st < 64) {
-    // Shortest prefix of the ranking whose running float32 sum reaches tau: the sum is strictly
-    // sequential (one rounding per element, in ranking order); the first wave of the row gathers
-    // 64 ranked values at a time and adds them one by one from the lanes.  (double)c >= tau is
-    // tested as c >= tf, tf the least float with (double)tf >= tau.
+    // Coverage: the ranking as a bitonic sort of next_pow2(n) 64-bit keys in LDS by the row's
+    // wave, then the shortest prefix whose running float32 sum reaches tau.  The sum is strictly
+    // sequential (one rounding per element, in ranking order), 64 ranked values at a time.
+    // (double)c >= tau is tested as c >= tf, tf the least float with (double)tf >= tau.
     const float tf = a.tau_f;
     float c = 0.f;
-    int kk = n;
-    for (int m0 = 0; m0 < n; m0 += 64) {
-      const int m = m0 + st;
-      const float pv = (m < n) ? Ps[static_cast<int>(keys[m] & 0xffffffffull)] : 0.f;
-      const int cnt = min(64, n - m0);
-      int e = 0;
-      for (; e < cnt; ++e) {
-        c = __fadd_rn(c, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pv), e)));
-        if (c >= tf) break;
+    kk = n;
+    for (int p = lane; p < n2; p += 64)
+      L.keys[p] = (p < n) ? ((a.keep_first && p == 0) ? 0ull : desc_sort_key(L.P[p], static_cast<uint32_t>(p)))
+                          : ~0ull;
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        wave_sync();
+        for (int t = lane; t < (n2 >> 1); t += 64) {
+          const int lo = 2 * t - (t & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = ((lo & size) == 0);
+          const uint64_t x = L.keys[lo], y = L.keys[hi];
+          if ((x > y) == up) {
+            L.keys[lo] = y;
+            L.keys[hi] = x;
+          }
+        }
       }
-      if (e < cnt) {
-        kk = m0 + e + 1;
+    }
+    wave_sync();
+    for (int m0 = 0; m0 < n; m0 += 64) {
+      const int m = m0 + lane;
+      const float pv = (m < n) ? L.P[static_cast<int>(L.keys[m] & 0xffffffffull)] : 0.f;
+      const int hit = seq_sum64(c, pv, reinterpret_cast<float*>(L.hist), lane, tf);
+      if (hit >= 0 && m0 + hit < n) {
+        kk = m0 + hit + 1;
         break;
       }
     }
-    if (st == 0) kept[sub] = kk;
+    for (int j = lane; j < n; j += 64) L.flag[j] = 0;
+    wave_sync();
+    for (int m = lane; m < kk; m += 64) L.flag[static_cast<int>(L.keys[m] & 0xffffffffull)] = 1;
+    wave_sync();
   }
-  if (a.mode != 0) {
-    for (int j = st; j < n; j += kSub) flag[j] = 0;
-    __syncthreads();   // also publishes kept[sub] from the coverage scan
-    const int kc = kept[sub];
-    for (int m = st; m < kc; m += kSub) flag[static_cast<int>(keys[m] & 0xffffffffull)] = 1;
-    __syncthreads();
-  }
-  const int kk = kept[sub];
 
-  // ascending compaction: thread st of the row owns candidates [st*per, (st+1)*per)
-  const int per = (n + kSub - 1) / kSub;
-  const int lo = min(st * per, n), hi = min(lo + per, n);
+  // ascending compaction: lane l of the row owns candidates [l*per, (l+1)*per)
+  const int per = (n + 63) / 64;
+  const int lo = min(lane * per, n), hend = min(lo + per, n);
   int cnt = 0;
-  for (int j = lo; j < hi; ++j) cnt += flag[j];
-  int32_t* sc = scan + sub * kSub;
-  sc[st] = cnt;
-  __syncthreads();
-  for (int off = 1; off < kSub; off <<= 1) {
-    const int v = (st >= off) ? sc[st - off] : 0;
-    __syncthreads();
-    sc[st] += v;
-    __syncthreads();
-  }
-  int pos = sc[st] - cnt;
+  for (int j = lo; j < hend; ++j) cnt += L.flag[j];
+  int pos = wave_scan_incl(cnt, lane) - cnt;
   int32_t* out = a.idx + row * a.max_off;
-  for (int j = lo; j < hi; ++j)
-    if (flag[j]) out[pos++] = first + j;
-  if (st == 0) a.counts[row] = kk;
+  for (int j = lo; j < hend; ++j)
+    if (L.flag[j]) out[pos++] = first + j;
+  if (lane == 0) a.counts[row] = kk;
 }
 
 template <int D, int BS>
@@ -423,9 +446,9 @@ hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t*
   int n2 = 1;
   while (n2 < d.max_off) n2 <<= 1;
   sa.n2max = n2;
-  // Heads per workgroup: the largest of 4, 2, 1 that divides the group size and keeps the
-  // workgroup's LDS within 64 KiB (two workgroups per CU).
-  const size_t per_row = static_cast<size_t>(n2) * (sizeof(uint64_t) + sizeof(float) + sizeof(int32_t));
+  // Heads per workgroup (one wave each): the largest of 4, 2, 1 that divides the group size and
+  // keeps the workgroup's LDS within 64 KiB (at least two workgroups per CU).
+  const size_t per_row = row_lds_bytes(n2, mode);
   int hpw = 4;
   while (hpw > 1 && (d.G % hpw != 0 || hpw * per_row > 65536)) hpw >>= 1;
   sa.hpw = hpw;
@@ -435,11 +458,12 @@ hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t*
   sa.tau_f = static_cast<float>(param);
   if (static_cast<double>(sa.tau_f) < param) sa.tau_f = std::nextafter(sa.tau_f, INFINITY);
   const size_t shmem = hpw * per_row;
-  auto kern = d.d == 128 ? select_kernel<128> : select_kernel<64>;
+  auto kern = d.d == 128 ? (mode == 0 ? select_kernel<128, 0> : select_kernel<128, 1>)
+                         : (mode == 0 ? select_kernel<64, 0> : select_kernel<64, 1>);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
   if (e != hipSuccess) return e;
-  return launch(kern, dim3(d.nb, d.B * (d.Hq / hpw)), dim3(kSub * hpw), shmem, stream, sa);
+  return launch(kern, dim3(d.nb, d.B * (d.Hq / hpw)), dim3(64 * hpw), shmem, stream, sa);
 }
 
 }  // namespace pbs

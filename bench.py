@@ -4,13 +4,16 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa_128k] [--keep R]
 
 One step is one PBS-Attn prefill of the whole workload: pbs_score -> pbs_permute ->
-pbs_block_select -> pbs_attn_fwd on one stream, inputs already resident in HBM.  The default
-workload is the 128K-token GQA layer (1 x 32 query / 8 KV heads, d=128, block 128, segment
-8192, keep ratio 0.1) with synthetic planted-salient-key inputs.  Prints one JSON line:
-latency per prefill (the metric, lower is better), per-stage times from HIP events on the
-launch stream, effective TFLOP/s of the attention kernel on the blocks it computes, the dense
-causal baseline run by the same kernel, the attention kernel's roofline object and the CPU
-oracle timed on a bounded sample (extrapolated to a whole prefill).
+pbs_block_select -> pbs_attn_fwd on one stream, inputs already resident in HBM, L2 and MALL
+evicted before every timed step by a 512 MiB write outside the timed region (mean, median and
+min reported).  The default workload is the 128K-token GQA layer (1 x 32 query / 8 KV heads,
+d=128, block 128, segment 8192, keep ratio 0.1) with synthetic planted-salient-key inputs.
+Prints one JSON line: latency per prefill (the metric, lower is better), per-stage times from
+HIP events on the launch stream, effective TFLOP/s of the attention kernel on the blocks it
+computes, the dense causal baseline run by the same kernel, the attention kernel's roofline
+object, the other synthetic workloads timed the same way (configs), and the CPU oracle timed
+on a bounded sample of the 128K workload (extrapolated to a whole prefill) and in full on the
+two smallest workloads.
 """
 from __future__ import annotations
 
@@ -87,6 +90,191 @@ def read_traffic(workload: str):
         return None
 
 
+FLUSH_BYTES = 512 << 20
+
+
+class Flusher:
+    """Writes 512 MiB of device memory (more than the 8 x 4 MiB of L2 and the 256 MiB of MALL)
+    on the current stream, so that the call timed next starts with cold caches: a prefill is a
+    one-shot pass over its inputs."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n & 0xff)
+
+
+def stats(xs) -> dict:
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 4), "median": round(float(np.median(a)), 4),
+            "min": round(float(a.min()), 4), "max": round(float(a.max()), 4), "n": int(a.size)}
+
+
+def time_calls(fn, steps: int, warmup: int, flush, stream) -> list:
+    """Event time (ms) of each of `steps` calls of fn on `stream`, every call preceded by a cache
+    flush outside the events, after `warmup` untimed calls."""
+    import torch
+    for _ in range(warmup):
+        flush()
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = []
+    for _ in range(steps):
+        flush()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+def measure_configs(args, flush, stream, dev, skip: str) -> dict:
+    """Prefill (the four calls) and dense causal attention on every other configured workload,
+    at each of its evaluation parameters, timed like the headline: per-step hipEvents after a
+    cache flush.  Steps: min(--steps, 10) after 2 warm-ups."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_pbs_amd as P
+    import pbs_synth
+    steps = max(1, min(args.steps, 10))
+    out = {}
+    for name, w in pbs_synth.WORKLOADS.items():
+        if name == skip:
+            continue
+        inp = pbs_synth.make_inputs(w)
+        q, k, v = [torch.from_numpy(inp[x].view(np.int16)).view(torch.bfloat16).to(dev)
+                   for x in ("q", "k", "v")]
+        del inp
+        sh = P.shape_of(q, k, w.block, w.segment)
+        scale = P.default_scale(w.head_dim)
+        bf = P.Buffers(sh, dev)
+        B, Hq, Hkv, N, d, Bs, S = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment
+        nb, G = N // Bs, Hq // Hkv
+        flop_per_block = 4.0 * Bs * Bs * d
+        dense_blocks = B * Hq * nb * (nb + 1) // 2
+        od = torch.empty_like(q)
+        dense = stats(time_calls(lambda: P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale,
+                                                        od, None, stream=stream), steps, 2, flush, stream))
+        mode = P.PBS_SELECT_KEEP_RATIO if w.mode == "keep" else P.PBS_SELECT_COVERAGE
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        points = []
+        for param in w.params:
+            def run(record):
+                if record:
+                    ev[0].record(stream)
+                P.pbs_score(sh, q, k, scale, bf.scores, bf.workspace, stream=stream)
+                P.pbs_permute(sh, bf.scores, k, v, bf.perm, bf.k_perm, bf.v_perm, bf.k_pool,
+                              bf.blk_minpos, bf.perm_inv, stream=stream)
+                P.pbs_block_select(sh, q, bf.k_perm, bf.k_pool, scale, mode, param, None, 0,
+                                   bf.counts, bf.idx, bf.workspace, stream=stream)
+                if record:
+                    ev[1].record(stream)
+                P.pbs_attn_fwd(sh, q, bf.k_perm, bf.v_perm, bf.perm, bf.perm_inv, bf.counts,
+                               bf.idx, scale, bf.o, bf.lse, stream=stream)
+                if record:
+                    ev[2].record(stream)
+            for _ in range(2):
+                flush()
+                run(False)
+            torch.cuda.synchronize()
+            pre, att = [], []
+            for _ in range(steps):
+                flush()
+                run(True)
+                ev[2].synchronize()
+                pre.append(ev[0].elapsed_time(ev[1]))
+                att.append(ev[1].elapsed_time(ev[2]))
+            prefill = stats(np.array(pre) + np.array(att))
+            computed = int(bf.counts.sum().item()) + own_segment_blocks(bf.perm.cpu().numpy(), Bs, S, G)
+            att_mean = float(np.mean(att))
+            tflops = computed * flop_per_block / (att_mean * 1e-3) / 1e12
+            points.append({
+                "mode": w.mode, "param": param,
+                "prefill_ms": prefill, "attention_ms_mean": round(att_mean, 4),
+                "score_permute_select_ms_mean": round(float(np.mean(pre)), 4),
+                "speedup_vs_dense_median": round(dense["median"] / prefill["median"], 3),
+                "computed_blocks": round(computed, 3), "dense_blocks": dense_blocks,
+                "effective_tflops_computed_blocks": round(tflops, 1),
+                "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4)})
+            print(f"[bench] config {name} {w.mode}={param}: prefill median {prefill['median']:.4f} ms, "
+                  f"dense median {dense['median']:.4f} ms", file=sys.stderr, flush=True)
+        out[name] = {"shape": f"B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} block={Bs} segment={S}",
+                     "dense_causal_ms": dense,
+                     "dense_causal_tflops": round(dense_blocks * flop_per_block / (dense["mean"] * 1e-3) / 1e12, 1),
+                     "points": points}
+        del bf, q, k, v, od
+        torch.cuda.empty_cache()
+    return out
+
+
+def host_description() -> dict:
+    """The host the oracle runs on: CPU model, the cores this process may use, and the threads the
+    numpy BLAS library actually runs with (the oracle's matrix products)."""
+    import numpy as np
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        import threadpoolctl
+        np.ones(2) @ np.ones(2)
+        for info in threadpoolctl.threadpool_info():
+            if info.get("user_api") == "blas":
+                blas = int(info["num_threads"])
+                break
+    except Exception:   # threadpoolctl missing or unable to inspect the library
+        blas = None
+    nproc = len(os.sched_getaffinity(0))
+    return {"cpu_model": model, "nproc": nproc, "blas_threads": blas if blas else nproc,
+            "blas_threads_source": "threadpoolctl" if blas else "nproc"}
+
+
+def oracle_full_seconds(name: str) -> dict:
+    """Wall seconds of the whole oracle prefill (scores, permutation, block probabilities,
+    selection, attention of every row) and of the oracle's dense causal attention on a workload,
+    at each of its evaluation parameters."""
+    import oracle
+    import pbs_synth
+    w = pbs_synth.WORKLOADS[name]
+    inp = pbs_synth.make_inputs(w)
+    scale = oracle.default_scale(w.head_dim)
+    mode = oracle.KEEP if w.mode == "keep" else oracle.COVERAGE
+    out = {}
+    for param in w.params:
+        t = time.perf_counter()
+        oracle.prefill(inp["q"], inp["k"], inp["v"], block=w.block, segment=w.segment, scale=scale,
+                       mode=mode, param=param)
+        out[f"{w.mode}={param}"] = round(time.perf_counter() - t, 3)
+    t = time.perf_counter()
+    oracle.dense_causal(inp["q"], inp["k"], inp["v"], block=w.block, scale=scale)
+    out["dense_causal"] = round(time.perf_counter() - t, 3)
+    return out
+
+
+def cpu_full_main(args):
+    """The whole oracle, timed on every workload but the 128K one (minutes of CPU work; the
+    128K workload's oracle is only sampled, in the bench line's cpu_baseline)."""
+    res = {"host": host_description(), "kind": "oracle", "unit": "s"}
+    for name in args.cpu_full.split(","):
+        print(f"[bench] full oracle on {name}", file=sys.stderr, flush=True)
+        res[name] = oracle_full_seconds(name)
+        print(json.dumps({name: res[name]}), file=sys.stderr, flush=True)
+    print(json.dumps({"cpu_full_oracle": res}), flush=True)
+
+
 def cpu_oracle_baseline(w, inp, scale, param):
     """The oracle as it stands, on a bounded sample of the workload, extrapolated to one whole
     prefill.  Sample: key scores (twice) and permutation for KV head 0, pooled block scores +
@@ -121,9 +309,15 @@ def cpu_oracle_baseline(w, inp, scale, param):
                      counts=counts, idx=idx, qblocks=sample)
     t_attn = time.perf_counter() - t
     total_s = (t_score + t_perm) * w.heads_kv + t_sel * w.heads_q + t_attn * (w.heads_q * nb / len(sample))
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    host = host_description()
+    # the whole oracle pipeline on the two smallest workloads (seconds of CPU work)
+    full = {}
+    for name in ("toy_1k", "gqa_8k"):
+        full[name] = oracle_full_seconds(name)
     return {
-        "value": total_s * 1e3, "unit": "ms", "cores": threads, "kind": "oracle",
+        "value": total_s * 1e3, "unit": "ms", "cores": host["blas_threads"], "kind": "oracle",
+        "host": host,
+        "full_oracle_prefill_s": full,
         "sample": (f"float64 numpy oracle on KV head 0 (scores, permutation), query heads 0..{nh - 1} "
                    f"(block scores, selection; attention on all {nb} query blocks of each); extrapolated x{w.heads_kv} / x{w.heads_q} / x{w.heads_q * nb / len(sample):.1f}; "
                    f"{time.perf_counter() - t_all:.1f} s of CPU work"),
@@ -332,6 +526,11 @@ def main():
                     help="skip the torch scaled_dot_product_attention reference")
     ap.add_argument("--no-gemm", action="store_true",
                     help="skip the hipBLASLt bf16 GEMM reference measurement")
+    ap.add_argument("--cpu-full", default=None,
+                    help="comma-separated workloads: time the whole CPU oracle on each (no GPU); "
+                         "one JSON line instead of the bench line")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other synthetic workloads (the configs object)")
     ap.add_argument("--no-hybrid", action="store_true",
                     help="skip timing pbs_attn_fwd_hybrid (own segment from the original K/V)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -348,6 +547,9 @@ def main():
     ap.add_argument("--k-boost", type=float, default=None,
                     help="density mode: override the planted salient-key boost (attention concentration)")
     args = ap.parse_args()
+    if args.cpu_full:
+        cpu_full_main(args)
+        return
     if args.sweep:
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)
@@ -417,20 +619,26 @@ def main():
         if record:
             ev[4].record(stream)
 
+    flush = Flusher(dev)
     for _ in range(args.warmup):
+        flush()
         step(False)
     torch.cuda.synchronize()
-    stage = np.zeros(4)
+    per_step = []   # [score, permute, select, attention] of every timed step
     t0 = time.perf_counter()
     for _ in range(args.steps):
+        flush()      # L2 and MALL evicted before every step, outside the events
         step(True)
         ev[4].synchronize()
-        stage += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+        per_step.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    stage /= args.steps
+    per_step = np.array(per_step)
+    stage = per_step.mean(axis=0)
+    prefill_steps = per_step.sum(axis=1)
     pbs_ms = float(stage.sum())
-    print(f"[bench] {w.name}: PBS prefill {pbs_ms:.3f} ms (wall {wall_ms:.3f} ms/step)", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: PBS prefill {pbs_ms:.3f} ms (wall {wall_ms:.3f} ms/step incl. the flush)",
+          file=sys.stderr, flush=True)
 
     # The same four calls recorded once in a HIP graph and replayed (the library only enqueues
     # kernels: no allocation, memset or synchronisation inside a call), timed the same way; the
@@ -454,15 +662,9 @@ def main():
         g.replay()
         torch.cuda.synchronize()
         same = bool(torch.equal(bf.o.view(torch.int16), o_eager.view(torch.int16)))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        tot = 0.0
-        for _ in range(args.steps):
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            e1.synchronize()
-            tot += e0.elapsed_time(e1)
-        graph = {"prefill_ms": round(tot / args.steps, 4), "output_bit_identical_to_eager": same}
+        gt = stats(time_calls(g.replay, args.steps, 1, flush, stream))
+        graph = {"prefill_ms": gt["mean"], "prefill_ms_median": gt["median"],
+                 "output_bit_identical_to_eager": same}
         del g, o_eager
 
     # Algorithmic work of the attention launch: 4*Bs^2*d flops per computed key block.
@@ -479,20 +681,14 @@ def main():
     eff_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
 
     dense_ms = None
+    dense_stats = None
     if not args.no_dense:
         o_dense = torch.empty_like(q)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(max(1, args.warmup)):
-            P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale, o_dense, None, stream=stream)
-        torch.cuda.synchronize()
-        tot = 0.0
-        for _ in range(args.steps):
-            e0.record(stream)
-            P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale, o_dense, None, stream=stream)
-            e1.record(stream)
-            e1.synchronize()
-            tot += e0.elapsed_time(e1)
-        dense_ms = tot / args.steps
+        dt = time_calls(lambda: P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale, o_dense,
+                                               None, stream=stream),
+                        args.steps, max(1, args.warmup), flush, stream)
+        dense_stats = stats(dt)
+        dense_ms = dense_stats["mean"]
         del o_dense
     dense_tflops = dense_blocks * flop_per_block / (dense_ms * 1e-3) / 1e12 if dense_ms else None
 
@@ -502,20 +698,10 @@ def main():
     hybrid = None
     if not args.no_hybrid:
         o_h = torch.empty_like(q)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(max(1, args.warmup)):
-            P.pbs_attn_fwd_hybrid(sh, q, bf.k_perm, bf.v_perm, k, v, bf.counts, bf.idx, scale, o_h,
-                                  None, stream=stream)
-        torch.cuda.synchronize()
-        tot = 0.0
-        for _ in range(args.steps):
-            e0.record(stream)
-            P.pbs_attn_fwd_hybrid(sh, q, bf.k_perm, bf.v_perm, k, v, bf.counts, bf.idx, scale, o_h,
-                                  None, stream=stream)
-            e1.record(stream)
-            e1.synchronize()
-            tot += e0.elapsed_time(e1)
-        h_ms = tot / args.steps
+        h_ms = stats(time_calls(lambda: P.pbs_attn_fwd_hybrid(sh, q, bf.k_perm, bf.v_perm, k, v,
+                                                               bf.counts, bf.idx, scale, o_h, None,
+                                                               stream=stream),
+                                args.steps, max(1, args.warmup), flush, stream))["mean"]
         own_nat = B * Hq * int((np.arange(nb) % bps + 1).sum())
         h_blocks = int(counts.sum()) + own_nat
         h_tflops = h_blocks * flop_per_block / (h_ms * 1e-3) / 1e12
@@ -554,10 +740,12 @@ def main():
                 eq[3].record(stream)
 
         for _ in range(max(1, args.warmup)):
+            flush()
             qstep(False)
         torch.cuda.synchronize()
         qt = np.zeros(3)
         for _ in range(args.steps):
+            flush()
             qstep(True)
             eq[3].synchronize()
             qt += [eq[j].elapsed_time(eq[j + 1]) for j in range(3)]
@@ -626,6 +814,11 @@ def main():
         except Exception as ex:   # backend missing on this build of torch
             sdpa = {"unavailable": str(ex)[:200]}
 
+    # The other synthetic workloads, each timed the same way (prefill and dense causal).
+    configs = None
+    if not args.no_configs:
+        configs = measure_configs(args, flush, stream, dev, skip=w.name)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -670,6 +863,14 @@ def main():
         "dense_causal_tflops": round(dense_tflops, 1) if dense_tflops else None,
         "speedup_vs_dense": round(dense_ms / pbs_ms, 3) if dense_ms else None,
         "non_attention_frac": round(float(stage[:3].sum()) / pbs_ms, 4),
+        "prefill_ms_stats": stats(prefill_steps),
+        "attention_ms_stats": stats(per_step[:, 3]),
+        "dense_causal_ms_stats": dense_stats,
+        "timing": ("hipEvents on the launch stream around every call; every timed step (and every "
+                   "timed dense, hybrid, graph and permuted-query call) is preceded by a 512 MiB "
+                   "device write that evicts L2 and MALL, outside the events; value = mean "
+                   "prefill, ms_per_step = wall clock per step including that write"),
+        "configs": configs,
         "roofline": {
             "kernel": "attn_fwd_kernel<128,128>",
             "bound": "mfma",

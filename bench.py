@@ -338,13 +338,23 @@ def density_main(args):
     import block_sparse_attention_pbs_amd as P
     import pbs_synth
 
-    names = args.density.split(",")
     taus = [float(x) for x in args.taus.split(",")]
-    target = args.coverage_target
-    for name in names:
-        w = pbs_synth.WORKLOADS[name]
+    targets = [float(x) for x in args.coverage_target.split(",")]
+    if args.density_lengths:
+        # one workload shape at several sequence lengths (the pages' Fig. 4 axis), segment fixed
+        base = pbs_synth.WORKLOADS[args.density]
+        items = []
+        for n in (int(x) for x in args.density_lengths.split(",")):
+            seg = min(args.density_segment, n // 2)
+            items.append((f"{base.name}@N={n}", base.scaled(seq_len=n, segment=seg)))
+    else:
+        items = [(name, pbs_synth.WORKLOADS[name]) for name in args.density.split(",")]
+    summary = []
+    for name, w in items:
         if args.k_boost is not None:
             w = w.scaled(k_boost=args.k_boost)
+        if args.q_boost is not None:
+            w = w.scaled(q_boost=args.q_boost)
         inp = pbs_synth.make_inputs(w)
         dev = torch.device("cuda:0")
 
@@ -395,7 +405,7 @@ def density_main(args):
                              "coverage_p10": round(float(torch.quantile(cov[..., seg_rows].flatten()[::97].float(), 0.1).item()), 5)})
             res[order] = rows
 
-        def at_target(rows):
+        def at_target(rows, target):
             """Selected blocks at mean coverage (later segments) = target, interpolated."""
             pts = sorted((r["coverage_mean_later_segments"], r["selected"]) for r in rows)
             for (c0, s0_), (c1, s1_) in zip(pts, pts[1:]):
@@ -403,18 +413,27 @@ def density_main(args):
                     return s0_ + (s1_ - s0_) * (target - c0) / (c1 - c0)
             return None
 
-        sp, sn = at_target(res["permuted"]), at_target(res["natural"])
-        delta = (1.0 - sp / sn) if (sp is not None and sn) else None
-        print(json.dumps({
+        at = {}
+        for target in targets:
+            sp, sn = at_target(res["permuted"], target), at_target(res["natural"], target)
+            delta = (1.0 - sp / sn) if (sp is not None and sn) else None
+            at[str(target)] = {
+                "selected": {"permuted": None if sp is None else round(sp, 1),
+                             "natural": None if sn is None else round(sn, 1)},
+                "density_offdiag": {"permuted": None if sp is None else round(sp / candidates, 4),
+                                    "natural": None if sn is None else round(sn / candidates, 4)},
+                "delta": None if delta is None else round(delta, 4)}
+        line = {
             "workload": name, "shape": f"B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} block={Bs} segment={S}",
-            "salient_key_boost": w.k_boost, "salient_frac": w.salient_frac,
-            "candidates": candidates, "dense_blocks": dense_blocks, "coverage_target": target,
-            "selected_at_target": {"permuted": None if sp is None else round(sp, 1),
-                                   "natural": None if sn is None else round(sn, 1)},
-            "delta_at_target": None if delta is None else round(delta, 4),
-            "sweep": res}), flush=True)
+            "salient_key_boost": w.k_boost, "query_boost": w.q_boost, "salient_frac": w.salient_frac,
+            "candidates": candidates, "dense_blocks": dense_blocks, "at_coverage": at,
+            "sweep": res}
+        print(json.dumps(line), flush=True)
+        summary.append({"workload": name, "N": N, "at_coverage": at})
         del bf, q, k, v, o
         torch.cuda.empty_cache()
+    if len(summary) > 1:
+        print(json.dumps({"density_summary": summary}), flush=True)
 
 
 def sweep_main(args):
@@ -543,9 +562,18 @@ def main():
                     help="latency and speedup vs dense over keep ratios (64K, 28/4 heads) or over "
                          "sequence lengths 16K..256K (one JSON line instead of the bench line)")
     ap.add_argument("--taus", default="0.5,0.7,0.8,0.9,0.95,0.98,0.99,0.995")
-    ap.add_argument("--coverage-target", type=float, default=0.975)
+    ap.add_argument("--coverage-target", default="0.95,0.975",
+                    help="density mode: comma-separated mean coverages at which the two orders' "
+                         "selected blocks are compared")
+    ap.add_argument("--density-lengths", default=None,
+                    help="density mode: comma-separated sequence lengths; the one workload named by "
+                         "--density is run at each (segment = min(--density-segment, N/2))")
+    ap.add_argument("--density-segment", type=int, default=4096)
     ap.add_argument("--k-boost", type=float, default=None,
                     help="density mode: override the planted salient-key boost (attention concentration)")
+    ap.add_argument("--q-boost", type=float, default=None,
+                    help="density mode: override the queries' component along the planted direction "
+                         "(how consistently the salient keys stand out across queries)")
     args = ap.parse_args()
     if args.cpu_full:
         cpu_full_main(args)

@@ -439,7 +439,8 @@ def density_main(args):
 def sweep_main(args):
     """Latency and speedup against dense causal over keep ratios (the 28/4-head 64K sweep
     workload, or --workload) or over sequence lengths (the 128K workload's structure at
-    16K..256K, keep 0.1): one JSON line with one point per setting."""
+    16K..256K, keep 0.1): one JSON line with one point per setting.  Every timed call starts
+    with cold caches (a 512 MiB flush outside the events); medians are reported."""
     import numpy as np
     import torch
     import block_sparse_attention_pbs_amd as P
@@ -457,6 +458,7 @@ def sweep_main(args):
         raise SystemExit(f"bench.py: unknown sweep {args.sweep!r} (keep or length)")
     res = []
     inputs = {}
+    flush = Flusher(dev)
     for w, keep in points:
         if w.name not in inputs:
             inputs.clear()
@@ -486,14 +488,15 @@ def sweep_main(args):
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        pre = att = 0.0
+        pres, atts = [], []
         for _ in range(args.steps):
+            flush()
             step()
             ev[2].synchronize()
-            pre += ev[0].elapsed_time(ev[1])
-            att += ev[1].elapsed_time(ev[2])
-        pre /= args.steps
-        att /= args.steps
+            pres.append(ev[0].elapsed_time(ev[1]))
+            atts.append(ev[1].elapsed_time(ev[2]))
+        pre_s, att_s = stats(pres), stats(atts)
+        pre, att = pre_s["median"], att_s["median"]
         B, Hq, Hkv, N, d, Bs, S = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment
         nb, bps, G = N // Bs, S // Bs, Hq // Hkv
         counts = bf.counts.cpu().numpy().astype(np.int64)
@@ -503,19 +506,23 @@ def sweep_main(args):
         for _ in range(max(1, args.warmup)):
             P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale, od, None, stream=stream)
         torch.cuda.synchronize()
-        dense = 0.0
+        dts = []
         for _ in range(max(1, args.steps // 2)):
+            flush()
             ev[0].record(stream)
             P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale, od, None, stream=stream)
             ev[1].record(stream)
             ev[1].synchronize()
-            dense += ev[0].elapsed_time(ev[1])
-        dense /= max(1, args.steps // 2)
+            dts.append(ev[0].elapsed_time(ev[1]))
+        dense_s = stats(dts)
+        dense = dense_s["median"]
         diff_dense = float((od.float() - bf.o.float()).abs().max().item()) if keep >= 1.0 else None
         dense_blocks = B * Hq * nb * (nb + 1) // 2
         res.append({"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} block={Bs} segment={S}",
                     "keep": keep, "prefill_ms": round(pre + att, 4), "attention_ms": round(att, 4),
                     "score_permute_select_ms": round(pre, 4), "dense_causal_ms": round(dense, 4),
+                    "attention_ms_stats": att_s, "score_permute_select_ms_stats": pre_s,
+                    "dense_causal_ms_stats": dense_s,
                     "speedup_vs_dense": round(dense / (pre + att), 3),
                     "computed_block_frac": round(computed / dense_blocks, 4),
                     "effective_tflops_computed_blocks": round(computed * flop_per_block / (att * 1e-3) / 1e12, 1),

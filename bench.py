@@ -258,6 +258,8 @@ def oracle_full_seconds(name: str) -> dict:
         oracle.prefill(inp["q"], inp["k"], inp["v"], block=w.block, segment=w.segment, scale=scale,
                        mode=mode, param=param)
         out[f"{w.mode}={param}"] = round(time.perf_counter() - t, 3)
+        print(f"[bench] oracle {name} {w.mode}={param}: {out[f'{w.mode}={param}']} s", file=sys.stderr,
+              flush=True)
     t = time.perf_counter()
     oracle.dense_causal(inp["q"], inp["k"], inp["v"], block=w.block, scale=scale)
     out["dense_causal"] = round(time.perf_counter() - t, 3)

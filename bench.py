@@ -438,6 +438,44 @@ def density_main(args):
         print(json.dumps({"density_summary": summary}), flush=True)
 
 
+def operand_probe_main(args):
+    """The attention launch of the 128K workload, timed on the same visit lists (the same
+    instruction stream and MFMA count) with its K and V operands as generated and with V, K or
+    both replaced by zeros: what operand data alone does to the launch time (the chip's clock
+    follows its power draw)."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_pbs_amd as P
+    import pbs_synth
+
+    w = pbs_synth.WORKLOADS["gqa_128k"]
+    inp = pbs_synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = [torch.from_numpy(inp[x].view(np.int16)).view(torch.bfloat16).to(dev)
+               for x in ("q", "k", "v")]
+    del inp
+    sh = P.shape_of(q, k, w.block, w.segment)
+    scale = P.default_scale(w.head_dim)
+    bf = P.prefill(q, k, v, block=w.block, segment=w.segment, keep=w.params[0], scale=scale)
+    torch.cuda.synchronize()
+    o = torch.empty_like(q)
+    flush = Flusher(dev)
+    stream = torch.cuda.current_stream()
+    kz, vz = torch.zeros_like(bf.k_perm), torch.zeros_like(bf.v_perm)
+    cases = [("generated K, V", bf.k_perm, bf.v_perm), ("V zero", bf.k_perm, vz),
+             ("K zero", kz, bf.v_perm), ("K and V zero", kz, vz),
+             ("generated K, V (again)", bf.k_perm, bf.v_perm)]
+    res = {}
+    for name, kp, vp in cases:
+        t = time_calls(lambda: P.pbs_attn_fwd(sh, q, kp, vp, bf.perm, bf.perm_inv, bf.counts,
+                                              bf.idx, scale, o, None, stream=stream),
+                       args.steps, 2, flush, stream)
+        res[name] = stats(t)
+        print(f"[bench] operand probe {name}: {res[name]['median']} ms", file=sys.stderr, flush=True)
+    print(json.dumps({"operand_probe": "attn_fwd_kernel<128,128,1> at gqa_128k keep 0.1, same lists",
+                      "attention_ms": res}), flush=True)
+
+
 def sweep_main(args):
     """Latency and speedup against dense causal over keep ratios (the 28/4-head 64K sweep
     workload, or --workload) or over sequence lengths (the 128K workload's structure at
@@ -561,6 +599,9 @@ def main():
                     help="skip timing the other synthetic workloads (the configs object)")
     ap.add_argument("--no-hybrid", action="store_true",
                     help="skip timing pbs_attn_fwd_hybrid (own segment from the original K/V)")
+    ap.add_argument("--operand-probe", action="store_true",
+                    help="time the 128K attention launch on its own lists with K/V as generated and "
+                         "zeroed (one JSON line instead of the bench line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of 1 GiB (5 times): the known-size "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -598,6 +639,12 @@ def main():
             print("bench.py: one GPU only", file=sys.stderr)
             sys.exit(2)
         density_main(args)
+        return
+    if args.operand_probe:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            sys.exit(2)
+        operand_probe_main(args)
         return
     if args.copy_calibration:
         import torch

@@ -138,6 +138,51 @@ __device__ __forceinline__ int seq_sum64(float& c, float pv, float* stage, int l
   return first;
 }
 
+// x from lane (lane ^ m) of the wave, for a 64-bit value.
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
+  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(x)), m));
+  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(x >> 32)), m));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Bitonic sort (ascending) of 64*E 64-bit keys held in registers, element lane*E + r in x[r].
+// Compare-exchange partners closer than E elements sit in the same lane; the others are a lane
+// xor away, exchanged with shuffles.  Keys are distinct apart from equal padding, so the result
+// is the unique ascending order.
+template <int E>
+__device__ __forceinline__ void bitonic_regs(uint64_t (&x)[E], int lane) {
+  constexpr int LE = E == 1 ? 0 : E == 2 ? 1 : E == 4 ? 2 : E == 8 ? 3 : 4;
+  static_assert((1 << LE) == E, "E must be 1, 2, 4, 8 or 16");
+  constexpr int LOGN = 6 + LE;
+#pragma unroll
+  for (int ls = 1; ls <= LOGN; ++ls) {
+#pragma unroll
+    for (int lt = ls - 1; lt >= 0; --lt) {
+      const int size = 1 << ls, stride = 1 << lt;
+      if (stride < E) {
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          if (r & stride) continue;
+          const int r2 = r | stride;
+          const bool up = (size < E) ? ((r & size) == 0) : (((lane * E) & size) == 0);
+          const uint64_t u = x[r], v = x[r2];
+          const bool sw = (u > v) == up;
+          x[r] = sw ? v : u;
+          x[r2] = sw ? u : v;
+        }
+      } else {
+        const int lx = stride / E;
+        const bool take_min = ((lane & lx) == 0) == (((lane * E) & size) == 0);
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const uint64_t y = shfl_xor64(x[r], lx);
+          x[r] = ((x[r] < y) == take_min) ? x[r] : y;
+        }
+      }
+    }
+  }
+}
+
 // Per-row LDS of the select kernel (one wave per row), carved from the dynamic LDS: the ranking
 // keys (64-bit for the coverage sort, their 32-bit top words for the keep-ratio select), the
 // probabilities, the kept flags and a 256-bin histogram.
@@ -164,6 +209,78 @@ __device__ __forceinline__ RowLds row_lds(unsigned char* base, int n2max, int mo
   p += 4u * n2max;
   L.flag = p;
   return L;
+}
+
+// Coverage ranking of one row of n <= 64*E candidates (n2 = next_pow2(n) = 64*E) in registers:
+// the ranking keys sorted by bitonic_regs, the probabilities staged in LDS in ranking order, then
+// the running float32 sum.  The sum is the same strictly sequential chain as seq_sum64, 64 values
+// at a time; a chunk is first added without tracking where it crosses tf and, only if it ends at
+// or past tf (or a value is negative or NaN, where the running sum need not grow), added again
+// from its start with the tracking.  Sets the kept flags; returns the kept count.
+template <int E>
+__device__ __forceinline__ int coverage_regs(const RowLds& L, int n, int lane, bool keep_first,
+                                             float tf) {
+  uint64_t x[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int p = lane * E + r;
+    x[r] = (p < n) ? ((keep_first && p == 0) ? 0ull : desc_sort_key(L.P[p], static_cast<uint32_t>(p)))
+                   : ~0ull;
+  }
+  bitonic_regs<E>(x, lane);
+  float* stage = reinterpret_cast<float*>(L.keys);
+  bool odd = false;
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int m = lane * E + r;
+    const float pv = (m < n) ? L.P[static_cast<uint32_t>(x[r])] : 0.f;
+    odd |= !(pv >= 0.f);
+    stage[m] = pv;
+  }
+  const bool plain = __builtin_amdgcn_ballot_w64(odd) == 0;
+  wave_sync();
+  int kk = n;
+  float c = 0.f;
+  for (int m0 = 0; m0 < n; m0 += 64) {
+    const float4* s4 = reinterpret_cast<const float4*>(stage + m0);
+    if (plain) {
+      const float c0 = c;
+#pragma unroll
+      for (int e4 = 0; e4 < 16; ++e4) {
+        const float4 v = s4[e4];
+        c = __fadd_rn(c, v.x);
+        c = __fadd_rn(c, v.y);
+        c = __fadd_rn(c, v.z);
+        c = __fadd_rn(c, v.w);
+      }
+      if (c < tf) continue;
+      c = c0;
+    }
+    int first = -1;
+#pragma unroll
+    for (int e4 = 0; e4 < 16; ++e4) {
+      const float4 v = s4[e4];
+      c = __fadd_rn(c, v.x);
+      first = (first < 0 && c >= tf) ? 4 * e4 : first;
+      c = __fadd_rn(c, v.y);
+      first = (first < 0 && c >= tf) ? 4 * e4 + 1 : first;
+      c = __fadd_rn(c, v.z);
+      first = (first < 0 && c >= tf) ? 4 * e4 + 2 : first;
+      c = __fadd_rn(c, v.w);
+      first = (first < 0 && c >= tf) ? 4 * e4 + 3 : first;
+    }
+    if (first >= 0 && m0 + first < n) {
+      kk = m0 + first + 1;
+      break;
+    }
+  }
+  for (int j = lane; j < n; j += 64) L.flag[j] = 0;
+  wave_sync();
+#pragma unroll
+  for (int r = 0; r < E; ++r)
+    if (lane * E + r < kk) L.flag[static_cast<uint32_t>(x[r])] = 1;
+  wave_sync();
+  return kk;
 }
 
 // One workgroup per (query block, group of hpw query heads sharing a KV head), one wave per head
@@ -348,6 +465,15 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     const float tf = a.tau_f;
     float c = 0.f;
     kk = n;
+    if (n2 >= 64 && n2 <= 1024) {   // n2 is uniform over the workgroup
+      switch (n2 >> 6) {
+        case 1: kk = coverage_regs<1>(L, n, lane, a.keep_first, tf); break;
+        case 2: kk = coverage_regs<2>(L, n, lane, a.keep_first, tf); break;
+        case 4: kk = coverage_regs<4>(L, n, lane, a.keep_first, tf); break;
+        case 8: kk = coverage_regs<8>(L, n, lane, a.keep_first, tf); break;
+        default: kk = coverage_regs<16>(L, n, lane, a.keep_first, tf); break;
+      }
+    } else {
     for (int p = lane; p < n2; p += 64)
       L.keys[p] = (p < n) ? ((a.keep_first && p == 0) ? 0ull : desc_sort_key(L.P[p], static_cast<uint32_t>(p)))
                           : ~0ull;
@@ -380,6 +506,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     wave_sync();
     for (int m = lane; m < kk; m += 64) L.flag[static_cast<int>(L.keys[m] & 0xffffffffull)] = 1;
     wave_sync();
+    }
   }
 
   // ascending compaction: lane l of the row owns candidates [l*per, (l+1)*per)

@@ -162,6 +162,43 @@ def test_select_keep_ratio_ties_and_specials():
                     assert np.array_equal(ix[0, g, i, :kk], np.sort(order[:kk])), (param, keep_first, g, i)
 
 
+def test_select_coverage_row_sizes():
+    """Coverage selection on rows of every candidate count class around the powers of two
+    (1 to 2047 candidates: the register-sorted sizes 64..1024 and the LDS-sorted rest), with
+    softmax rows, rows full of ties and zeros, and rows holding NaN, -0 and a negative value,
+    with and without the first block forced first: bit-exact against the oracle."""
+    say("select coverage row sizes")
+    B, Hq, N, d, Bs, S = 1, 2, 2048 * 64, 64, 64, 64   # one block per segment: row i has i candidates
+    nb = N // Bs
+    rng = np.random.default_rng(21)
+    rows = [1, 2, 63, 64, 65, 100, 127, 128, 129, 255, 256, 300, 511, 512, 513, 700, 960, 1023,
+            1024, 1025, 1500, nb - 1]
+    tie_vals = np.array([0.0, 0.25, 0.125, 1e-30, 2.0 ** -20, 0.5, 0.0625], np.float32)
+    Pm = np.zeros((B, Hq, nb, nb), np.float32)
+    for t, i in enumerate(rows):
+        x = rng.normal(size=i) * 2.0
+        e = np.exp(x - x.max())
+        Pm[0, 0, i, :i] = (e / e.sum()).astype(np.float32)
+        r = rng.choice(tie_vals, size=i) / max(1.0, i / 16.0)
+        if t % 3 == 2 and i > 3:
+            r[rng.integers(i)] = np.nan
+            r[rng.integers(i)] = -0.0
+            r[rng.integers(i)] = -0.125
+        Pm[0, 1, i, :i] = r.astype(np.float32)
+    sh = shape(B, Hq, 1, N, d, Bs, S)
+    for tau, keep_first in ((0.5, False), (0.9, True), (0.999, False), (1.0, True)):
+        say(f"coverage tau={tau} keep_first={keep_first}")
+        flags = P.PBS_FLAG_SCORES_IN | (P.PBS_FLAG_KEEP_FIRST if keep_first else 0)
+        counts, idx = run_select(sh, None, None, None, 0.125, P.PBS_SELECT_COVERAGE, tau,
+                                 blk_scores=dev(Pm), flags=flags)
+        rc, ri = oracle.select_blocks(Pm, block=Bs, segment=S, mode=oracle.COVERAGE, param=tau,
+                                      keep_first=keep_first)
+        c = counts.cpu().numpy()
+        assert lists_equal(c, idx.cpu().numpy(), rc, ri), (tau, keep_first)
+        if tau < 1.0:   # the softmax rows stop before their end
+            assert (c[0, 0, rows[3:]] < np.array(rows[3:])).all()
+
+
 def test_permute_largest_segment():
     """The largest supported segment (16384 keys sorted in one workgroup)."""
     say("permute S=16384")

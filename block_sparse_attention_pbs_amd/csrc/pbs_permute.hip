@@ -79,10 +79,11 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     const int src = a.perm[head + pos];
     mn = min(mn, src);
     const size_t so = a.km.off(b, h, src) + c * 8, po = a.km.off(b, h, pos) + c * 8;
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(a.k + so);
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v + so);
-    *reinterpret_cast<u32x4*>(a.k_perm + po) = kv;
-    *reinterpret_cast<u32x4*>(a.v_perm + po) = vv;
+    // non-temporal loads and stores: every source row is read once, every output row written once
+    const u32x4 kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k + so));
+    const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.v + so));
+    __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(a.k_perm + po));
+    __builtin_nontemporal_store(vv, reinterpret_cast<u32x4*>(a.v_perm + po));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       sum[2 * e] += __uint_as_float(kv[e] << 16);
@@ -140,8 +141,9 @@ __global__ __launch_bounds__(256) void qgather_kernel(QGatherArgs a) {
     const int p = blockIdx.x * ROWS + r;
     if (p >= a.N) break;
     const int src = min(max(a.perm[phead + p], 0), a.N - 1);
-    const u32x4 x = *reinterpret_cast<const u32x4*>(a.q + a.qm.off(b, g, src) + c * 8);
-    *reinterpret_cast<u32x4*>(a.q_perm + a.qm.off(b, g, p) + c * 8) = x;
+    const u32x4 x =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.q + a.qm.off(b, g, src) + c * 8));
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(a.q_perm + a.qm.off(b, g, p) + c * 8));
   }
 }
 

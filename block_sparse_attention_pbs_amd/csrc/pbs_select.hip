@@ -15,16 +15,20 @@
 // sequence (block 0 above is then the sequence's first block).
 //
 // Kernels:
-//  * pool: float32 mean of every block of Bs rows (queries; keys too when the caller has no
-//    pooled keys from pbs_permute).  HBM-bound, one workgroup per (head, block).
+//  * pool: float32 mean of every block of Bs key rows, when the caller has no pooled keys from
+//    pbs_permute.  HBM-bound, one workgroup per (head, block).
 //  * select: one workgroup per (query block, up to 4 query heads of one KV head), one wave per
-//    head.  Logits are plain fp32 dot products (n <= 8192 candidates x d) computed by the whole
-//    workgroup, so each pooled key is read once for the group; after one barrier every row is
+//    head.  The workgroup first pools its query blocks (the query rows are read from HBM while the
+//    other workgroups of the CU rank their rows).  Logits are plain fp32 dot products (n <= 8192
+//    candidates x d) computed by the whole workgroup, so each pooled key is read once for the
+//    group; after one barrier every row is
 //    its wave's own: softmax with wave reductions; keep ratio: the top-k set from a radix select
 //    over the ranking keys with a per-row histogram in LDS (no sort); coverage: a bitonic sort
-//    of next_pow2(n) 64-bit keys in LDS and one strictly sequential fp32 coverage sum (so it is
-//    bit-identical to any other sequential fp32 sum of the same values); the kept blocks are
-//    compacted in ascending order with a wave scan.  No workgroup barrier after the logits.
+//    of next_pow2(n) 64-bit keys (in registers for 64 <= next_pow2(n) <= 1024, else in LDS) and
+//    one strictly sequential fp32 coverage sum (so it is bit-identical to any other sequential
+//    fp32 sum of the same values); the kept blocks are compacted in ascending order with a wave
+//    scan.  No workgroup barrier after the logits.
+#include <algorithm>
 #include <cmath>
 
 #include "pbs_device.h"
@@ -54,11 +58,13 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   float sum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sum[e] = 0.f;
-  // every row load of the thread in flight at once (BS / RP of them)
+  // every row load of the thread in flight at once (BS / RP of them); non-temporal: the rows are
+  // read once here, and the whole tensor is far larger than L2 and MALL
   u32x4 rows[BS / RP];
 #pragma unroll
   for (int q = 0; q < BS / RP; ++q)
-    rows[q] = *reinterpret_cast<const u32x4*>(x0 + static_cast<size_t>(rg + q * RP) * rs);
+    rows[q] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(x0 + static_cast<size_t>(rg + q * RP) * rs));
 #pragma unroll
   for (int q = 0; q < BS / RP; ++q) {
     const u32x4 xv = rows[q];
@@ -79,7 +85,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 }
 
 struct SelArgs {
-  const float* qbar;   // [B*Hq, nb, D]
+  const uint16_t* q;   // the queries (pooled here, block by block)
+  RowMap qm;           // row addressing of q (either layout)
   const float* kbar;   // [B*Hkv, nb, D]
   float* P;            // [B*Hq, nb, nb] or null
   int32_t* counts;     // [B*Hq, nb]
@@ -211,6 +218,54 @@ __device__ __forceinline__ RowLds row_lds(unsigned char* base, int n2max, int mo
   return L;
 }
 
+// The float32 mean of the Bs rows of query block i of query head g into dst[0, D) (LDS), with
+// the same summation order as pool_kernel for 256 threads: thread t of the nt takes dims
+// (t % CH)*8 .. +8 of rows t / CH, + RP, + 2 RP, ... (RP = nt / CH), added in row order, then the
+// RP partial sums are added in order and divided by Bs.  red holds RP * D floats.  Every thread of
+// the workgroup takes part (two workgroup barriers).
+template <int D>
+__device__ __forceinline__ void pool_query_block(const SelArgs& a, int b, int g, int i, float* red,
+                                                 float* dst, int tid, int nt) {
+  constexpr int CH = D / 8;
+  const int RP = nt / CH;
+  const int c = tid % CH, rg = tid / CH;
+  const size_t rs = static_cast<size_t>(a.qm.stride());
+  const uint16_t* x0 = a.q + a.qm.off(b, g, i * a.bs) + c * 8;
+  float sum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sum[e] = 0.f;
+  for (int r0 = rg; r0 < a.bs; r0 += 8 * RP) {
+    // up to 8 row loads in flight; non-temporal: the query rows are read once here
+    u32x4 rows[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + u * RP;
+      rows[u] = r < a.bs ? __builtin_nontemporal_load(
+                               reinterpret_cast<const u32x4*>(x0 + static_cast<size_t>(r) * rs))
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (r0 + u * RP < a.bs) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sum[2 * e] += __uint_as_float(rows[u][e] << 16);
+          sum[2 * e + 1] += __uint_as_float(rows[u][e] & 0xffff0000u);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg * D + c * 8 + e] = sum[e];
+  __syncthreads();
+  for (int dd = tid; dd < D; dd += nt) {
+    float tot = 0.f;
+    for (int q = 0; q < RP; ++q) tot += red[q * D + dd];
+    dst[dd] = tot / static_cast<float>(a.bs);
+  }
+  __syncthreads();   // dst is complete, and red may be refilled
+}
+
 // Coverage ranking of one row of n <= 64*E candidates (n2 = next_pow2(n) = 64*E) in registers:
 // the ranking keys sorted by bitonic_regs, the probabilities staged in LDS in ranking order, then
 // the running float32 sum.  The sum is the same strictly sequential chain as seq_sum64, 64 values
@@ -331,12 +386,17 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     constexpr int TPC = D / 8;
     const int nt = 64 * a.hpw;
     const int sl = tid % TPC, grp = tid / TPC;
-    const size_t row0 = (static_cast<size_t>(b) * a.Hq + g0) * a.nb + i;   // first row
+    // The rows' pooled queries, pooled here from Q (the first LDS bytes, which the rows' areas
+    // reuse once the pooled queries are in registers): the query rows are read while other
+    // workgroups on the CU rank theirs.
+    float* qlds = reinterpret_cast<float*>(smem);
+    for (int r = 0; r < a.hpw; ++r)
+      pool_query_block<D>(a, b, g0 + r, i, qlds + a.hpw * D, qlds + r * D, tid, nt);
     float qv[4][8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (r < a.hpw) {
-        const float4* qp = reinterpret_cast<const float4*>(a.qbar + (row0 + static_cast<size_t>(r) * a.nb) * D + sl * 8);
+        const float4* qp = reinterpret_cast<const float4*>(qlds + r * D + sl * 8);
         const float4 x0 = qp[0], x1 = qp[1];
         qv[r][0] = x0.x; qv[r][1] = x0.y; qv[r][2] = x0.z; qv[r][3] = x0.w;
         qv[r][4] = x1.x; qv[r][5] = x1.y; qv[r][6] = x1.z; qv[r][7] = x1.w;
@@ -345,6 +405,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
         for (int e = 0; e < 8; ++e) qv[r][e] = 0.f;
       }
     }
+    __syncthreads();   // every thread holds its pooled queries; the LDS goes to the rows
     const float* kb = a.kbar + ((static_cast<size_t>(b) * a.Hkv + h) * a.nb + first) * D;
     for (int j0 = grp * TPC; j0 < n; j0 += nt) {
       float part[4][TPC];
@@ -543,9 +604,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 }  // namespace
 
 size_t select_workspace_bytes(const Dims& d) {
-  const size_t qbar = static_cast<size_t>(d.B) * d.Hq * d.nb * d.d * sizeof(float);
   const size_t kbar = static_cast<size_t>(d.B) * d.Hkv * d.nb * d.d * sizeof(float);
-  return align256(qbar) + align256(kbar);
+  return align256(kbar);
 }
 
 hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t* k_perm,
@@ -553,22 +613,16 @@ hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t*
                                float* blk_scores, bool scores_in, bool keep_first, int32_t* counts,
                                int32_t* idx, void* ws, const int32_t* cu, int nseq,
                                hipStream_t stream) {
-  float* qbar = static_cast<float*>(ws);
-  float* kbar_ws = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                            align256(static_cast<size_t>(d.B) * d.Hq * d.nb * d.d * sizeof(float)));
+  float* kbar_ws = static_cast<float*>(ws);
   hipError_t e;
   const float* kbar = k_pool;
-  if (!scores_in) {
-    e = launch_pool(q, qbar, d.Hq, d, stream);
+  if (!scores_in && !kbar) {   // pooled keys (the queries are pooled inside the select kernel)
+    e = launch_pool(k_perm, kbar_ws, d.Hkv, d, stream);
     if (e != hipSuccess) return e;
-    if (!kbar) {
-      e = launch_pool(k_perm, kbar_ws, d.Hkv, d, stream);
-      if (e != hipSuccess) return e;
-      kbar = kbar_ws;
-    }
+    kbar = kbar_ws;
   }
   SelArgs sa;
-  sa.qbar = qbar; sa.kbar = kbar; sa.P = blk_scores; sa.counts = counts; sa.idx = idx;
+  sa.q = q; sa.qm = q_rows(d); sa.kbar = kbar; sa.P = blk_scores; sa.counts = counts; sa.idx = idx;
   sa.Hq = d.Hq; sa.Hkv = d.Hkv; sa.G = d.G; sa.nb = d.nb; sa.bps = d.bps; sa.max_off = d.max_off;
   int n2 = 1;
   while (n2 < d.max_off) n2 <<= 1;
@@ -584,7 +638,10 @@ hipError_t launch_block_select(const Dims& d, const uint16_t* q, const uint16_t*
   sa.cu = cu; sa.nseq = nseq; sa.N = d.N; sa.bs = d.Bs;
   sa.tau_f = static_cast<float>(param);
   if (static_cast<double>(sa.tau_f) < param) sa.tau_f = std::nextafter(sa.tau_f, INFINITY);
-  const size_t shmem = hpw * per_row;
+  // the rows' areas; before them, the same bytes hold the pooled queries and the pooling sums
+  const size_t pool_bytes =
+      scores_in ? 0 : static_cast<size_t>(hpw + 64 * hpw / (d.d / 8)) * d.d * sizeof(float);
+  const size_t shmem = std::max(hpw * per_row, pool_bytes);
   auto kern = d.d == 128 ? (mode == 0 ? select_kernel<128, 0> : select_kernel<128, 1>)
                          : (mode == 0 ? select_kernel<64, 0> : select_kernel<64, 1>);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

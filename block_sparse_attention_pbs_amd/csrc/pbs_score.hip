@@ -39,6 +39,7 @@ struct ScoreArgs {
   float2* part;   // [B, Hkv, nseg, nchunk, R] (m, l) of each key chunk
   float* lse2;    // [B, Hkv, nseg, R] log2-normaliser of each (segment, row)
   int Hq, Hkv, G, N, S, nseg, R, Bs;
+  int bs_log2;    // Bs = 1 << bs_log2 (64 or 128)
   int chunk, nchunk;  // keys per chunk, chunks per segment
   float c;        // scale * log2(e)
   RowMap qm, km;  // row addressing of q and k (either layout)
@@ -57,8 +58,8 @@ __device__ __forceinline__ int seq_end(const ScoreArgs& a, int sigma) {
 // Bs positions of the sequence, which ends at `end`.
 __device__ __forceinline__ void score_row(const ScoreArgs& a, int r, int end, int& g_local,
                                           int& t) {
-  g_local = r / a.Bs;
-  t = min(max(end - a.Bs + (r - g_local * a.Bs), 0), a.N - 1);
+  g_local = r >> a.bs_log2;
+  t = min(max(end - a.Bs + (r & (a.Bs - 1)), 0), a.N - 1);
 }
 
 constexpr int kStatKeys = 64;  // keys per LDS tile in the stats pass
@@ -313,6 +314,8 @@ hipError_t launch_score(const Dims& d, const uint16_t* q, const uint16_t* k, flo
   a.cu = cu; a.nseq = nseq;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.N = d.N; a.S = d.S; a.nseg = d.nseg;
   a.R = d.G * d.Bs; a.Bs = d.Bs;
+  a.bs_log2 = 0;
+  while ((1 << a.bs_log2) < d.Bs) ++a.bs_log2;
   a.chunk = score_chunk(d);
   a.nchunk = d.S / a.chunk;
   const size_t rows = static_cast<size_t>(d.B) * d.Hkv * d.nseg * a.R;

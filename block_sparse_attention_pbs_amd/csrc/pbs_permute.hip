@@ -10,7 +10,9 @@
 //  * seg_sort: one workgroup per (batch, KV head, segment).  The segment's scores become 64-bit
 //    keys (order-preserving float bits, inverted for descending order, with the in-segment
 //    position in the low word so equal scores keep their original order) and are sorted by a
-//    bitonic network in LDS (S <= 16384 keys = 128 KiB).  The same pass writes the inverse
+//    bitonic network: held in registers by the workgroup's 16 waves, with only the steps between
+//    waves going through LDS, when next_pow2(S) >= 1024; wholly in LDS for smaller segments
+//    (S <= 16384 keys = 128 KiB).  The same pass writes the inverse
 //    permutation (the slot of every original position), which the attention kernel walks to
 //    read a query block's visible own-segment keys without searching the segment.
 //  * gather: one workgroup per (batch, KV head, block of Bs slots).  16-byte lanes read whole
@@ -30,14 +32,49 @@ struct SortArgs {
   int N, S, n2;
 };
 
+// Segments of 1024 <= next_pow2(S) = 1024*E <= 16384 keys: the 16 waves hold the keys in
+// registers (E per lane) and sort them with bitonic_sort_regs, which needs the LDS only for the
+// compare-exchange steps between waves (10 of the 91 steps at S = 8192).
+template <int E>
+__device__ __forceinline__ void seg_sort_regs(const SortArgs& a, uint64_t* lds, size_t base,
+                                              int s0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e0 = tid * E;
+  uint64_t x[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int p = e0 + r;
+    x[r] = (p < a.S) ? desc_sort_key(a.scores[base + p], static_cast<uint32_t>(p)) : ~0ull;
+  }
+  bitonic_sort_regs<E, 16>(x, lane, wave, lds);
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int p = e0 + r;
+    if (p < a.S) {
+      const int32_t src = static_cast<int32_t>(x[r] & 0xffffffffull);   // position in segment
+      a.perm[base + p] = s0 + src;
+      if (a.inv) a.inv[base + src] = s0 + p;
+    }
+  }
+}
+
 __global__ __launch_bounds__(1024) void seg_sort_kernel(SortArgs a) {
   extern __shared__ uint64_t keys[];
   const int sigma = blockIdx.x;
   const size_t base = static_cast<size_t>(blockIdx.y) * a.N + static_cast<size_t>(sigma) * a.S;
+  const int s0 = sigma * a.S;
+  if (a.n2 >= 1024 && blockDim.x == 1024) {   // uniform: the launch picks the path
+    switch (a.n2 >> 10) {
+      case 1: seg_sort_regs<1>(a, keys, base, s0); return;
+      case 2: seg_sort_regs<2>(a, keys, base, s0); return;
+      case 4: seg_sort_regs<4>(a, keys, base, s0); return;
+      case 8: seg_sort_regs<8>(a, keys, base, s0); return;
+      default: seg_sort_regs<16>(a, keys, base, s0); return;
+    }
+  }
   for (int p = threadIdx.x; p < a.n2; p += blockDim.x)
     keys[p] = (p < a.S) ? desc_sort_key(a.scores[base + p], static_cast<uint32_t>(p)) : ~0ull;
   bitonic_sort_lds(keys, a.n2);
-  const int s0 = sigma * a.S;
   for (int p = threadIdx.x; p < a.S; p += blockDim.x) {
     const int32_t src = static_cast<int32_t>(keys[p] & 0xffffffffull);   // position in segment
     a.perm[base + p] = s0 + src;

@@ -145,51 +145,6 @@ __device__ __forceinline__ int seq_sum64(float& c, float pv, float* stage, int l
   return first;
 }
 
-// x from lane (lane ^ m) of the wave, for a 64-bit value.
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
-  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(x)), m));
-  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(x >> 32)), m));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// Bitonic sort (ascending) of 64*E 64-bit keys held in registers, element lane*E + r in x[r].
-// Compare-exchange partners closer than E elements sit in the same lane; the others are a lane
-// xor away, exchanged with shuffles.  Keys are distinct apart from equal padding, so the result
-// is the unique ascending order.
-template <int E>
-__device__ __forceinline__ void bitonic_regs(uint64_t (&x)[E], int lane) {
-  constexpr int LE = E == 1 ? 0 : E == 2 ? 1 : E == 4 ? 2 : E == 8 ? 3 : 4;
-  static_assert((1 << LE) == E, "E must be 1, 2, 4, 8 or 16");
-  constexpr int LOGN = 6 + LE;
-#pragma unroll
-  for (int ls = 1; ls <= LOGN; ++ls) {
-#pragma unroll
-    for (int lt = ls - 1; lt >= 0; --lt) {
-      const int size = 1 << ls, stride = 1 << lt;
-      if (stride < E) {
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          if (r & stride) continue;
-          const int r2 = r | stride;
-          const bool up = (size < E) ? ((r & size) == 0) : (((lane * E) & size) == 0);
-          const uint64_t u = x[r], v = x[r2];
-          const bool sw = (u > v) == up;
-          x[r] = sw ? v : u;
-          x[r2] = sw ? u : v;
-        }
-      } else {
-        const int lx = stride / E;
-        const bool take_min = ((lane & lx) == 0) == (((lane * E) & size) == 0);
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          const uint64_t y = shfl_xor64(x[r], lx);
-          x[r] = ((x[r] < y) == take_min) ? x[r] : y;
-        }
-      }
-    }
-  }
-}
-
 // Per-row LDS of the select kernel (one wave per row), carved from the dynamic LDS: the ranking
 // keys (64-bit for the coverage sort, their 32-bit top words for the keep-ratio select), the
 // probabilities, the kept flags and a 256-bin histogram.
@@ -267,8 +222,8 @@ __device__ __forceinline__ void pool_query_block(const SelArgs& a, int b, int g,
 }
 
 // Coverage ranking of one row of n <= 64*E candidates (n2 = next_pow2(n) = 64*E) in registers:
-// the ranking keys sorted by bitonic_regs, the probabilities staged in LDS in ranking order, then
-// the running float32 sum.  The sum is the same strictly sequential chain as seq_sum64, 64 values
+// the ranking keys sorted by bitonic_sort_regs, the probabilities staged in LDS in ranking order,
+// then the running float32 sum.  The sum is the same strictly sequential chain as seq_sum64, 64 values
 // at a time; a chunk is first added without tracking where it crosses tf and, only if it ends at
 // or past tf (or a value is negative or NaN, where the running sum need not grow), added again
 // from its start with the tracking.  Sets the kept flags; returns the kept count.
@@ -282,7 +237,7 @@ __device__ __forceinline__ int coverage_regs(const RowLds& L, int n, int lane, b
     x[r] = (p < n) ? ((keep_first && p == 0) ? 0ull : desc_sort_key(L.P[p], static_cast<uint32_t>(p)))
                    : ~0ull;
   }
-  bitonic_regs<E>(x, lane);
+  bitonic_sort_regs<E, 1>(x, lane, 0, nullptr);
   float* stage = reinterpret_cast<float*>(L.keys);
   bool odd = false;
 #pragma unroll

@@ -111,14 +111,33 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_scan_incl(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP moves: a Hillis-Steele scan inside
+// each row of 16 lanes (shifts by 1, 2, 4, 8; lanes shifted in from before the row read 0), then
+// the last lane of row 0 / row 2 added to rows 1 / 3 and lane 31 added to rows 2 and 3.
+__device__ __forceinline__ int wave_scan_incl(int x, int /*lane*/) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15, rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31, rows 2, 3
   return x;
+}
+
+// One level of the logits' transposing butterfly (half-width HW, then the narrower levels): the
+// lanes of a group exchange half of their partial sums with the lane HW away.
+template <int HW, int TPC>
+__device__ __forceinline__ void butterfly_levels(float (&part)[4][TPC], int sl) {
+  const bool upper = (sl & HW) != 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < HW; ++c) {
+      const float send = upper ? part[r][c] : part[r][c + HW];
+      const float keep = upper ? part[r][c + HW] : part[r][c];
+      part[r][c] = keep + __uint_as_float(xor_lane<HW>(__float_as_uint(send)));
+    }
+  if constexpr (HW > 1) butterfly_levels<HW / 2, TPC>(part, sl);
 }
 
 // One chunk of the coverage sum: c runs through the chunk's 64 ranked values (staged in LDS by
@@ -374,18 +393,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
           part[r][c] = qv[r][0] * k0.x + qv[r][1] * k0.y + qv[r][2] * k0.z + qv[r][3] * k0.w +
                        qv[r][4] * k1.x + qv[r][5] * k1.y + qv[r][6] * k1.z + qv[r][7] * k1.w;
       }
-#pragma unroll
-      for (int hw = TPC / 2; hw >= 1; hw >>= 1) {
-        const bool upper = (sl & hw) != 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int c = 0; c < hw; ++c) {
-            const float send = upper ? part[r][c] : part[r][c + hw];
-            const float keep = upper ? part[r][c + hw] : part[r][c];
-            part[r][c] = keep + __shfl_xor(send, hw);
-          }
-      }
+      butterfly_levels<TPC / 2, TPC>(part, sl);
       const int j = j0 + sl;
       if (j < n)
 #pragma unroll
@@ -454,8 +462,8 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
           if (below + c2 < need) { below += c2; ++dgt; } } }
       const uint64_t bal = __builtin_amdgcn_ballot_w64(excl < need && need <= incl);
       const int src = __builtin_ctzll(bal);
-      dgt = __shfl(dgt, src);
-      below = __shfl(below, src);
+      dgt = __builtin_amdgcn_readlane(dgt, src);
+      below = __builtin_amdgcn_readlane(below, src);
       prefix |= static_cast<uint32_t>(dgt) << shift;
       pmask |= 0xffu << shift;
       need -= below;

@@ -21,6 +21,7 @@
 //    mean of the block's keys (reduced through LDS) and the block's smallest original position.
 #include "pbs_device.h"
 #include "pbs_internal.h"
+#include "pbs_sort.h"
 
 namespace pbs {
 namespace {

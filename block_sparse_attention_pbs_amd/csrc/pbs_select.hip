@@ -33,6 +33,7 @@
 
 #include "pbs_device.h"
 #include "pbs_internal.h"
+#include "pbs_sort.h"
 
 namespace pbs {
 namespace {

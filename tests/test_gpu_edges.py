@@ -216,6 +216,29 @@ def test_permute_largest_segment():
     assert np.array_equal(pinv.cpu().numpy(), inverse_of(ref))
 
 
+@pytest.mark.parametrize("S", [1536, 3072, 12288])
+def test_permute_segment_not_power_of_two(S):
+    """Segments whose length is not a power of two (the sort pads to the next one: 2048, 4096
+    and 16384 keys, all register-sorted across the workgroup's waves), with ties and specials:
+    the GPU permutation and its inverse equal the oracle's."""
+    say(f"permute S={S}")
+    B, H, d, Bs = 1, 2, 64, 64
+    N = 2 * S
+    rng = np.random.default_rng(S)
+    vals = np.array([0.0, -0.0, 1e-30, 0.25, np.nan, -1.0, np.inf, 3.0], np.float32)
+    sc = (rng.random((B, H, N)) * 1e-3).astype(np.float32)
+    mask = rng.random((B, H, N)) < 0.2
+    sc[mask] = rng.choice(vals, size=int(mask.sum()))
+    k = pbs_synth.random_bf16((B, H, N, d), 20)
+    v = pbs_synth.random_bf16((B, H, N, d), 21)
+    sh = shape(B, H, H, N, d, Bs, S)
+    perm, kp, vp, _, mpos, pinv = run_permute(sh, dev(sc), dev_bf16(k), dev_bf16(v), pool=False)
+    ref = oracle.segment_permutation(sc, segment=S)
+    assert np.array_equal(perm.cpu().numpy(), ref)
+    assert np.array_equal(pinv.cpu().numpy(), inverse_of(ref))
+    assert np.array_equal(mpos.cpu().numpy(), ref.reshape(B, H, N // Bs, Bs).min(-1))
+
+
 def test_deterministic():
     """Two runs of the whole pipeline give bitwise-identical results."""
     say("determinism")

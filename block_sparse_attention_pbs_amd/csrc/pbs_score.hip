@@ -199,6 +199,9 @@ __global__ __launch_bounds__(64 * kRedWaves) void score_reduce_kernel(ScoreArgs 
   const float* st_seg = a.lse2 + (static_cast<size_t>(bh) * a.nseg + sigma) * a.R;
   const int end = seq_end(a, sigma);
   const bool causal = active && key0 + 31 > end - a.Bs;   // uniform: a key may follow a row
+  // The rows' log2-normalisers are read one chunk ahead (R is a multiple of 32; the last chunk
+  // reads its own again), so their load is in flight while the chunk before them is computed.
+  float l2_next = active ? st_seg[c32] : 0.f;
   for (int rc = 0; rc < a.R; rc += 32) {
     __syncthreads();
     {
@@ -213,6 +216,8 @@ __global__ __launch_bounds__(64 * kRedWaves) void score_reduce_kernel(ScoreArgs 
     }
     __syncthreads();
     if (!active) continue;
+    const float nl = -l2_next;
+    l2_next = st_seg[min(rc + 32, a.R - 32) + c32];
     f32x16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -222,7 +227,6 @@ __global__ __launch_bounds__(64 * kRedWaves) void score_reduce_kernel(ScoreArgs 
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], *reinterpret_cast<const bf16x8*>(qrow + ks * 16),
                                                    s, 0, 0, 0);
     // lane column = scoring row rc + c32; lane value e = key key0 + (e/4)*8 + hl*4 + e%4
-    const float nl = -st_seg[rc + c32];
     if (causal) {
       int gl, tt;
       score_row(a, rc + c32, end, gl, tt);

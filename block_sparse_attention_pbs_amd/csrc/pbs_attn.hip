@@ -300,6 +300,9 @@ struct StageIter {
 
 struct Stage {
   int key0;     // first key of the stage in the head's key order (block * Bs + stage * 32)
+  int pos0;     // original position of its first key; its 32 keys hold positions pos0 .. pos0+31
+                // (a key-stream stage walks positions in order; a block stage of the diagonal
+                // block holds them in order in modes 0, 2 and 3)
   bool masked;
   bool orig;    // read from the original keys and values (mode 3 own segment)
   // Own-segment key-stream stage (mode 1): the slots of its 32 keys (perm_inv entries, in LDS);
@@ -312,6 +315,7 @@ template <int BS, int SK>
 __device__ __forceinline__ Stage stage_of(const StageIter& it) {
   Stage st;
   st.key0 = it.j * BS + it.half * SK;
+  st.pos0 = it.kidx >= 0 ? it.seg_first * BS + it.kidx : st.key0;
   st.masked = it.masked;
   st.orig = it.orig;
   st.slots = nullptr;
@@ -473,7 +477,7 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
                                            const int32_t* Ps, int key0, int lane, int t,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                            f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs,
-                                           Pre&& pre) {
+                                           Pre&& pre, bool skip = false) {
   using C = Cfg<D, BS>;
   const int hl = lane >> 5;
   const int c32 = lane & 31;
@@ -485,6 +489,7 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
     for (int kt = 0; kt < C::NKT; ++kt)
       k0[kt] = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kt * 32 + c32, hl * 8)]);
     pre();   // the next stage's loads, if the caller issues them here
+    if (skip) return;   // wave-uniform: nothing of this stage reaches the wave's rows
     if constexpr (MASKED) {
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
@@ -594,9 +599,15 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
         issue_ring(rr, it, it.ks, lc.seg_pos, w, lane);
       }
     };
+    // A masked stage whose keys all come after every row of this wave adds exactly nothing to
+    // the wave's rows: the wave only issues its share of the next loads (queries are in natural
+    // order outside mode 4, so the wave's last row is its first row + 31).
+    bool skip = false;
+    if constexpr (MASKED && MODE != 4)
+      skip = pp.cur.pos0 > __builtin_amdgcn_readfirstlane((t & ~31) + 31);
     attn_stage<D, BS, MODE, MASKED, MAXONLY>(
         a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
-        p ? Ps1 : Ps0, pp.cur.key0, lane, t, qf, oacc, rs, stream_issue);
+        p ? Ps1 : Ps0, pp.cur.key0, lane, t, qf, oacc, rs, stream_issue, skip);
     pp.cur = nxt;
     pp.p = p ^ 1;
   }

@@ -71,6 +71,14 @@ def own_segment_blocks(perm, block: int, segment: int, G: int) -> float:
     return total * G
 
 
+def diag_skipped_blocks(B: int, Hq: int, nb: int, Bs: int) -> float:
+    """Block-equivalents of every query block's diagonal positions that the attention kernel does
+    not compute: with W = Bs/32 waves of 32 rows and the block's Bs keys in W stages of 32, a wave
+    skips the stages whose keys all come after its rows, W(W-1)/2 of the W^2 wave-stage tiles."""
+    W = Bs // 32
+    return B * Hq * nb * (W - 1) / (2.0 * W)
+
+
 def read_traffic(workload: str):
     """HBM bytes per attention launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE,
     scaled by a copy-kernel calibration), valid only if the kernel source is unchanged."""
@@ -158,7 +166,7 @@ def measure_configs(args, flush, stream, dev, skip: str) -> dict:
         B, Hq, Hkv, N, d, Bs, S = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment
         nb, G = N // Bs, Hq // Hkv
         flop_per_block = 4.0 * Bs * Bs * d
-        dense_blocks = B * Hq * nb * (nb + 1) // 2
+        dense_blocks = B * Hq * nb * (nb + 1) // 2 - diag_skipped_blocks(B, Hq, nb, Bs)
         od = torch.empty_like(q)
         dense = stats(time_calls(lambda: P.pbs_attn_fwd(sh, q, k, v, None, None, None, None, scale,
                                                         od, None, stream=stream), steps, 2, flush, stream))
@@ -192,7 +200,8 @@ def measure_configs(args, flush, stream, dev, skip: str) -> dict:
                 pre.append(ev[0].elapsed_time(ev[1]))
                 att.append(ev[1].elapsed_time(ev[2]))
             prefill = stats(np.array(pre) + np.array(att))
-            computed = int(bf.counts.sum().item()) + own_segment_blocks(bf.perm.cpu().numpy(), Bs, S, G)
+            computed = (int(bf.counts.sum().item()) + own_segment_blocks(bf.perm.cpu().numpy(), Bs, S, G)
+                        - diag_skipped_blocks(B, Hq, nb, Bs))
             att_mean = float(np.mean(att))
             tflops = computed * flop_per_block / (att_mean * 1e-3) / 1e12
             points.append({
@@ -540,7 +549,8 @@ def sweep_main(args):
         B, Hq, Hkv, N, d, Bs, S = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment
         nb, bps, G = N // Bs, S // Bs, Hq // Hkv
         counts = bf.counts.cpu().numpy().astype(np.int64)
-        computed = int(counts.sum()) + own_segment_blocks(bf.perm.cpu().numpy(), Bs, S, G)
+        computed = (int(counts.sum()) + own_segment_blocks(bf.perm.cpu().numpy(), Bs, S, G)
+                    - diag_skipped_blocks(B, Hq, nb, Bs))
         flop_per_block = 4.0 * Bs * Bs * d
         od = torch.empty_like(q)
         for _ in range(max(1, args.warmup)):
@@ -557,7 +567,7 @@ def sweep_main(args):
         dense_s = stats(dts)
         dense = dense_s["median"]
         diff_dense = float((od.float() - bf.o.float()).abs().max().item()) if keep >= 1.0 else None
-        dense_blocks = B * Hq * nb * (nb + 1) // 2
+        dense_blocks = B * Hq * nb * (nb + 1) // 2 - diag_skipped_blocks(B, Hq, nb, Bs)
         res.append({"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} block={Bs} segment={S}",
                     "keep": keep, "prefill_ms": round(pre + att, 4), "attention_ms": round(att, 4),
                     "score_permute_select_ms": round(pre, 4), "dense_causal_ms": round(dense, 4),
@@ -755,12 +765,15 @@ def main():
     B, Hq, Hkv, N, d, Bs, S = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.block, w.segment
     nb, bps, G = N // Bs, S // Bs, Hq // Hkv
     counts = bf.counts.cpu().numpy().astype(np.int64)
-    # kept earlier-segment blocks in full, plus the own segment's visible keys (32-key stages)
-    computed = int(counts.sum()) + own_segment_blocks(bf.perm.cpu().numpy(), Bs, S, G)
+    # kept earlier-segment blocks in full, plus the own segment's visible keys (32-key stages),
+    # less the diagonal tiles a wave skips because all their keys follow its rows
+    computed = (int(counts.sum()) + own_segment_blocks(bf.perm.cpu().numpy(), Bs, S, G)
+                - diag_skipped_blocks(B, Hq, nb, Bs))
     computed = int(round(computed)) if abs(computed - round(computed)) < 1e-6 else round(computed, 3)
     flop_per_block = 4.0 * Bs * Bs * d
     attn_flops = computed * flop_per_block
-    dense_blocks = B * Hq * nb * (nb + 1) // 2
+    dense_blocks = B * Hq * nb * (nb + 1) // 2 - diag_skipped_blocks(B, Hq, nb, Bs)
+    dense_blocks = int(round(dense_blocks)) if abs(dense_blocks - round(dense_blocks)) < 1e-6 else dense_blocks
     attn_ms = float(stage[3])
     eff_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
 
@@ -787,7 +800,8 @@ def main():
                                                                stream=stream),
                                 args.steps, max(1, args.warmup), flush, stream))["mean"]
         own_nat = B * Hq * int((np.arange(nb) % bps + 1).sum())
-        h_blocks = int(counts.sum()) + own_nat
+        h_blocks = int(counts.sum()) + own_nat - diag_skipped_blocks(B, Hq, nb, Bs)
+        h_blocks = int(round(h_blocks)) if abs(h_blocks - round(h_blocks)) < 1e-6 else h_blocks
         h_tflops = h_blocks * flop_per_block / (h_ms * 1e-3) / 1e12
         max_diff = float((o_h.float() - bf.o.float()).abs().max().item())
         hybrid = {"attention_ms": round(h_ms, 4),
@@ -965,7 +979,8 @@ def main():
             "traffic": traffic,
             "work_per_launch": (f"{computed} computed blocks x {flop_per_block / 1e6:.3f} MFLOP "
                                 "(selected off-diagonal blocks + visible own-segment keys in "
-                                f"32-key stages / {Bs})"),
+                                f"32-key stages / {Bs}, less the 32x32 diagonal tiles whose keys "
+                                "all follow their rows)"),
         },
         "hip_graph_replay": graph,
         "library_gemm_reference": gemm,

@@ -39,3 +39,18 @@ def test_own_segment_work_sees_a_broken_permutation():
     late = int(np.argmax(bad[0, 0, :S]))         # the key at position S-1 ...
     bad[0, 0, late] = 0                            # ... now repeats position 0: seen too early
     assert bench.own_segment_blocks(bad, Bs, S, G) != tri
+
+
+def test_diagonal_skip_count_brute_force():
+    """The diagonal tiles the attention kernel skips: a 32-row wave tile and a 32-key stage of a
+    query block's own Bs positions are skipped when no (row, key) pair in them is causal-visible.
+    Counted element by element on every tile of one Bs x Bs diagonal block."""
+    for Bs in (64, 128):
+        rows = np.arange(Bs)
+        visible = rows[:, None] >= rows[None, :]          # key position <= row position
+        W = Bs // 32
+        skipped = sum(1 for w in range(W) for s in range(W)
+                      if not visible[w * 32:(w + 1) * 32, s * 32:(s + 1) * 32].any())
+        per_block = skipped / (W * W)                     # block-equivalents per query block
+        B, Hq, nb = 2, 3, 5
+        assert bench.diag_skipped_blocks(B, Hq, nb, Bs) == B * Hq * nb * per_block

@@ -10,9 +10,10 @@
 //
 // Three kernels, the matrix work on v_mfma_f32_32x32x16_bf16 with S^T = K Q^T (a lane owns one
 // scoring row in the first, one key column in the last):
-//  1. stats:   per (segment, chunk of keys, row) the softmax max m (log2 units) and sum l over
-//              the chunk, streaming its keys through LDS.  Segments are split into chunks of at
-//              most 1024 keys so that enough workgroups run to hide the loads' latency;
+//  1. stats:   per (segment, chunk of keys, row) a reference m (log2 units) and the sum l of
+//              exp2(z - m) over the chunk, streaming its keys through LDS.  Segments are split
+//              into chunks of at most 1024 keys so that enough workgroups run to hide the loads'
+//              latency;
 //  2. combine: per (segment, row) the chunks' (m, l) merged into one log2-normaliser
 //              L = m + log2(l);
 //  3. reduce:  per key, the sum over all rows of exp2(z - L).  A wave owns 32 keys for the whole
@@ -25,6 +26,7 @@
 // workgroup streams each K tile once for 256 scoring rows, a reduce workgroup stages each chunk
 // of rows once for 256 keys.
 #include <mutex>
+#include <type_traits>
 
 #include "pbs_device.h"
 #include "pbs_internal.h"
@@ -97,50 +99,65 @@ __global__ __launch_bounds__(64 * kStatWaves) void score_stats_kernel(ScoreArgs 
   const size_t krs = static_cast<size_t>(a.km.stride());
   const int kbeg = sigma * a.S + ch * a.chunk;
   const int first_row = end - a.Bs;   // every scoring row is >= first_row
+  // (m, l): the lane's reference (log2 units) and its sum of exp2(z - m) over the chunk.  The
+  // reference is fixed at the max of the first 32 keys this lane's row sees, so later keys need
+  // no max and no rescaling; the chunk's sum then holds terms up to exp2(max - m).  If a sum leaves
+  // [0, 2^100] (a later key far above the reference), the workgroup runs the chunk again with a
+  // running max, rescaling at every 32 keys (ONLINE).
   float m = -INFINITY, l = 0.f;
-  for (int k0 = kbeg; k0 < kbeg + a.chunk; k0 += kStatKeys) {
-    __syncthreads();
-    {
-      const uint16_t* kb = a.k + a.km.off(b, h, k0);
-      constexpr int CH = D / 8;
-      for (int c = tid; c < kStatKeys * CH; c += 64 * kStatWaves) {
-        const int rr = c / CH, col = (c % CH) * 8;
-        *reinterpret_cast<u32x4*>(&Ks[rr * STR + col]) =
-            *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(rr) * krs + col);
-      }
-    }
-    __syncthreads();
-    if (!active) continue;
-    const bool causal = k0 + kStatKeys - 1 > first_row;   // uniform: a key may follow a row
-#pragma unroll
-    for (int kt = 0; kt < kStatKeys / 32; ++kt) {
-      f32x16 s;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-      const uint16_t* krow = &Ks[(kt * 32 + c32) * STR + hl * 8];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(krow + ks * 16),
-                                                     qf[ks], s, 0, 0, 0);
-      if (causal) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kt * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
-          if (key > t) s[e] = -INFINITY;
+  auto chunk_pass = [&](auto online_tag) {
+    constexpr bool ONLINE = decltype(online_tag)::value;
+    m = -INFINITY;
+    l = 0.f;
+    for (int k0 = kbeg; k0 < kbeg + a.chunk; k0 += kStatKeys) {
+      __syncthreads();
+      {
+        const uint16_t* kb = a.k + a.km.off(b, h, k0);
+        constexpr int CH = D / 8;
+        for (int c = tid; c < kStatKeys * CH; c += 64 * kStatWaves) {
+          const int rr = c / CH, col = (c % CH) * 8;
+          *reinterpret_cast<u32x4*>(&Ks[rr * STR + col]) =
+              *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(rr) * krs + col);
         }
       }
-      float mx = -INFINITY;
+      __syncthreads();
+      if (!active) continue;
+      const bool causal = k0 + kStatKeys - 1 > first_row;   // uniform: a key may follow a row
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-      const float m_new = fmaxf(m, mx * a.c);   // a.c > 0: the max commutes with the scaling
-      if (m_new == -INFINITY) continue;
-      float acc = 0.f;
+      for (int kt = 0; kt < kStatKeys / 32; ++kt) {
+        f32x16 s;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc += fast_exp2(fmaf(s[e], a.c, -m_new));
-      l = l * fast_exp2(m - m_new) + acc;
-      m = m_new;
+        for (int e = 0; e < 16; ++e) s[e] = 0.f;
+        const uint16_t* krow = &Ks[(kt * 32 + c32) * STR + hl * 8];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(krow + ks * 16),
+                                                       qf[ks], s, 0, 0, 0);
+        if (causal) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = k0 + kt * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+            if (key > t) s[e] = -INFINITY;
+          }
+        }
+        if (ONLINE || m == -INFINITY) {   // a.c > 0: the max commutes with the scaling
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+          const float m_new = fmaxf(m, mx * a.c);
+          if (m_new == -INFINITY) continue;   // no key of the row yet
+          if (ONLINE) l *= fast_exp2(m - m_new);
+          m = m_new;
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc += fast_exp2(fmaf(s[e], a.c, -m));
+        l += acc;
+      }
     }
-  }
+  };
+  chunk_pass(std::false_type{});
+  if (__syncthreads_or((active && !(l <= 0x1p100f)) ? 1 : 0)) chunk_pass(std::true_type{});
   if (!active) return;
   // merge the two half-waves (same row, different keys)
   const float m2 = __shfl_xor(m, 32);

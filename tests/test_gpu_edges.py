@@ -7,7 +7,7 @@ import block_sparse_attention_pbs_amd as P
 import oracle
 import pbs_synth
 from gpu_helpers import (check_attn, dev, dev_bf16, inverse_of, lists_equal, run_attn, run_permute,
-                         run_select, say, shape)
+                         run_score, run_select, say, shape)
 
 pytestmark = pytest.mark.gpu
 
@@ -283,6 +283,25 @@ def test_dominant_late_key_dense():
     o, lse = run_attn(sh, dev_bf16(q), dev_bf16(k), dev_bf16(v), None, None, None, None, scale)
     check_attn(o.float().cpu().numpy(), od, "dominant key dense")
     assert np.abs(lse.cpu().numpy() - ol).max() < 1e-3
+
+
+def test_scores_dominant_late_key():
+    """Key scores where one key of a segment lies about 150 (log2 units) above the first keys
+    its scoring rows see: the scoring pass's fixed reference would overflow its sum, so the
+    chunk is run again with a running max.  Scores against the oracle: relative 1e-4 where they
+    are representable, and every segment still sums to one."""
+    say("scores, dominant late key")
+    q, k, _ = _dominant_key_inputs(23)
+    scale = oracle.default_scale(128)
+    N, Bs, S = 2048, 128, 512
+    ref = oracle.key_scores(q, k, block=Bs, segment=S, scale=scale).astype(np.float64)
+    assert ref[0, 0, 700] > 0.95            # the key takes nearly all of its segment's mass
+    sh = shape(1, 2, 1, N, 128, Bs, S)
+    s = run_score(sh, dev_bf16(q), dev_bf16(k), scale).cpu().numpy().astype(np.float64)
+    big = ref > 1e-30
+    assert (np.abs(s - ref)[big] <= 1e-4 * ref[big]).all()
+    assert (np.abs(s - ref)[~big] <= 1e-30).all()
+    assert np.allclose(s.reshape(1, 1, -1, S).sum(-1), 1.0, atol=1e-4)
 
 
 @pytest.mark.parametrize("permuted", [True, False])

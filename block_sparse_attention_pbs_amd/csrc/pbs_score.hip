@@ -11,16 +11,18 @@
 // Three kernels, the matrix work on v_mfma_f32_32x32x16_bf16 with S^T = K Q^T (a lane owns one
 // scoring row in the first, one key column in the last):
 //  1. stats:   per (segment, chunk of keys, row) a reference m (log2 units) and the sum l of
-//              exp2(z - m) over the chunk, streaming its keys through LDS.  Segments are split
-//              into chunks of at most 1024 keys so that enough workgroups run to hide the loads'
-//              latency;
+//              exp2(z - m) over the chunk, streaming its keys through LDS in tiles of 128 keys
+//              (64 where 128 does not divide the chunk), the next tile loaded into registers
+//              while the current one is computed.  Segments are split into chunks of at most
+//              1024 keys so that enough workgroups run to hide the loads' latency;
 //  2. combine: per (segment, row) the chunks' (m, l) merged into one log2-normaliser
 //              L = m + log2(l);
 //  3. reduce:  per key, the sum over all rows of exp2(z - L).  A wave owns 32 keys for the whole
 //              pass (its K fragments stay in registers); the rows stream through LDS in chunks
-//              of 32; each lane accumulates its 16 keys over its rows in fp32 and a final
-//              butterfly over the 32 lanes of each half-wave (wavefront reduction) gives the
-//              per-key sum, scaled by 1/R.
+//              of 64 (the next chunk loaded into registers while the current one is computed,
+//              32 rows per MFMA chain); each lane accumulates its 16 keys over its rows in
+//              fp32, in row order, and a final butterfly over the 32 lanes of each half-wave
+//              (wavefront reduction) gives the per-key sum, scaled by 1/R.
 // A key can be after a scoring row only in the last Bs positions of the sequence, so only tiles
 // that reach them apply the causal test.  Both passes run eight waves per workgroup: a stats
 // workgroup streams each K tile once for 256 scoring rows, a reduce workgroup stages each chunk
@@ -64,7 +66,7 @@ __device__ __forceinline__ void score_row(const ScoreArgs& a, int r, int end, in
   t = min(max(end - a.Bs + (r & (a.Bs - 1)), 0), a.N - 1);
 }
 
-constexpr int kStatKeys = 64;  // keys per LDS tile in the stats pass
+constexpr int kStatKeys = 64;   // stats chunks are multiples of this LDS tile; 128-key tiles where they divide
 #ifndef PBS_SCORE_STAT_WAVES
 #define PBS_SCORE_STAT_WAVES 8
 #endif
@@ -74,11 +76,11 @@ constexpr int kStatKeys = 64;  // keys per LDS tile in the stats pass
 constexpr int kStatWaves = PBS_SCORE_STAT_WAVES;  // waves (32 scoring rows each) per stats workgroup
 constexpr int kRedWaves = PBS_SCORE_RED_WAVES;    // waves (32 keys each) per reduce workgroup
 
-template <int D>
+template <int D, int TK>   // TK: keys per LDS tile (64 or 128; divides the chunk)
 __global__ __launch_bounds__(64 * kStatWaves) void score_stats_kernel(ScoreArgs a) {
   constexpr int STR = D + 8;
   constexpr int NKS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kStatKeys * STR];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[TK * STR];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, c32 = lane & 31;
   const int sigma = blockIdx.x / a.nchunk, ch = blockIdx.x - sigma * a.nchunk;
@@ -109,22 +111,34 @@ __global__ __launch_bounds__(64 * kStatWaves) void score_stats_kernel(ScoreArgs 
     constexpr bool ONLINE = decltype(online_tag)::value;
     m = -INFINITY;
     l = 0.f;
-    for (int k0 = kbeg; k0 < kbeg + a.chunk; k0 += kStatKeys) {
+    // Staging: thread tid copies 16-byte pieces tid, tid + 64*waves, ... of each K tile; the next
+    // tile's pieces are loaded into registers before the current tile is computed.
+    constexpr int CH = D / 8;
+    constexpr int NPT = TK * CH / (64 * kStatWaves);
+    static_assert(NPT * 64 * kStatWaves == TK * CH, "whole 16-byte pieces per thread");
+    u32x4 kv[NPT];
+    auto load_tile = [&](int k0) {
+      const uint16_t* kb = a.k + a.km.off(b, h, k0);
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int c = tid + i * 64 * kStatWaves, rr = c / CH, col = (c % CH) * 8;
+        kv[i] = *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(rr) * krs + col);
+      }
+    };
+    load_tile(kbeg);
+    for (int k0 = kbeg; k0 < kbeg + a.chunk; k0 += TK) {
       __syncthreads();
-      {
-        const uint16_t* kb = a.k + a.km.off(b, h, k0);
-        constexpr int CH = D / 8;
-        for (int c = tid; c < kStatKeys * CH; c += 64 * kStatWaves) {
-          const int rr = c / CH, col = (c % CH) * 8;
-          *reinterpret_cast<u32x4*>(&Ks[rr * STR + col]) =
-              *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(rr) * krs + col);
-        }
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int c = tid + i * 64 * kStatWaves, rr = c / CH, col = (c % CH) * 8;
+        *reinterpret_cast<u32x4*>(&Ks[rr * STR + col]) = kv[i];
       }
       __syncthreads();
+      if (k0 + TK < kbeg + a.chunk) load_tile(k0 + TK);
       if (!active) continue;
-      const bool causal = k0 + kStatKeys - 1 > first_row;   // uniform: a key may follow a row
+      const bool causal = k0 + TK - 1 > first_row;   // uniform: a key may follow a row
 #pragma unroll
-      for (int kt = 0; kt < kStatKeys / 32; ++kt) {
+      for (int kt = 0; kt < TK / 32; ++kt) {
         f32x16 s;
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -191,8 +205,9 @@ template <int D>
 __global__ __launch_bounds__(64 * kRedWaves) void score_reduce_kernel(ScoreArgs a) {
   constexpr int STR = D + 8;
   constexpr int NKS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[32 * STR];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * STR];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so the chunk loop is scalar
   const int hl = lane >> 5, c32 = lane & 31;
   const int bh = blockIdx.y;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
@@ -216,45 +231,72 @@ __global__ __launch_bounds__(64 * kRedWaves) void score_reduce_kernel(ScoreArgs 
   const float* st_seg = a.lse2 + (static_cast<size_t>(bh) * a.nseg + sigma) * a.R;
   const int end = seq_end(a, sigma);
   const bool causal = active && key0 + 31 > end - a.Bs;   // uniform: a key may follow a row
-  // The rows' log2-normalisers are read one chunk ahead (R is a multiple of 32; the last chunk
-  // reads its own again), so their load is in flight while the chunk before them is computed.
-  float l2_next = active ? st_seg[c32] : 0.f;
-  for (int rc = 0; rc < a.R; rc += 32) {
+  // Rows are staged RC at a time (RC divides Bs, so a staged chunk is one query head's
+  // consecutive positions t0 ... t0 + RC - 1, clamped at 0 for a sequence shorter than Bs) and
+  // computed 32 at a time.  Thread tid copies the 16-byte pieces tid, tid + 64*waves, ... (piece c:
+  // row c / (D/8), column chunk c % (D/8)); the next chunk's pieces and log2-normalisers are
+  // loaded into registers before the current chunk is computed.
+  constexpr int RC = 64, NSUB = RC / 32;
+  constexpr int CH = D / 8, NPIECE = RC * CH;
+  constexpr int NPT = (NPIECE + 64 * kRedWaves - 1) / (64 * kRedWaves);
+  const size_t qstride = static_cast<size_t>(a.qm.stride());
+  auto load_chunk = [&](int rc, u32x4 (&qv)[NPT]) {
+    const int t0 = end - a.Bs + (rc & (a.Bs - 1));
+    const uint16_t* head = a.q + a.qm.off(b, h * a.G + (rc >> a.bs_log2), 0);
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int c = tid + i * 64 * kRedWaves;
+      if (NPIECE % (64 * kRedWaves) == 0 || c < NPIECE)
+        qv[i] = *reinterpret_cast<const u32x4*>(
+            head + static_cast<size_t>(max(t0 + c / CH, 0)) * qstride + (c % CH) * 8);
+    }
+  };
+  u32x4 qv[NPT];
+  load_chunk(0, qv);
+  float l2c[NSUB];
+#pragma unroll
+  for (int j = 0; j < NSUB; ++j) l2c[j] = active ? st_seg[j * 32 + c32] : 0.f;
+  for (int rc = 0; rc < a.R; rc += RC) {
     __syncthreads();
-    {
-      constexpr int CH = D / 8;
-      for (int c = tid; c < 32 * CH; c += 64 * kRedWaves) {
-        const int rr = c / CH, col = (c % CH) * 8;
-        int gl, tt;
-        score_row(a, rc + rr, end, gl, tt);
-        const uint16_t* src = a.q + a.qm.off(b, h * a.G + gl, tt) + col;
-        *reinterpret_cast<u32x4*>(&Qs[rr * STR + col]) = *reinterpret_cast<const u32x4*>(src);
-      }
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int c = tid + i * 64 * kRedWaves;
+      if (NPIECE % (64 * kRedWaves) == 0 || c < NPIECE)
+        *reinterpret_cast<u32x4*>(&Qs[(c / CH) * STR + (c % CH) * 8]) = qv[i];
     }
     __syncthreads();
+    const int rn = __builtin_amdgcn_readfirstlane(rc + RC);
+    if (rn < a.R) load_chunk(rn, qv);
     if (!active) continue;
-    const float nl = -l2_next;
-    l2_next = st_seg[min(rc + 32, a.R - 32) + c32];
-    f32x16 s;
+    float nl[NSUB];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = 0.f;
-    const uint16_t* qrow = &Qs[c32 * STR + hl * 8];
+    for (int j = 0; j < NSUB; ++j) {
+      nl[j] = -l2c[j];
+      l2c[j] = st_seg[min(rn, a.R - RC) + j * 32 + c32];
+    }
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], *reinterpret_cast<const bf16x8*>(qrow + ks * 16),
-                                                   s, 0, 0, 0);
-    // lane column = scoring row rc + c32; lane value e = key key0 + (e/4)*8 + hl*4 + e%4
-    if (causal) {
-      int gl, tt;
-      score_row(a, rc + c32, end, gl, tt);
+    for (int j = 0; j < NSUB; ++j) {
+      f32x16 s;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = key0 + (e >> 2) * 8 + hl * 4 + (e & 3);
-        if (key <= tt) acc[e] += fast_exp2(fmaf(s[e], a.c, nl));
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+      const uint16_t* qrow = &Qs[(j * 32 + c32) * STR + hl * 8];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], *reinterpret_cast<const bf16x8*>(qrow + ks * 16),
+                                                     s, 0, 0, 0);
+      // lane column = scoring row rc + 32j + c32; lane value e = key key0 + (e/4)*8 + hl*4 + e%4
+      if (causal) {
+        int gl, tt;
+        score_row(a, rc + j * 32 + c32, end, gl, tt);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = key0 + (e >> 2) * 8 + hl * 4 + (e & 3);
+          if (key <= tt) acc[e] += fast_exp2(fmaf(s[e], a.c, nl[j]));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += fast_exp2(fmaf(s[e], a.c, nl[j]));
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] += fast_exp2(fmaf(s[e], a.c, nl));
     }
   }
   if (!active) return;
@@ -276,7 +318,9 @@ __global__ __launch_bounds__(64 * kRedWaves) void score_reduce_kernel(ScoreArgs 
 template <int D>
 hipError_t launch_score_t(const Dims& d, const ScoreArgs& a, hipStream_t stream) {
   dim3 g1(d.nseg * a.nchunk, (a.R + 32 * kStatWaves - 1) / (32 * kStatWaves), d.B * d.Hkv);
-  hipError_t e = launch(score_stats_kernel<D>, g1, dim3(64 * kStatWaves), 0, stream, a);
+  hipError_t e = (a.chunk % 128 == 0)
+                    ? launch(score_stats_kernel<D, 128>, g1, dim3(64 * kStatWaves), 0, stream, a)
+                    : launch(score_stats_kernel<D, 64>, g1, dim3(64 * kStatWaves), 0, stream, a);
   if (e != hipSuccess) return e;
   dim3 gc((d.nseg * a.R + 255) / 256, d.B * d.Hkv);
   e = launch(score_combine_kernel, gc, dim3(256), 0, stream, a);

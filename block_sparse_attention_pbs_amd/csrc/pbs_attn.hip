@@ -14,7 +14,9 @@
 //    sees every key of every visited block, so no cross-wave reduction is needed;
 //  * keys stream through LDS in stages of 32 keys, double-buffered and filled by asynchronous
 //    direct buffer->LDS loads (buffer_load_dwordx4 ... lds, bounds-checked) one stage ahead of
-//    the compute.  A workgroup needs at most ~52 KiB of LDS and 168 VGPRs per lane, so three
+//    the compute; a wave issues its share of the next stage's loads one by one between the
+//    MFMAs of the current stage's score chain, where their issue costs no MFMA time, and reads
+//    the first K fragments of a stage right after the barrier that lands it.  A workgroup needs at most ~52 KiB of LDS and 168 VGPRs per lane, so three
 //    workgroups share a CU (three waves per SIMD): while one waits or runs its softmax, the
 //    others keep the matrix cores busy;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 (A = K rows from
@@ -43,11 +45,22 @@
 //  * work order: heaviest query blocks first, and consecutive workgroups of one XCD (the
 //    hardware deals workgroups round-robin over the 8 XCDs) walk one KV head, so the K/V tiles a
 //    head's query blocks share stay in that XCD's L2.
+#include <type_traits>
+
 #include "pbs_device.h"
 #include "pbs_internal.h"
 
 namespace pbs {
 namespace {
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 struct AttnArgs {
   const uint16_t* q;
@@ -87,7 +100,7 @@ struct AttnArgs {
 constexpr int kStageKeys = PBS_ATTN_STAGE_KEYS;  // keys per LDS stage
 constexpr int kOffWindow = 1792; // off-diagonal list entries held in LDS at a time
 constexpr int kOwnMax = 256;     // own-segment blocks (S / Bs <= 16384 / 64)
-constexpr int kRing = 3;         // key-stream stages whose slots are held in LDS (mode 1)
+constexpr int kRing = 4;         // key-stream stages whose slots are held in LDS (mode 1)
 
 template <int D, int BS>
 struct Cfg {
@@ -344,43 +357,120 @@ __device__ __forceinline__ void issue_ring(const Rsrc& rr, const StageIter& it, 
 // A key-stream stage gathers its rows: row r of the stage is the slot slots[r] of the own
 // segment, read through buffer resources that span only that segment, so a slot outside it
 // reads zeros instead of another segment's or head's memory.
+//
+// The loads of a stage are numbered items, issued one by one (item I by piece I, the last piece
+// taking every item left), so that a caller can spread them over the MFMAs of the stage it
+// computes meanwhile.  Gathered stage: items 0 .. UK-1 are its K loads, UK .. UK+UV-1 its V
+// loads, then the positions of a masked stage and, last, the slots of a later stream stage into
+// the ring.  Their slots are read from LDS into registers first (read()), before any item.
+template <int D, int BS>
+struct Gather {
+  using C = Cfg<D, BS>;
+  // Load u of wave w is load w + u*NW of the stage; only the last u can pass the last load (UK,
+  // UV round up): a wave with fewer loads than the others repeats the last one (the same bytes
+  // to the same place).  Straight-line code, no lane masks.
+  static constexpr int UK = (C::NGK + C::NW - 1) / C::NW, UV = (C::NGV + C::NW - 1) / C::NW;
+  static constexpr int NI = UK + UV + 2;
+  uint32_t sk[UK], sv[UV];
+  __device__ __forceinline__ void read(const Stage& st, int w, int lane) {
+    const int rk = lane / C::KROW, rv = lane / C::VROW;
+    const int32_t* slk = st.slots + rk + w * C::RK;
+    const int32_t* slv = st.slots + rv + w * C::RV;
+#pragma unroll
+    for (int u = 0; u + 1 < UK; ++u) sk[u] = static_cast<uint32_t>(slk[u * C::NW * C::RK]);
+    sk[UK - 1] =
+        static_cast<uint32_t>(st.slots[rk + min(w + (UK - 1) * C::NW, C::NGK - 1) * C::RK]);
+#pragma unroll
+    for (int u = 0; u + 1 < UV; ++u) sv[u] = static_cast<uint32_t>(slv[u * C::NW * C::RV]);
+    sv[UV - 1] =
+        static_cast<uint32_t>(st.slots[rv + min(w + (UV - 1) * C::NW, C::NGV - 1) * C::RV]);
+  }
+  // cok / cov: this lane's chunk offset minus the segment's first row, so that one 24-bit
+  // multiply-add turns a global slot into an offset in the segment.  `ring` issues the last
+  // item (the caller's load of a later stream stage's slots).
+  template <int I, class Ring>
+  __device__ __forceinline__ void item(const AttnArgs& a, const Rsrc& rr, const Stage& st,
+                                       uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w, int lane,
+                                       uint32_t cok, uint32_t cov, Ring&& ring) const {
+    const uint32_t rowb = static_cast<uint32_t>(a.kv_rs) * 2;   // < 2^24: checked on the host
+    if constexpr (I < UK) {
+      const int j = min(w + I * C::NW, C::NGK - 1);
+      load_lds16_free(rr.ks, Kst + j * C::RK * C::KROW * 8, __umul24(sk[I], rowb) + cok, 0u);
+    } else if constexpr (I < UK + UV) {
+      const int j = min(w + (I - UK) * C::NW, C::NGV - 1);
+      load_lds16_free(rr.vs, Vst + j * C::RV * C::VROW * 8, __umul24(sv[I - UK], rowb) + cov, 0u);
+    } else if constexpr (I == UK + UV) {
+      if (st.masked && w == 0 && lane < C::SK)
+        load_lds4(rr.p, Pst, static_cast<uint32_t>(st.slots[lane]) * 4, 0u);
+    } else {
+      ring();
+    }
+  }
+};
+
 template <int D, int BS>
 __device__ __forceinline__ void issue_gathered(const AttnArgs& a, const Rsrc& rr, Stage st,
                                                uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
                                                int lane, uint32_t cok, uint32_t cov) {
+  // Every slot is read before the first load is issued: the loads are asm with side effects,
+  // which the compiler never moves an LDS read across, so reading the slots in between would
+  // wait out one LDS round trip per load.
+  Gather<D, BS> gt;
+  gt.read(st, w, lane);
+  static_for<0, Gather<D, BS>::NI - 1>([&](auto i) {
+    gt.template item<decltype(i)::value>(a, rr, st, Kst, Vst, Pst, w, lane, cok, cov, [] {});
+  });
+}
+
+// The loads of a contiguous (key-block) stage as numbered items: item I < UKB is this wave's
+// K load I, then its V loads, then (permuted queries only) the positions of a masked stage.
+template <int D, int BS, int MODE>
+struct BlockLoads {
   using C = Cfg<D, BS>;
-  const uint32_t rowb = static_cast<uint32_t>(a.kv_rs) * 2;   // < 2^24: checked on the host
-  // Straight-line code (no lane masks, no branches).  Every slot is read from the ring before
-  // the first load is issued: the loads are asm with side effects, which the compiler never
-  // moves an LDS read across, so reading the slots in between would wait out one LDS round
-  // trip per load.  A wave with fewer loads than the others repeats the last one (the same
-  // bytes to the same place).  cok / cov: this lane's chunk offset minus the segment's first
-  // row, so that one 24-bit multiply-add turns a global slot into an offset in the segment.
-  constexpr int UK = (C::NGK + C::NW - 1) / C::NW, UV = (C::NGV + C::NW - 1) / C::NW;
-  const int rk = lane / C::KROW, rv = lane / C::VROW;
-  // Load u of wave w is load w + u*NW of the stage; only the last u can pass the last load
-  // (UK, UV round up), so the others are a fixed offset from one per-stage address.
-  uint32_t sk[UK], sv[UV];
-  const int32_t* slk = st.slots + rk + w * C::RK;
-  const int32_t* slv = st.slots + rv + w * C::RV;
-#pragma unroll
-  for (int u = 0; u + 1 < UK; ++u) sk[u] = static_cast<uint32_t>(slk[u * C::NW * C::RK]);
-  sk[UK - 1] = static_cast<uint32_t>(st.slots[rk + min(w + (UK - 1) * C::NW, C::NGK - 1) * C::RK]);
-#pragma unroll
-  for (int u = 0; u + 1 < UV; ++u) sv[u] = static_cast<uint32_t>(slv[u * C::NW * C::RV]);
-  sv[UV - 1] = static_cast<uint32_t>(st.slots[rv + min(w + (UV - 1) * C::NW, C::NGV - 1) * C::RV]);
-#pragma unroll
-  for (int u = 0; u < UK; ++u) {
-    const int j = min(w + u * C::NW, C::NGK - 1);
-    load_lds16_free(rr.ks, Kst + j * C::RK * C::KROW * 8, __umul24(sk[u], rowb) + cok, 0u);
+  static constexpr int UKB = (C::NLDK + C::NW - 1) / C::NW, UVB = (C::NLDV + C::NW - 1) / C::NW;
+  static constexpr int NI = UKB + UVB + (MODE == 4 ? 1 : 0);
+  template <int I>
+  __device__ __forceinline__ static void item(const AttnArgs& a, const Rsrc& rr, const Stage& st,
+                                              uint16_t* Kst, uint16_t* Vst, int32_t* Pst, int w,
+                                              int lane, bool more) {
+    const uint32_t base = static_cast<uint32_t>(st.key0) * static_cast<uint32_t>(a.kv_rs) * 2;
+    if constexpr (I < UKB) {
+      const int n = w + I * C::NW;
+      const int P = n * 64 + lane;
+      const int r = P / (C::CPR + C::KPAD), pc = P - r * (C::CPR + C::KPAD);
+      // A partial last load (KCH not a multiple of 64) runs its tail lanes too: they write the
+      // spare rows behind the tile (never read) with the next rows of the head, or zeros past
+      // its end, so the only test is the wave-uniform one.
+      static_assert(C::KCH % 64 == 0 || (C::KTILE_A - C::KTILE) / 8 >= 64 - C::KCH % 64,
+                    "spare rows take a partial load's tail");
+      if (more && n < C::NLDK)
+        load_lds16(st.orig ? rr.k2 : rr.k, Kst + n * 512,
+                   static_cast<uint32_t>((r * a.kv_rs + (pc < C::CPR ? pc : 0) * 8) * 2), base);
+    } else if constexpr (I < UKB + UVB) {
+      const int n = w + (I - UKB) * C::NW;
+      const int P = n * 64 + lane;
+      const int r = P / (C::CPR + C::VPAD), pc = P - r * (C::CPR + C::VPAD);
+      static_assert(C::VCH % 64 == 0 || (C::VTILE_A - C::VTILE) / 8 >= 64 - C::VCH % 64,
+                    "spare rows take a partial load's tail");
+      if (more && n < C::NLDV)
+        load_lds16(st.orig ? rr.v2 : rr.v, Vst + n * 512,
+                   static_cast<uint32_t>((r * a.kv_rs + (pc < C::CPR ? pc : 0) * 8) * 2), base);
+    } else {
+      if (more && st.masked && w == 0 && lane < C::SK)
+        load_lds4(rr.p, Pst, static_cast<uint32_t>(lane * 4), static_cast<uint32_t>(st.key0) * 4);
+    }
   }
-#pragma unroll
-  for (int u = 0; u < UV; ++u) {
-    const int j = min(w + u * C::NW, C::NGV - 1);
-    load_lds16_free(rr.vs, Vst + j * C::RV * C::VROW * 8, __umul24(sv[u], rowb) + cov, 0u);
+};
+
+// Items [U, U+1) of N, the last piece (U == NP - 1) taking every item from U on.
+template <int U, int NP, int N, class F>
+__device__ __forceinline__ void piece_items(F&& f) {
+  if constexpr (U >= 0 && U < N) {
+    if constexpr (U + 1 < NP)
+      f(std::integral_constant<int, U>{});
+    else
+      static_for<U, N>(f);
   }
-  if (st.masked && w == 0 && lane < C::SK)
-    load_lds4(rr.p, Pst, static_cast<uint32_t>(st.slots[lane]) * 4, 0u);
 }
 
 template <int D, int BS, bool MAYBE_STREAM = true>
@@ -477,39 +567,45 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
                                            const int32_t* Ps, int key0, int lane, int t,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NKS],
                                            f32x16 (&oacc)[Cfg<D, BS>::NMT], RowState& rs,
-                                           Pre&& pre, bool skip = false) {
+                                           const bf16x8 (&k01)[2], Pre&& pre, bool skip = false) {
   using C = Cfg<D, BS>;
   const int hl = lane >> 5;
   const int c32 = lane & 31;
   const int gp = lane >> 4, li = lane & 15;
+  static_assert(C::NKT == 1, "one 32-key sub-tile per stage");
   f32x16 s[C::NKT];
-  {
-    bf16x8 k0[C::NKT];
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt)
-      k0[kt] = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kt * 32 + c32, hl * 8)]);
-    pre();   // the next stage's loads, if the caller issues them here
-    if (skip) return;   // wave-uniform: nothing of this stage reaches the wave's rows
-    if constexpr (MASKED) {
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            k0[kt], qf[0], mask_init<MODE>(Ps, key0, kt, hl, t), 0, 0, 0);
+  // The next stage's loads go out in pieces between the MFMAs of this stage's score chain:
+  // pre(-1) (address reads) before the first MFMA, pre(u) after MFMA u, so that their issue
+  // and the latency of the address reads sit in the shadow of the chain.  A skipped stage
+  // issues every piece and returns.
+  // K fragments are read two k-steps ahead of their MFMA, in source order before the load piece
+  // of that step (the block loads are ordered against LDS accesses); the first two come from the
+  // caller, read as soon as the stage has landed.
+  bf16x8 kf[C::NKS];
+  kf[0] = k01[0];
+  kf[1] = k01[1];
+  pre(std::integral_constant<int, -1>{});
+  if constexpr (MASKED) {
+    // A masked stage (a few per query block) issues every piece up front: a wave whose rows
+    // all precede the stage's keys then skips it (wave-uniform: nothing of it reaches them).
+    static_for<0, C::NKS>([&](auto u) { pre(u); });
+    if (skip) return;
+  }
+  static_for<0, C::NKS>([&](auto ksc) {
+    constexpr int ks = decltype(ksc)::value;
+    if constexpr (ks == 0) {
+      if constexpr (MASKED)
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0],
+                                                       mask_init<MODE>(Ps, key0, 0, hl, t), 0, 0, 0);
+      else
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16{}, 0, 0, 0);
     } else {
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0[kt], qf[0], f32x16{}, 0, 0, 0);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s[0], 0, 0, 0);
     }
-  }
-#pragma unroll
-  for (int kt = 0; kt < C::NKT; ++kt) {
-#pragma unroll
-    for (int ks = 1; ks < C::NKS; ++ks) {
-      const bf16x8 kf =
-          *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(kt * 32 + c32, ks * 16 + hl * 8)]);
-      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
-    }
-  }
+    if constexpr (ks + 2 < C::NKS)
+      kf[ks + 2] = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(c32, (ks + 2) * 16 + hl * 8)]);
+    if constexpr (!MASKED) pre(ksc);
+  });
   if constexpr (MAXONLY) {
     float mx = -INFINITY;
 #pragma unroll
@@ -550,6 +646,14 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
   }
 }
 
+// The first two K fragments (A operands of the first two score MFMAs) of a stage in LDS.
+template <int D>
+__device__ __forceinline__ void read_k01(const uint16_t* Ks, int lane, bf16x8 (&k01)[2]) {
+  const int c32 = lane & 31, hl = lane >> 5;
+  k01[0] = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(c32, hl * 8)]);
+  k01[1] = *reinterpret_cast<const bf16x8*>(&Ks[koff<D>(c32, 16 + hl * 8)]);
+}
+
 // Pipeline state carried from one stage to the next within a pass.
 struct Pipe {
   Stage cur;    // the stage whose loads are in flight or landed in buffer `p`
@@ -581,22 +685,40 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // the current stage landed; the other buffer is no longer read
     const int p = pp.p;
+    // the first score MFMAs' operands are requested before the iterator's scalar work
+    bf16x8 k01[2];
+    read_k01<D>(smem + (p ? a.tile_off[1] : a.tile_off[0]), lane, k01);
     const bool more = it.template next_of<KIND>(tid, C::NT);
     const Stage nxt = stage_of<BS, C::SK>(it);
     uint16_t* Kn = smem + (p ? a.tile_off[0] : a.tile_off[1]);
     uint16_t* Vn = smem + (p ? a.tile_off[2] : a.tile_off[3]);
-    if constexpr (KIND != 2) {
-      if (more) issue_stage<D, BS, KIND == 0>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane, lc.cok,
-                                              lc.cov);
+    if constexpr (KIND == 0) {
+      if (more) issue_stage<D, BS, true>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane, lc.cok, lc.cov);
     }
-    // Key stream: the loads go out after the stage's first K fragment reads, so the LDS reads of
-    // their slots overlap those; no branch around them.  Past the end of the stream the
-    // iterator still names the current stage, which is then loaded again into the free buffer.
-    // The slots of the stage after the next one go into the ring at the same time.
-    auto stream_issue = [&]() {
-      if constexpr (KIND == 2) {
-        issue_gathered<D, BS>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane, lc.cok, lc.cov);
-        issue_ring(rr, it, it.ks, lc.seg_pos, w, lane);
+    // Key blocks (KIND 1): the next stage's loads go out in pieces between this stage's score
+    // MFMAs.  Key stream (KIND 2): the same, after its slots are read from the ring (pre(-1));
+    // no branch around them: past the end of the stream the iterator still names the current
+    // stage, which is then loaded again into the free buffer.  The slots of the stage after the
+    // next one go into the ring with the last piece.
+    Gather<D, BS> gt;
+    auto pre = [&](auto u) {
+      constexpr int U = decltype(u)::value;
+      if constexpr (KIND == 1) {
+        piece_items<U, C::NKS, BlockLoads<D, BS, MODE>::NI>([&](auto i) {
+          BlockLoads<D, BS, MODE>::template item<decltype(i)::value>(a, rr, nxt, Kn, Vn,
+                                                                     p ? Ps0 : Ps1, w, lane, more);
+        });
+      } else if constexpr (KIND == 2) {
+        if constexpr (U < 0) {
+          gt.read(nxt, w, lane);
+        } else {
+          piece_items<U, C::NKS, Gather<D, BS>::NI>([&](auto i) {
+            gt.template item<decltype(i)::value>(a, rr, nxt, Kn, Vn, p ? Ps0 : Ps1, w, lane,
+                                                 lc.cok, lc.cov, [&] {
+                                                   issue_ring(rr, it, it.ks, lc.seg_pos, w, lane);
+                                                 });
+          });
+        }
       }
     };
     // A masked stage whose keys all come after every row of this wave adds exactly nothing to
@@ -607,7 +729,7 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
       skip = pp.cur.pos0 > __builtin_amdgcn_readfirstlane((t & ~31) + 31);
     attn_stage<D, BS, MODE, MASKED, MAXONLY>(
         a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
-        p ? Ps1 : Ps0, pp.cur.key0, lane, t, qf, oacc, rs, stream_issue, skip);
+        p ? Ps1 : Ps0, pp.cur.key0, lane, t, qf, oacc, rs, k01, pre, skip);
     pp.cur = nxt;
     pp.p = p ^ 1;
   }
@@ -646,12 +768,14 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       RowState first{0.f, 0.f, -INFINITY};
+      bf16x8 k01[2];
+      read_k01<D>(smem + a.tile_off[0], lane, k01);
       if (n_unm_stages > 0)
         attn_stage<D, BS, MODE, false, true>(a, smem + a.tile_off[0], smem + a.tile_off[2], Ps0,
-                                             pp.cur.key0, lane, t, qf, oacc, first, [] {});
+                                             pp.cur.key0, lane, t, qf, oacc, first, k01, [](auto) {});
       else
         attn_stage<D, BS, MODE, true, true>(a, smem + a.tile_off[0], smem + a.tile_off[2], Ps0,
-                                            pp.cur.key0, lane, t, qf, oacc, first, [] {});
+                                            pp.cur.key0, lane, t, qf, oacc, first, k01, [](auto) {});
       rs.mref = (first.mseen == -INFINITY) ? 0.f : first.mseen;
     }
     // n_blk_stages contiguous stages (key blocks), then, in mode 1, the rest of the unmasked

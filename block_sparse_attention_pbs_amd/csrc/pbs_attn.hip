@@ -615,34 +615,38 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
     rs.mseen = fmaxf(rs.mseen, pair_max(mx) * a.c);
   } else {
     const float nm = -rs.mref;
+    // O^T += V^T P^T in NJ steps, step j = s2 * NMT + mt (keys 16*s2 .. +15, head dims
+    // 32*mt .. +31).  The V^T fragment of step j is read two steps ahead, the first two before
+    // the exp2 work, so that no step waits out a whole LDS round trip.
+    constexpr int NJ = 2 * C::NMT;
+    auto read_v = [&](int j) {
+      const int s2 = j / C::NMT, mt = j % C::NMT;
+      const int vr = 16 * s2 + 4 * (gp >> 1) + (li >> 2);
+      const int dv = mt * 32 + (gp & 1) * 16 + 4 * (li & 3);
+      const u32x2 lo = ds_read_tr(&Vs[voff<D>(vr, dv)]);
+      const u32x2 hi = ds_read_tr(&Vs[voff<D>(vr + 8, dv)]);
+      return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    bf16x8 vf[NJ];
+    vf[0] = read_v(0);
+    vf[1] = read_v(1);
+    bf16x8 pb[2];
+    float sum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
-      bf16x8 pb[2];
-      float sum = 0.f;
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)   // v_cvt_pk_bf16_f32, round to nearest even
-        {
-          const float pe = fast_exp2(fmaf(s[kt][8 * s2 + e], a.c, nm));
-          sum += pe;
-          pb[s2][e] = static_cast<__bf16>(pe);
-        }
-      rs.lsum += sum;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int vr = kt * 32 + 16 * s2 + 4 * (gp >> 1) + (li >> 2);
-#pragma unroll
-        for (int mt = 0; mt < C::NMT; ++mt) {
-          const int dv = mt * 32 + (gp & 1) * 16 + 4 * (li & 3);
-          const u32x2 lo = ds_read_tr(&Vs[voff<D>(vr, dv)]);
-          const u32x2 hi = ds_read_tr(&Vs[voff<D>(vr + 8, dv)]);
-          const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4),
-                                                             pb[s2], oacc[mt], 0, 0, 0);
-        }
+      for (int e = 0; e < 8; ++e) {   // v_cvt_pk_bf16_f32, round to nearest even
+        const float pe = fast_exp2(fmaf(s[0][8 * s2 + e], a.c, nm));
+        sum += pe;
+        pb[s2][e] = static_cast<__bf16>(pe);
       }
-    }
+    rs.lsum += sum;
+    static_for<0, NJ>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      oacc[j % C::NMT] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pb[j / C::NMT], oacc[j % C::NMT], 0, 0, 0);
+      if constexpr (j + 2 < NJ) vf[j + 2] = read_v(j + 2);
+    });
   }
 }
 

@@ -562,7 +562,7 @@ struct RowState {
 // row's reference is set to its max over the pass's first stage (0 for a row that sees no key of
 // it; the MAXONLY form of this function computes that max), and a row sum outside [2^-60, 2^64]
 // after the pass sends the workgroup through the exact-max fallback.
-template <int D, int BS, int MODE, bool MASKED, bool MAXONLY, class Pre>
+template <int D, int BS, int MODE, bool MASKED, bool MAXONLY, bool VPRE = true, class Pre>
 __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks, const uint16_t* Vs,
                                            const int32_t* Ps, int key0, int lane, int t,
                                            const bf16x8 (&qf)[Cfg<D, BS>::NKS],
@@ -617,7 +617,8 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
     const float nm = -rs.mref;
     // O^T += V^T P^T in NJ steps, step j = s2 * NMT + mt (keys 16*s2 .. +15, head dims
     // 32*mt .. +31).  The V^T fragment of step j is read two steps ahead, the first two before
-    // the exp2 work, so that no step waits out a whole LDS round trip.
+    // the exp2 work, so that no step waits out a whole LDS round trip.  (VPRE false: each read
+    // just before its step, fewer live registers, for the rarely run exact-max pass.)
     constexpr int NJ = 2 * C::NMT;
     auto read_v = [&](int j) {
       const int s2 = j / C::NMT, mt = j % C::NMT;
@@ -628,8 +629,10 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
       return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
     bf16x8 vf[NJ];
-    vf[0] = read_v(0);
-    vf[1] = read_v(1);
+    if constexpr (VPRE) {
+      vf[0] = read_v(0);
+      vf[1] = read_v(1);
+    }
     bf16x8 pb[2];
     float sum = 0.f;
 #pragma unroll
@@ -643,9 +646,10 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, const uint16_t* Ks
     rs.lsum += sum;
     static_for<0, NJ>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
+      if constexpr (!VPRE) vf[j] = read_v(j);
       oacc[j % C::NMT] =
           __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pb[j / C::NMT], oacc[j % C::NMT], 0, 0, 0);
-      if constexpr (j + 2 < NJ) vf[j + 2] = read_v(j + 2);
+      if constexpr (VPRE && j + 2 < NJ) vf[j + 2] = read_v(j + 2);
     });
   }
 }
@@ -677,7 +681,7 @@ struct LoadCtx {
 // uniform offsets, so the loop body is one straight copy of the stage code and the accumulators
 // stay in place from one iteration to the next.
 // KIND: 0 any stage may follow, 1 only key-block stages follow, 2 only key-stream stages.
-template <int D, int BS, int MODE, bool MASKED, bool MAXONLY, int KIND>
+template <int D, int BS, int MODE, bool MASKED, bool MAXONLY, int KIND, bool VPRE = true>
 __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int count, Pipe& pp,
                                            const Rsrc& rr, const LoadCtx& lc, uint16_t* smem,
                                            int32_t* Ps0, int32_t* Ps1, int w, int lane, int t,
@@ -731,7 +735,7 @@ __device__ __forceinline__ void run_stages(const AttnArgs& a, StageIter& it, int
     bool skip = false;
     if constexpr (MASKED && MODE != 4)
       skip = pp.cur.pos0 > __builtin_amdgcn_readfirstlane((t & ~31) + 31);
-    attn_stage<D, BS, MODE, MASKED, MAXONLY>(
+    attn_stage<D, BS, MODE, MASKED, MAXONLY, VPRE>(
         a, smem + (p ? a.tile_off[1] : a.tile_off[0]), smem + (p ? a.tile_off[3] : a.tile_off[2]),
         p ? Ps1 : Ps0, pp.cur.key0, lane, t, qf, oacc, rs, k01, pre, skip);
     pp.cur = nxt;
@@ -787,19 +791,19 @@ __device__ __forceinline__ void attn_pass(const AttnArgs& a, StageIter& it, int 
     if constexpr (MODE == 1) {
       // key blocks (the last one hands over to the stream), then the stream's stages
       if (n_blk_stages > 0) {
-        run_stages<D, BS, MODE, false, MAXONLY, 1>(a, it, n_blk_stages - 1, pp, rr, lc, smem, Ps0,
+        run_stages<D, BS, MODE, false, MAXONLY, 1, PRIME>(a, it, n_blk_stages - 1, pp, rr, lc, smem, Ps0,
                                                    Ps1, w, lane, t, qf, oacc, rs);
-        run_stages<D, BS, MODE, false, MAXONLY, 0>(a, it, 1, pp, rr, lc, smem, Ps0, Ps1, w, lane,
+        run_stages<D, BS, MODE, false, MAXONLY, 0, PRIME>(a, it, 1, pp, rr, lc, smem, Ps0, Ps1, w, lane,
                                                    t, qf, oacc, rs);
       }
-      run_stages<D, BS, MODE, false, MAXONLY, 2>(a, it, n_unm_stages - n_blk_stages, pp, rr, lc,
+      run_stages<D, BS, MODE, false, MAXONLY, 2, PRIME>(a, it, n_unm_stages - n_blk_stages, pp, rr, lc,
                                                  smem, Ps0, Ps1, w, lane, t, qf, oacc, rs);
-      run_stages<D, BS, MODE, true, MAXONLY, 2>(a, it, n_msk_stages, pp, rr, lc, smem, Ps0, Ps1,
+      run_stages<D, BS, MODE, true, MAXONLY, 2, PRIME>(a, it, n_msk_stages, pp, rr, lc, smem, Ps0, Ps1,
                                                 w, lane, t, qf, oacc, rs);
     } else {
-      run_stages<D, BS, MODE, false, MAXONLY, 1>(a, it, n_unm_stages, pp, rr, lc, smem, Ps0, Ps1,
+      run_stages<D, BS, MODE, false, MAXONLY, 1, PRIME>(a, it, n_unm_stages, pp, rr, lc, smem, Ps0, Ps1,
                                                  w, lane, t, qf, oacc, rs);
-      run_stages<D, BS, MODE, true, MAXONLY, 1>(a, it, n_msk_stages, pp, rr, lc, smem, Ps0, Ps1,
+      run_stages<D, BS, MODE, true, MAXONLY, 1, PRIME>(a, it, n_msk_stages, pp, rr, lc, smem, Ps0, Ps1,
                                                 w, lane, t, qf, oacc, rs);
     }
   }

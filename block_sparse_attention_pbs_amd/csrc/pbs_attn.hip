@@ -16,9 +16,10 @@
 //    direct buffer->LDS loads (buffer_load_dwordx4 ... lds, bounds-checked) one stage ahead of
 //    the compute; a wave issues its share of the next stage's loads one by one between the
 //    MFMAs of the current stage's score chain, where their issue costs no MFMA time, and reads
-//    the first K fragments of a stage right after the barrier that lands it.  A workgroup needs at most ~52 KiB of LDS and 168 VGPRs per lane, so three
-//    workgroups share a CU (three waves per SIMD): while one waits or runs its softmax, the
-//    others keep the matrix cores busy;
+//    the first K fragments of a stage right after the barrier that lands it.  A workgroup
+//    needs at most ~44 KiB of LDS and 168 VGPRs per lane, so three workgroups share a CU (three
+//    waves per SIMD): while one waits or runs its softmax, the others keep the matrix cores
+//    busy;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 (A = K rows from
 //    LDS, B = the wave's Q rows held in registers), so each lane owns one query row and the
 //    softmax statistics need one cross-half exchange.  The accumulators live in VGPRs (built
